@@ -1,0 +1,184 @@
+/*
+ * libidx -- dense prefill indexer for AMD Instinct MI355X (gfx950).
+ *
+ * The indexer scores a prefill chunk of T query rows against a compressed key
+ * prefix of L rows and keeps, per query row, the top-K keys:
+ *
+ *     I[t, s] = sum_h w[t, h] * max(0, scale * <qd[t, h, :], kd[s, :]>),
+ *     s in the row's key window [ks[t], ke[t])
+ *
+ * qd / kd are the dequantised fp8 E4M3 queries and fp8 E4M3 or MXFP4 keys.
+ * The pages this library follows describe the call but do not print the
+ * formula; it is the DeepSeek sparse-attention indexer score.  Sources, cited
+ * by page title and section:
+ *
+ *   P1  "Running CHUNKED_PREFILL_SIZE above 1024 without the long-prompt
+ *       memory problem" -- section 1 (the dense indexer call: T rows against
+ *       the whole compressed prefix, output [T, max_seqlen_k] fp32, ragged
+ *       top-k, the layer-20 candidate source pooling 8-key blocks into a
+ *       top-2048 block mask consumed by later layers through masked_fill_),
+ *       section 2.3 (key blocks of B_k with per-block top-k and a merge:
+ *       topk(union) == topk(union of per-block topk); memory c*T*B_k).
+ *   P2  "[DeepSeek-V4.1] Bound the dense prefill indexer transient: row-chunk
+ *       logits, tail-only candidate masks" -- Motivation (fp8 q x fp4 k
+ *       logits [T, lc] fp32 are the transient), Modifications (row chunks
+ *       under a 2 GiB logits budget, top-k of each chunk into one shared
+ *       selected buffer, masks written into one preallocated [rows, lc]
+ *       tensor), Accuracy/equivalence (index sets and masks compared
+ *       bitwise; row-count invariance; determinism).
+ *   P3  commit messages of an SGLang fork -- the NSA-indexer chunk-budget
+ *       microbenchmark (fp8_mqa_logits + fast_topk_transform_fused at H=32,
+ *       D=128, topk=2048) and the per-batch ragged plan / no per-request
+ *       host syncs in forward_indexer.
+ *
+ * Conventions for every entry point:
+ *   - Data pointers are DEVICE pointers owned by the caller.  libidx never
+ *     allocates or frees memory and never synchronises the stream.  Scratch
+ *     space is the caller's `ws` buffer, sized by idx_workspace_size().
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = default stream).
+ *   - A status other than IDX_OK from argument checking means nothing was
+ *     enqueued.  IDX_E_LAUNCH reports a failed launch (hipGetLastError); the
+ *     outputs are then undefined.
+ *   - Arrays are row-major with a contiguous last dimension; leading
+ *     dimensions (ld*) count elements.  q, k and logits need 16-byte
+ *     alignment, everything else its element alignment.
+ *   - Key indices in outputs are absolute rows of k.  Selected indices of a
+ *     row are ascending; unused slots hold -1 (values -inf).
+ *   - Order of selection: fp32 score descending, then key index ascending.
+ *     The selected set is unique under this total order, so results are
+ *     bitwise deterministic and independent of row chunking and key blocking.
+ *   - Preconditions the host cannot check without reading device memory
+ *     (0 <= ks[t] <= ke[t] <= L, finite inputs, q_scale/k_scale >= 0, window
+ *     length <= W where a W is given) are the caller's; violating them gives
+ *     undefined results but no out-of-bounds access of q/k (key rows are
+ *     clamped to [0, L)).
+ *   - Supported: D = 128; H in {32, 64}; 1 <= K <= 2048; block_k a multiple of
+ *     256 in [256, 32768]; pool = 8; 1 <= n_blocks <= 2048.
+ */
+#ifndef LIBIDX_IDX_H
+#define LIBIDX_IDX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t idx_status;
+enum {
+  IDX_OK = 0,
+  IDX_E_NULL = 1,        /* a required pointer is NULL                          */
+  IDX_E_SHAPE = 2,       /* inconsistent sizes (T, L, W, leading dimensions)    */
+  IDX_E_PARAM = 3,       /* parameter out of range (K, block_k, row_chunk, ...) */
+  IDX_E_FORMAT = 4,      /* unknown key format                                  */
+  IDX_E_WORKSPACE = 5,   /* ws_bytes below idx_workspace_size()                 */
+  IDX_E_UNSUPPORTED = 6, /* valid but not provided (D != 128, H, ...)           */
+  IDX_E_LAUNCH = 7,      /* a kernel launch failed                              */
+  IDX_E_ALIGN = 8        /* a pointer lacks the required alignment              */
+};
+
+enum { IDX_K_FP8_E4M3 = 0, IDX_K_MXFP4 = 1 };
+
+/* Operations for idx_workspace_size(). */
+enum {
+  IDX_OP_MQA_LOGITS = 0,       /* idx_mqa_logits: no workspace                          */
+  IDX_OP_TOPK = 1,             /* idx_topk: no workspace                                */
+  IDX_OP_LOGITS_TOPK_FUSED = 2,
+  IDX_OP_BLOCK_CANDIDATES = 3, /* idx_block_candidates with logits == NULL (fused)      */
+  IDX_OP_BLOCK_CANDIDATES_DENSE = 4 /* idx_block_candidates from given logits           */
+};
+
+/* One indexer call's inputs (all device pointers). */
+typedef struct idx_problem {
+  const uint8_t *q;       /* [T, H, D] fp8 E4M3 (OCP "FN": max 448, no inf)                 */
+  const float *q_scale;   /* [T, H] dequantisation scale of each (t, h) row of D, >= 0       */
+  const void *k;          /* fp8: uint8 [L, D] E4M3;  MXFP4: uint8 [L, D/2] E2M1 pairs,
+                             element d in the low nibble of byte d/2 when d is even          */
+  const void *k_scale;    /* fp8: float [L] per key row, >= 0;  MXFP4: uint8 E8M0 [L, D/32],
+                             one power-of-two scale per 32 consecutive d                    */
+  int32_t k_fmt;          /* IDX_K_FP8_E4M3 or IDX_K_MXFP4                                  */
+  const float *w;         /* [T, H] head weights, any sign                                   */
+  const int32_t *ks;      /* [T] first key of row t's window                                 */
+  const int32_t *ke;      /* [T] one past the last key of row t's window                     */
+  int32_t T, H, D, L;     /* query rows, heads, head dim (128), key rows                     */
+  float scale;            /* extra positive factor inside the ReLU (1.0 if unused)           */
+} idx_problem;
+
+/* Dense MQA logits (P1 section 1: output [T, max_seqlen_k] fp32; P2 Motivation).
+ * logits: [T, ld] fp32, ld >= W.  Column j of row t holds I[t, ks[t] + j] for
+ * j < ke[t] - ks[t] and -inf for ke[t] - ks[t] <= j < W.  Columns >= W are not
+ * touched.  W is normally the longest window (max_seqlen_k). */
+idx_status idx_mqa_logits(const idx_problem *p, float *logits, int64_t ld, int32_t W, void *stream);
+
+/* Logits of one rectangle in key-block layout: rows [row0, row0 + nrows) and
+ * absolute keys [key0, key0 + nkeys), key0 a multiple of 256.  out: [nrows, ld]
+ * fp32, ld >= nkeys; column c of row r holds I[row0 + r, key0 + c] where that key
+ * is inside the row's window; other columns are not written.  This is the
+ * scoring stage of the key-blocked indexer (P1 section 2.3), exposed so callers
+ * can drive their own block loop. */
+idx_status idx_mqa_logits_block(const idx_problem *p, int32_t row0, int32_t nrows, int32_t key0,
+                                int32_t nkeys, float *out, int64_t ld, void *stream);
+
+/* Top-K of dense row-relative logits (P2 Modifications: ragged top-k into the
+ * shared selected buffer; P1 section 2.3).
+ * logits: [T, ld] fp32 as written by idx_mqa_logits; row t's candidates are
+ * columns j < ke[t] - ks[t] (key ks[t] + j).  mask (nullable): [T, ld_mask]
+ * bytes over the same columns; keys whose mask byte is 0 are never selected.
+ * block_k: columns scored per pass (the selection is exact for any value).
+ * out_idx: [T, K] int32 absolute key indices, ascending, -1 padded.
+ * out_val (nullable): [T, K] fp32 logits of the selected keys, -inf padded.
+ * ws may be NULL (no workspace). */
+idx_status idx_topk(const float *logits, int64_t ld, int32_t W, const int32_t *ks, const int32_t *ke,
+                    const uint8_t *mask, int64_t ld_mask, int32_t T, int32_t K, int32_t block_k,
+                    int32_t *out_idx, float *out_val, void *ws, size_t ws_bytes, void *stream);
+
+/* Fused key-blocked indexer (P1 section 2.3): for each chunk of row_chunk rows
+ * and each key block of block_k keys, score the block into workspace and merge
+ * its top-K into the running top-K of those rows.  [T, L] logits are never
+ * materialised: workspace is O(row_chunk * block_k), independent of L.
+ * Result equals idx_mqa_logits + idx_topk bitwise.  mask (nullable):
+ * [T, ld_mask] bytes, column j <-> key ks[t] + j (the candidate mask of
+ * idx_block_candidates); keys with mask 0 are excluded.  Outputs as idx_topk. */
+idx_status idx_logits_topk_fused(const idx_problem *p, int32_t K, int32_t block_k, int32_t row_chunk,
+                                 const uint8_t *mask, int64_t ld_mask, int32_t *out_idx,
+                                 float *out_val, void *ws, size_t ws_bytes, void *stream);
+
+/* Candidate source (P1 section 1, select_candidate_blocks; P2 Modifications:
+ * masks written in place into one preallocated [rows, lc] tensor).
+ * Pool the logits of each row over blocks of `pool` keys starting at ks[t]
+ * (max; a partial last block takes the max of its in-window keys), keep the
+ * n_blocks blocks with the highest pooled fp32 value (ties: lower block), and
+ * write mask: [T, ld_mask] bytes, mask[t, j] = 1 iff j < ke[t] - ks[t] and block
+ * j / pool is kept, else 0, for 0 <= j < W.
+ * logits != NULL: read dense row-relative logits [T, ld] (idx_mqa_logits layout;
+ * q/k/w of p are not read).  logits == NULL: score from p block by block
+ * (block_k keys, row_chunk rows); requires ks[t] % pool == 0 for every row.
+ * out_blocks (nullable): [T, n_blocks] int32 kept block ids, ascending, -1 padded. */
+idx_status idx_block_candidates(const idx_problem *p, const float *logits, int64_t ld, int32_t pool,
+                                int32_t n_blocks, int32_t block_k, int32_t row_chunk, uint8_t *mask,
+                                int64_t ld_mask, int32_t W, int32_t *out_blocks, void *ws,
+                                size_t ws_bytes, void *stream);
+
+/* Workspace bytes an operation needs (host only; touches no device). */
+idx_status idx_workspace_size(int32_t op, const idx_problem *p, int32_t K, int32_t block_k,
+                              int32_t row_chunk, int32_t pool, int32_t n_blocks, int32_t W,
+                              size_t *bytes);
+
+/* Per-row windows of a varlen batch (P3: one ragged plan per batch instead of
+ * per-layer descriptor rebuilds; P1 section 2.1: a request landing on a cached
+ * prefix).  Request i owns query rows [cu_q[i], cu_q[i+1]) and key rows
+ * [cu_k[i], cu_k[i+1]); its new rows are the last of its keys, so row j of
+ * request i gets ks = cu_k[i], ke = cu_k[i] + (len_k - len_q) + j + 1.
+ * cu_q, cu_k: device int32 [B + 1]; ks, ke: device int32 [T]; rows at or past
+ * cu_q[B] get the empty window ks = ke = 0. */
+idx_status idx_ragged_windows(const int32_t *cu_q, const int32_t *cu_k, int32_t B, int32_t T,
+                              int32_t *ks, int32_t *ke, void *stream);
+
+/* Static description of a status code. */
+const char *idx_status_str(idx_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBIDX_IDX_H */

@@ -1,0 +1,245 @@
+"""Python binding of libidx, the MI355X dense prefill indexer (MQA logits + top-K).
+
+Argument marshalling only: every step of the indexer runs in the HIP kernels
+behind the C ABI declared in include/idx.h.  PyTorch supplies device memory
+(outputs and workspace are allocated here with torch when the caller passes
+none) and the current HIP stream.  There is no fallback: if libidx.so is
+missing or fails to load, every call raises.
+
+Function names match the C entry points.  Tensors must be on the GPU and
+contiguous; key indices in outputs are absolute rows of k.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libidx.so")
+
+IDX_K_FP8_E4M3 = 0
+IDX_K_MXFP4 = 1
+IDX_OP_MQA_LOGITS = 0
+IDX_OP_TOPK = 1
+IDX_OP_LOGITS_TOPK_FUSED = 2
+IDX_OP_BLOCK_CANDIDATES = 3
+IDX_OP_BLOCK_CANDIDATES_DENSE = 4
+
+STATUS = {0: "IDX_OK", 1: "IDX_E_NULL", 2: "IDX_E_SHAPE", 3: "IDX_E_PARAM", 4: "IDX_E_FORMAT",
+          5: "IDX_E_WORKSPACE", 6: "IDX_E_UNSUPPORTED", 7: "IDX_E_LAUNCH", 8: "IDX_E_ALIGN"}
+
+EXPORTS = ("idx_mqa_logits", "idx_mqa_logits_block", "idx_topk", "idx_logits_topk_fused",
+           "idx_block_candidates", "idx_workspace_size", "idx_ragged_windows", "idx_status_str")
+
+
+class IdxError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({status_str(status)})")
+
+
+class idx_problem(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("q_scale", ctypes.c_void_p), ("k", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("k_fmt", ctypes.c_int32), ("w", ctypes.c_void_p),
+                ("ks", ctypes.c_void_p), ("ke", ctypes.c_void_p), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("L", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+_lib = None
+
+
+def load_library():
+    """Load libidx.so (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libidx is not built ({LIB_PATH} missing); run __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, VP = ctypes.POINTER(idx_problem), ctypes.c_void_p
+    i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.idx_mqa_logits.argtypes = [P, VP, i64, i32, VP]
+    lib.idx_mqa_logits_block.argtypes = [P, i32, i32, i32, i32, VP, i64, VP]
+    lib.idx_topk.argtypes = [VP, i64, i32, VP, VP, VP, i64, i32, i32, i32, VP, VP, VP, sz, VP]
+    lib.idx_logits_topk_fused.argtypes = [P, i32, i32, i32, VP, i64, VP, VP, VP, sz, VP]
+    lib.idx_block_candidates.argtypes = [P, VP, i64, i32, i32, i32, i32, VP, i64, i32, VP, VP, sz, VP]
+    lib.idx_workspace_size.argtypes = [i32, P, i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.idx_ragged_windows.argtypes = [VP, VP, i32, i32, VP, VP, VP]
+    lib.idx_status_str.argtypes = [i32]
+    lib.idx_status_str.restype = ctypes.c_char_p
+    for name in EXPORTS:
+        if name != "idx_status_str":
+            getattr(lib, name).restype = i32
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load_library().idx_status_str(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise IdxError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+@dataclass
+class Inputs:
+    """Device tensors of one indexer call (see include/idx.h, idx_problem)."""
+    q: torch.Tensor        # uint8 [T, H, D]
+    q_scale: torch.Tensor  # float32 [T, H]
+    k: torch.Tensor        # uint8 [L, D] (fp8) or [L, D/2] (MXFP4)
+    k_scale: torch.Tensor  # float32 [L] (fp8) or uint8 [L, D/32] (MXFP4)
+    w: torch.Tensor        # float32 [T, H]
+    ks: torch.Tensor       # int32 [T]
+    ke: torch.Tensor       # int32 [T]
+    k_fmt: int = IDX_K_FP8_E4M3
+    scale: float = 1.0
+
+    @property
+    def T(self):
+        return int(self.q.shape[0])
+
+    @property
+    def H(self):
+        return int(self.q.shape[1])
+
+    @property
+    def L(self):
+        return int(self.k.shape[0])
+
+    def struct(self) -> idx_problem:
+        return idx_problem(q=self.q.data_ptr(), q_scale=self.q_scale.data_ptr(), k=self.k.data_ptr(),
+                           k_scale=self.k_scale.data_ptr(), k_fmt=self.k_fmt, w=self.w.data_ptr(),
+                           ks=self.ks.data_ptr(), ke=self.ke.data_ptr(), T=self.T, H=self.H,
+                           D=int(self.q.shape[2]), L=self.L, scale=self.scale)
+
+    @staticmethod
+    def from_host(p, device="cuda") -> "Inputs":
+        """Copy a host problem (numpy arrays with the same field names) to the device."""
+        t = lambda a: torch.from_numpy(a).to(device)
+        return Inputs(q=t(p.q), q_scale=t(p.q_scale), k=t(p.k), k_scale=t(p.k_scale), w=t(p.w), ks=t(p.ks),
+                      ke=t(p.ke), k_fmt=int(p.k_fmt), scale=float(p.scale))
+
+
+def idx_workspace_size(op: int, p: Inputs, K: int = 0, block_k: int = 0, row_chunk: int = 0, pool: int = 0,
+                       n_blocks: int = 0, W: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    s = p.struct()
+    _check("idx_workspace_size",
+           load_library().idx_workspace_size(op, ctypes.byref(s), K, block_k, row_chunk, pool, n_blocks, W,
+                                             ctypes.byref(n)))
+    return n.value
+
+
+def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def idx_mqa_logits(p: Inputs, W: Optional[int] = None, out: Optional[torch.Tensor] = None, stream=None):
+    """Dense row-relative logits [T, W] fp32 (-inf past each row's window)."""
+    if W is None:
+        W = int((p.ke - p.ks).max().item()) if p.T else 0
+    if out is None:
+        out = torch.empty((p.T, W), dtype=torch.float32, device=p.q.device)
+    s = p.struct()
+    _check("idx_mqa_logits", load_library().idx_mqa_logits(ctypes.byref(s), _ptr(out), out.stride(0), W,
+                                                           _stream(stream)))
+    return out
+
+
+def idx_mqa_logits_block(p: Inputs, row0: int, nrows: int, key0: int, nkeys: int,
+                         out: Optional[torch.Tensor] = None, stream=None):
+    """Logits of rows [row0, row0+nrows) x keys [key0, key0+nkeys) (in-window entries only)."""
+    if out is None:
+        out = torch.full((nrows, nkeys), float("nan"), dtype=torch.float32, device=p.q.device)
+    s = p.struct()
+    _check("idx_mqa_logits_block",
+           load_library().idx_mqa_logits_block(ctypes.byref(s), row0, nrows, key0, nkeys, _ptr(out), out.stride(0),
+                                               _stream(stream)))
+    return out
+
+
+def idx_topk(logits: torch.Tensor, ks: torch.Tensor, ke: torch.Tensor, K: int, W: Optional[int] = None,
+             block_k: int = 0, mask: Optional[torch.Tensor] = None, out_idx: Optional[torch.Tensor] = None,
+             out_val: Optional[torch.Tensor] = None, with_values: bool = True, stream=None):
+    T = int(logits.shape[0])
+    W = int(logits.shape[1]) if W is None else W
+    dev = logits.device
+    if out_idx is None:
+        out_idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    if out_val is None and with_values:
+        out_val = torch.empty((T, K), dtype=torch.float32, device=dev)
+    _check("idx_topk", load_library().idx_topk(
+        _ptr(logits), logits.stride(0), W, _ptr(ks), _ptr(ke), _ptr(mask), mask.stride(0) if mask is not None else 0,
+        T, K, block_k, _ptr(out_idx), _ptr(out_val), None, 0, _stream(stream)))
+    return out_idx, out_val
+
+
+def idx_logits_topk_fused(p: Inputs, K: int, block_k: int = 32768, row_chunk: int = 0,
+                          mask: Optional[torch.Tensor] = None, out_idx: Optional[torch.Tensor] = None,
+                          out_val: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                          with_values: bool = True, stream=None):
+    dev = p.q.device
+    if out_idx is None:
+        out_idx = torch.empty((p.T, K), dtype=torch.int32, device=dev)
+    if out_val is None and with_values:
+        out_val = torch.empty((p.T, K), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = _workspace(idx_workspace_size(IDX_OP_LOGITS_TOPK_FUSED, p, K=K, block_k=block_k, row_chunk=row_chunk),
+                        dev)
+    s = p.struct()
+    _check("idx_logits_topk_fused", load_library().idx_logits_topk_fused(
+        ctypes.byref(s), K, block_k, row_chunk, _ptr(mask), mask.stride(0) if mask is not None else 0,
+        _ptr(out_idx), _ptr(out_val), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+    return out_idx, out_val
+
+
+def idx_block_candidates(p: Inputs, W: int, pool: int = 8, n_blocks: int = 2048,
+                         logits: Optional[torch.Tensor] = None, block_k: int = 32768, row_chunk: int = 0,
+                         mask: Optional[torch.Tensor] = None, out_blocks: Optional[torch.Tensor] = None,
+                         ws: Optional[torch.Tensor] = None, stream=None):
+    dev = p.ks.device
+    if mask is None:
+        mask = torch.empty((p.T, W), dtype=torch.uint8, device=dev)
+    op = IDX_OP_BLOCK_CANDIDATES_DENSE if logits is not None else IDX_OP_BLOCK_CANDIDATES
+    if ws is None:
+        ws = _workspace(idx_workspace_size(op, p, block_k=block_k, row_chunk=row_chunk, pool=pool,
+                                           n_blocks=n_blocks, W=W), dev)
+    s = p.struct()
+    _check("idx_block_candidates", load_library().idx_block_candidates(
+        ctypes.byref(s), _ptr(logits), logits.stride(0) if logits is not None else 0, pool, n_blocks, block_k,
+        row_chunk, _ptr(mask), mask.stride(0), W, _ptr(out_blocks), _ptr(ws), ws.numel() if ws is not None else 0,
+        _stream(stream)))
+    return mask, out_blocks
+
+
+def idx_ragged_windows(cu_q: torch.Tensor, cu_k: torch.Tensor, T: int, stream=None):
+    B = int(cu_q.numel()) - 1
+    ks = torch.empty(T, dtype=torch.int32, device=cu_q.device)
+    ke = torch.empty(T, dtype=torch.int32, device=cu_q.device)
+    _check("idx_ragged_windows", load_library().idx_ragged_windows(_ptr(cu_q), _ptr(cu_k), B, T, _ptr(ks), _ptr(ke),
+                                                                   _stream(stream)))
+    return ks, ke
+
+
+def idx_status_str(status: int) -> str:
+    return status_str(status)

@@ -1,0 +1,39 @@
+"""Compile libidx.so (the HIP kernels and the C ABI) for gfx950 with hipcc."""
+import glob
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libidx.so")
+ARCH = "gfx950"
+
+FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+    # packed fp32 VALU ops are kept out of every kernel
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def sources():
+    csrc = os.path.join(HERE, "csrc")
+    return sorted(glob.glob(os.path.join(csrc, "*.hip"))) + sorted(glob.glob(os.path.join(csrc, "*.cpp")))
+
+
+def build(verbose: bool = False) -> str:
+    """Always recompiles (hipcc cross-compiles gfx950 without a GPU)."""
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = ["hipcc", *FLAGS, "-I", os.path.join(ROOT, "include"), *sources(), "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in l)
+    if res.returncode != 0:
+        raise RuntimeError("libidx build failed:\n" + out)
+    if verbose and out.strip():
+        print(out)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,375 @@
+// libidx C ABI: argument checking, workspace arithmetic, row-chunk / key-block
+// planning and the launch sequence on the caller's stream.  Nothing here
+// allocates device memory or synchronises; every check runs on the host
+// before the first HIP call, so an error status means nothing was enqueued.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/idx.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int32_t MAX_K = 2048;
+constexpr int32_t MAX_BLOCK = 32768;
+constexpr int32_t MAX_W = 1 << 22;
+constexpr int32_t KEY_ALIGN = 256;
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+idx_status check_problem(const idx_problem *p, bool need_scores) {
+  if (!p) return IDX_E_NULL;
+  if (!p->ks || !p->ke) return IDX_E_NULL;
+  if (p->T < 0 || p->L < 0 || p->H <= 0 || p->D <= 0) return IDX_E_SHAPE;
+  if (!aligned(p->ks, 4) || !aligned(p->ke, 4)) return IDX_E_ALIGN;
+  if (!need_scores) return IDX_OK;
+  if (!p->q || !p->q_scale || !p->k || !p->k_scale || !p->w) return IDX_E_NULL;
+  if (p->k_fmt != IDX_K_FP8_E4M3 && p->k_fmt != IDX_K_MXFP4) return IDX_E_FORMAT;
+  if (p->D != 128) return IDX_E_UNSUPPORTED;
+  if (p->H != 32 && p->H != 64) return IDX_E_UNSUPPORTED;
+  if (!(p->scale > 0.f) || !std::isfinite(p->scale)) return IDX_E_PARAM;
+  if (!aligned(p->q, 16) || !aligned(p->k, 16)) return IDX_E_ALIGN;
+  if (!aligned(p->q_scale, 4) || !aligned(p->w, 4)) return IDX_E_ALIGN;
+  if (!aligned(p->k_scale, 4)) return IDX_E_ALIGN;  // fp32 per key, or 4 E8M0 bytes per key
+  return IDX_OK;
+}
+
+int32_t round_up(int32_t x, int32_t a) { return (x + a - 1) / a * a; }
+size_t round_up_sz(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Default / clamp the key block and row chunk.
+int32_t eff_block(const idx_problem *p, int32_t block_k) {
+  if (block_k > 0) return block_k;
+  const int32_t b = round_up(p->L > 0 ? p->L : 1, KEY_ALIGN);
+  return b < MAX_BLOCK ? b : MAX_BLOCK;
+}
+int32_t eff_chunk(const idx_problem *p, int32_t row_chunk) {
+  if (row_chunk > 0) return row_chunk < p->T ? row_chunk : (p->T > 0 ? p->T : 1);
+  return p->T > 0 ? p->T : 1;
+}
+idx_status check_block(int32_t block_k) {
+  if (block_k < KEY_ALIGN || block_k > MAX_BLOCK || block_k % KEY_ALIGN) return IDX_E_PARAM;
+  return IDX_OK;
+}
+
+// Workgroup key splits for one scoring launch over n keys: a multiple of 8 splits
+// when possible (one XCD per split residue), each a multiple of 128 keys.
+void plan_splits(int32_t n, int32_t &split, int32_t &nsplit) {
+  if (n <= 0) { split = 128; nsplit = 0; return; }
+  const int32_t target = 4096;
+  int32_t ns = 8 * ((n + 8 * target - 1) / (8 * target));
+  split = round_up((n + ns - 1) / ns, 128);
+  if (split < 512) split = 512;
+  nsplit = (n + split - 1) / split;
+}
+
+idx::LogitsArgs logits_args(const idx_problem *p, int32_t row0, int32_t nrows, int32_t key_lo, int32_t key_hi,
+                            float *out, int64_t ld, int32_t wcols) {
+  idx::LogitsArgs a{};
+  a.q = p->q;
+  a.q_scale = p->q_scale;
+  a.k = (const uint8_t *)p->k;
+  a.k_scale = (const uint8_t *)p->k_scale;
+  a.w = p->w;
+  a.ks = p->ks;
+  a.ke = p->ke;
+  a.L = p->L;
+  a.scale = p->scale;
+  a.row0 = row0;
+  a.nrows = nrows;
+  a.key_lo = key_lo;
+  a.key_hi = key_hi;
+  plan_splits(key_hi - key_lo, a.split, a.nsplit);
+  a.out = out;
+  a.ld = ld;
+  a.wcols = wcols;
+  return a;
+}
+
+idx_status launched(hipError_t e) { return e == hipSuccess ? IDX_OK : IDX_E_LAUNCH; }
+
+struct Carve {
+  uint8_t *base;
+  size_t off = 0;
+  template <class T>
+  T *take(size_t n) {
+    T *r = (T *)(base + off);
+    off = round_up_sz(off + n * sizeof(T), 256);
+    return r;
+  }
+};
+
+size_t fused_ws(int32_t Tc, int32_t Bk, int32_t K) {
+  return round_up_sz((size_t)Tc * Bk * 4, 256) + round_up_sz((size_t)Tc * K * 4, 256);
+}
+size_t cand_ws(int32_t Tc, int32_t pooled_cols, int32_t n_blocks) {
+  return round_up_sz((size_t)Tc * pooled_cols * 4, 256) + 2 * round_up_sz((size_t)Tc * n_blocks * 4, 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *idx_status_str(idx_status s) {
+  switch (s) {
+    case IDX_OK: return "ok";
+    case IDX_E_NULL: return "a required pointer is NULL";
+    case IDX_E_SHAPE: return "inconsistent sizes";
+    case IDX_E_PARAM: return "parameter out of range";
+    case IDX_E_FORMAT: return "unknown key format";
+    case IDX_E_WORKSPACE: return "workspace too small";
+    case IDX_E_UNSUPPORTED: return "unsupported configuration";
+    case IDX_E_LAUNCH: return "kernel launch failed";
+    case IDX_E_ALIGN: return "pointer not aligned";
+    default: return "unknown status";
+  }
+}
+
+idx_status idx_workspace_size(int32_t op, const idx_problem *p, int32_t K, int32_t block_k, int32_t row_chunk,
+                              int32_t pool, int32_t n_blocks, int32_t W, size_t *bytes) {
+  if (!bytes || !p) return IDX_E_NULL;
+  *bytes = 0;
+  if (p->T < 0 || p->L < 0) return IDX_E_SHAPE;
+  const int32_t Tc = eff_chunk(p, row_chunk);
+  switch (op) {
+    case IDX_OP_MQA_LOGITS:
+    case IDX_OP_TOPK: return IDX_OK;
+    case IDX_OP_LOGITS_TOPK_FUSED: {
+      if (K < 1 || K > MAX_K) return IDX_E_PARAM;
+      const int32_t Bk = eff_block(p, block_k);
+      if (check_block(Bk) != IDX_OK) return IDX_E_PARAM;
+      *bytes = fused_ws(Tc, Bk, K);
+      return IDX_OK;
+    }
+    case IDX_OP_BLOCK_CANDIDATES: {
+      if (pool != 8) return IDX_E_UNSUPPORTED;
+      if (n_blocks < 1 || n_blocks > MAX_K) return IDX_E_PARAM;
+      const int32_t Bk = eff_block(p, block_k);
+      if (check_block(Bk) != IDX_OK) return IDX_E_PARAM;
+      *bytes = cand_ws(Tc, Bk / pool, n_blocks);
+      return IDX_OK;
+    }
+    case IDX_OP_BLOCK_CANDIDATES_DENSE: {
+      if (pool != 8) return IDX_E_UNSUPPORTED;
+      if (n_blocks < 1 || n_blocks > MAX_K) return IDX_E_PARAM;
+      if (W < 0 || W > MAX_W) return IDX_E_SHAPE;
+      *bytes = cand_ws(Tc, (W + pool - 1) / pool, n_blocks);
+      return IDX_OK;
+    }
+    default: return IDX_E_PARAM;
+  }
+}
+
+idx_status idx_mqa_logits(const idx_problem *p, float *logits, int64_t ld, int32_t W, void *stream) {
+  idx_status st = check_problem(p, true);
+  if (st) return st;
+  if (!logits) return IDX_E_NULL;
+  if (W < 0 || ld < W || W > MAX_W) return IDX_E_SHAPE;
+  if (!aligned(logits, 16)) return IDX_E_ALIGN;
+  if (p->T == 0 || W == 0) return IDX_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (p->L > 0) {
+    idx::LogitsArgs a = logits_args(p, 0, p->T, 0, p->L, logits, ld, W);
+    st = launched(idx::launch_logits(a, p->k_fmt, p->H, idx::STORE_DENSE, s));
+    if (st) return st;
+  }
+  return launched(idx::launch_fill_tail(logits, ld, W, p->ks, p->ke, 0, p->T, s));
+}
+
+idx_status idx_mqa_logits_block(const idx_problem *p, int32_t row0, int32_t nrows, int32_t key0, int32_t nkeys,
+                                float *out, int64_t ld, void *stream) {
+  idx_status st = check_problem(p, true);
+  if (st) return st;
+  if (!out) return IDX_E_NULL;
+  if (row0 < 0 || nrows < 0 || (int64_t)row0 + nrows > p->T) return IDX_E_SHAPE;
+  if (key0 < 0 || nkeys < 0 || key0 % KEY_ALIGN) return IDX_E_PARAM;
+  if (ld < nkeys) return IDX_E_SHAPE;
+  if (!aligned(out, 16)) return IDX_E_ALIGN;
+  const int32_t key_hi = (int32_t)std::min<int64_t>((int64_t)key0 + nkeys, p->L);
+  if (nrows == 0 || key_hi <= key0) return IDX_OK;
+  idx::LogitsArgs a = logits_args(p, row0, nrows, key0, key_hi, out, ld, nkeys);
+  return launched(idx::launch_logits(a, p->k_fmt, p->H, idx::STORE_BLOCK, (hipStream_t)stream));
+}
+
+idx_status idx_topk(const float *logits, int64_t ld, int32_t W, const int32_t *ks, const int32_t *ke,
+                    const uint8_t *mask, int64_t ld_mask, int32_t T, int32_t K, int32_t block_k, int32_t *out_idx,
+                    float *out_val, void *ws, size_t ws_bytes, void *stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!logits || !ks || !ke || !out_idx) return IDX_E_NULL;
+  if (T < 0 || W < 0 || ld < W) return IDX_E_SHAPE;
+  if (mask && ld_mask < W) return IDX_E_SHAPE;
+  if (K < 1 || K > MAX_K) return IDX_E_PARAM;
+  if (block_k <= 0) block_k = MAX_BLOCK;
+  if (block_k > MAX_BLOCK) return IDX_E_PARAM;
+  if (!aligned(logits, 4) || !aligned(out_idx, 4) || (out_val && !aligned(out_val, 4))) return IDX_E_ALIGN;
+  if (T == 0) return IDX_OK;
+  idx::TopkArgs a{};
+  a.vals = logits;
+  a.ld = ld;
+  a.ncols = W;
+  a.block = block_k;
+  a.ks = ks;
+  a.ke = ke;
+  a.row0 = 0;
+  a.nrows = T;
+  a.mode = idx::TOPK_DENSE;
+  a.key0 = 0;
+  a.pool = 1;
+  a.mask = mask;
+  a.ld_mask = ld_mask;
+  a.mask_w = ld_mask < W ? ld_mask : W;
+  a.K = K;
+  a.out_idx = out_idx;
+  a.out_val = out_val;
+  a.first = 1;
+  return launched(idx::launch_topk(a, (hipStream_t)stream));
+}
+
+idx_status idx_logits_topk_fused(const idx_problem *p, int32_t K, int32_t block_k, int32_t row_chunk,
+                                 const uint8_t *mask, int64_t ld_mask, int32_t *out_idx, float *out_val, void *ws,
+                                 size_t ws_bytes, void *stream) {
+  idx_status st = check_problem(p, true);
+  if (st) return st;
+  if (!out_idx) return IDX_E_NULL;
+  if (K < 1 || K > MAX_K) return IDX_E_PARAM;
+  const int32_t Bk = eff_block(p, block_k);
+  if ((st = check_block(Bk))) return st;
+  if (row_chunk < 0) return IDX_E_PARAM;
+  const int32_t Tc = eff_chunk(p, row_chunk);
+  if (mask && ld_mask < 0) return IDX_E_SHAPE;
+  if (!aligned(out_idx, 4) || (out_val && !aligned(out_val, 4))) return IDX_E_ALIGN;
+  const size_t need = fused_ws(Tc, Bk, K);
+  if (p->T == 0) return IDX_OK;
+  if (!ws) return IDX_E_NULL;
+  if (ws_bytes < need) return IDX_E_WORKSPACE;
+  if (!aligned(ws, 256)) return IDX_E_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  Carve cv{(uint8_t *)ws};
+  float *scratch = cv.take<float>((size_t)Tc * Bk);
+  float *vbuf = cv.take<float>((size_t)Tc * K);
+  for (int32_t r0 = 0; r0 < p->T; r0 += Tc) {
+    const int32_t nr = std::min(Tc, p->T - r0);
+    float *vals = out_val ? out_val + (int64_t)r0 * K : vbuf;
+    int32_t kb = 0;
+    do {
+      const int32_t nk = std::min(Bk, p->L - kb);
+      if (nk > 0) {
+        idx::LogitsArgs a = logits_args(p, r0, nr, kb, kb + nk, scratch, Bk, nk);
+        if ((st = launched(idx::launch_logits(a, p->k_fmt, p->H, idx::STORE_BLOCK, s)))) return st;
+      }
+      idx::TopkArgs b{};
+      b.vals = scratch;
+      b.ld = Bk;
+      b.ncols = nk > 0 ? nk : 0;
+      b.block = Bk;
+      b.ks = p->ks;
+      b.ke = p->ke;
+      b.row0 = r0;
+      b.nrows = nr;
+      b.mode = idx::TOPK_BLOCK;
+      b.key0 = kb;
+      b.pool = 1;
+      b.mask = mask;
+      b.ld_mask = ld_mask;
+      b.mask_w = ld_mask;
+      b.K = K;
+      b.out_idx = out_idx + (int64_t)r0 * K;
+      b.out_val = vals;
+      b.first = kb == 0;
+      if ((st = launched(idx::launch_topk(b, s)))) return st;
+      kb += Bk;
+    } while (kb < p->L);
+  }
+  return IDX_OK;
+}
+
+idx_status idx_block_candidates(const idx_problem *p, const float *logits, int64_t ld, int32_t pool,
+                                int32_t n_blocks, int32_t block_k, int32_t row_chunk, uint8_t *mask, int64_t ld_mask,
+                                int32_t W, int32_t *out_blocks, void *ws, size_t ws_bytes, void *stream) {
+  idx_status st = check_problem(p, logits == nullptr);
+  if (st) return st;
+  if (!mask) return IDX_E_NULL;
+  if (pool != 8) return IDX_E_UNSUPPORTED;
+  if (n_blocks < 1 || n_blocks > MAX_K) return IDX_E_PARAM;
+  if (W < 0 || W > MAX_W || ld_mask < W) return IDX_E_SHAPE;
+  if (logits && ld < W) return IDX_E_SHAPE;
+  if (row_chunk < 0) return IDX_E_PARAM;
+  if (out_blocks && !aligned(out_blocks, 4)) return IDX_E_ALIGN;
+  if (logits && !aligned(logits, 4)) return IDX_E_ALIGN;
+  const int32_t Tc = eff_chunk(p, row_chunk);
+  const int32_t Bk = eff_block(p, block_k);
+  if (!logits && (st = check_block(Bk))) return st;
+  const int32_t pooled_cols = logits ? (W + pool - 1) / pool : Bk / pool;
+  const size_t need = cand_ws(Tc, pooled_cols, n_blocks);
+  if (p->T == 0) return IDX_OK;
+  if (!ws) return IDX_E_NULL;
+  if (ws_bytes < need) return IDX_E_WORKSPACE;
+  if (!aligned(ws, 256)) return IDX_E_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  Carve cv{(uint8_t *)ws};
+  float *pooled = cv.take<float>((size_t)Tc * pooled_cols);
+  int32_t *bbuf = cv.take<int32_t>((size_t)Tc * n_blocks);
+  float *vbuf = cv.take<float>((size_t)Tc * n_blocks);
+  for (int32_t r0 = 0; r0 < p->T; r0 += Tc) {
+    const int32_t nr = std::min(Tc, p->T - r0);
+    int32_t *blocks = out_blocks ? out_blocks + (int64_t)r0 * n_blocks : bbuf;
+    idx::TopkArgs b{};
+    b.ks = p->ks;
+    b.ke = p->ke;
+    b.row0 = r0;
+    b.nrows = nr;
+    b.pool = pool;
+    b.mask = nullptr;
+    b.K = n_blocks;
+    b.out_idx = blocks;
+    b.out_val = vbuf;
+    if (logits) {
+      if ((st = launched(idx::launch_pool_dense(logits + (int64_t)r0 * ld, ld, W, p->ks, p->ke, r0, nr, pool, pooled,
+                                                pooled_cols, pooled_cols, s))))
+        return st;
+      b.vals = pooled;
+      b.ld = pooled_cols;
+      b.ncols = pooled_cols;
+      b.block = MAX_BLOCK;
+      b.mode = idx::TOPK_POOL_DENSE;
+      b.key0 = 0;
+      b.first = 1;
+      if ((st = launched(idx::launch_topk(b, s)))) return st;
+    } else {
+      int32_t kb = 0;
+      do {
+        const int32_t nk = std::min(Bk, p->L - kb);
+        if (nk > 0) {
+          idx::LogitsArgs a = logits_args(p, r0, nr, kb, kb + nk, pooled, pooled_cols, (nk + pool - 1) / pool);
+          if ((st = launched(idx::launch_logits(a, p->k_fmt, p->H, idx::STORE_POOL8, s)))) return st;
+        }
+        b.vals = pooled;
+        b.ld = pooled_cols;
+        b.ncols = nk > 0 ? (nk + pool - 1) / pool : 0;
+        b.block = MAX_BLOCK;
+        b.mode = idx::TOPK_POOL_BLOCK;
+        b.key0 = kb;
+        b.first = kb == 0;
+        if ((st = launched(idx::launch_topk(b, s)))) return st;
+        kb += Bk;
+      } while (kb < p->L);
+    }
+    if ((st = launched(idx::launch_expand_mask(blocks, n_blocks, p->ks, p->ke, r0, nr, pool, W, mask, ld_mask, s))))
+      return st;
+  }
+  return IDX_OK;
+}
+
+idx_status idx_ragged_windows(const int32_t *cu_q, const int32_t *cu_k, int32_t B, int32_t T, int32_t *ks,
+                              int32_t *ke, void *stream) {
+  if (!cu_q || !cu_k || !ks || !ke) return IDX_E_NULL;
+  if (B < 0 || T < 0) return IDX_E_SHAPE;
+  if (!aligned(cu_q, 4) || !aligned(cu_k, 4) || !aligned(ks, 4) || !aligned(ke, 4)) return IDX_E_ALIGN;
+  return launched(idx::launch_ragged(cu_q, cu_k, B, T, ks, ke, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Internal interface between the C ABI layer (api.cpp) and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace idx {
+
+enum LogitsMode { STORE_DENSE = 0, STORE_BLOCK = 1, STORE_POOL8 = 2 };
+
+// One launch of the scoring kernel: rows [row0, row0 + nrows) against absolute
+// keys [key_lo, key_hi), split into nsplit workgroup ranges of `split` keys.
+struct LogitsArgs {
+  const uint8_t *q;
+  const float *q_scale;
+  const uint8_t *k;
+  const uint8_t *k_scale;  // fp8: float[L] bytes; MXFP4: uint8 [L, 4]
+  const float *w;
+  const int32_t *ks;
+  const int32_t *ke;
+  int32_t L;
+  float scale;
+  int32_t row0, nrows;
+  int32_t key_lo, key_hi;
+  int32_t split, nsplit;
+  float *out;     // row r of the launch is out + r * ld
+  int64_t ld;
+  int32_t wcols;  // columns available in an output row (dense W, block nkeys, pool ceil(nkeys/8))
+};
+
+hipError_t launch_logits(const LogitsArgs &a, int k_fmt, int H, int mode, hipStream_t s);
+
+// Top-K over row-major fp32 values (one workgroup per row, running top-K kept
+// across passes).  Row r of the launch is problem row t = row0 + r.  Column c
+// of that row is candidate id
+//   TOPK_DENSE:        ks[t] + c              (absolute key; row-relative logits)
+//   TOPK_BLOCK:        key0 + c               (absolute key; key-block scratch)
+//   TOPK_POOL_DENSE:   c                      (pooled block id; row-relative)
+//   TOPK_POOL_BLOCK:   (key0 - ks[t]) / pool + c   (pooled block id; key-block scratch)
+// Valid ids are [ks, ke) for keys and [0, ceil((ke - ks) / pool)) for blocks.
+enum TopkMode { TOPK_DENSE = 0, TOPK_BLOCK = 1, TOPK_POOL_DENSE = 2, TOPK_POOL_BLOCK = 3 };
+struct TopkArgs {
+  const float *vals;
+  int64_t ld;
+  int32_t ncols;          // columns in one row of vals
+  int32_t block;          // columns scored per pass (<= 32768)
+  const int32_t *ks, *ke;
+  int32_t row0, nrows;
+  int32_t mode;
+  int32_t key0;
+  int32_t pool;
+  const uint8_t *mask;    // nullable (key modes only); byte (id - ks) of row t
+  int64_t ld_mask;
+  int64_t mask_w;         // mask columns per row; bytes at or past it count as 0
+  int32_t K;
+  int32_t *out_idx;       // row r at out_idx + r * K
+  float *out_val;         // row r at out_val + r * K
+  int32_t first;          // 1: no running state yet (out_* contents are ignored)
+};
+hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
+
+// Dense-logits helpers
+hipError_t launch_fill_tail(float *logits, int64_t ld, int32_t W, const int32_t *ks, const int32_t *ke,
+                            int32_t row0, int32_t nrows, hipStream_t s);
+hipError_t launch_pool_dense(const float *logits, int64_t ld, int32_t W, const int32_t *ks, const int32_t *ke,
+                             int32_t row0, int32_t nrows, int32_t pool, float *out, int64_t ld_out,
+                             int32_t ncols_out, hipStream_t s);
+hipError_t launch_expand_mask(const int32_t *blocks, int32_t n_blocks, const int32_t *ks, const int32_t *ke,
+                              int32_t row0, int32_t nrows, int32_t pool, int32_t W, uint8_t *mask,
+                              int64_t ld_mask, hipStream_t s);
+hipError_t launch_ragged(const int32_t *cu_q, const int32_t *cu_k, int32_t B, int32_t T, int32_t *ks,
+                         int32_t *ke, hipStream_t s);
+
+}  // namespace idx

@@ -1,0 +1,268 @@
+// Indexer scoring kernel for gfx950:
+//   I[t, s] = k_scale[s] * sum_h w'[t, h] * max(0, <q8[t, h, :], k8[s, :]>),  w' = w * q_scale * scale
+// for fp8 keys, and with the MXFP4 E8M0 block scales applied inside the MFMA for fp4 keys.
+// Folding the positive scales out of the ReLU is exact in real arithmetic
+// (max(0, a x) = a max(0, x) for a >= 0).  The contraction over D = 128 runs on
+// v_mfma_scale_f32_16x16x128_f8f6f4; the ReLU, head weighting and head sum run
+// on the VALU straight from the accumulators (P1 section 1: the dense indexer
+// scores T rows against the whole prefix; P2 Motivation: fp8 q x fp4 k).
+//
+// Operand layout of v_mfma_scale_f32_16x16x128_f8f6f4, as measured on gfx950:
+// lane l holds row (A) / column (B) l % 16; for fp8, byte b of lane group
+// g = l / 16 is k = 64 (b / 16) + 16 g + b % 16; for fp4, nibble p (low nibble
+// first) of lane group g is k = 32 g + p; lane l's E8M0 scale covers its row /
+// column and k block l / 16 (32 consecutive k); the result C[4 (l / 16) + j][l % 16]
+// is element j of lane l.  So an MXFP4 key's 32-element scale block is exactly
+// one lane's 16 bytes and one lane's scale byte.
+//
+// Work decomposition.  The 16 A rows of one MFMA are QR query rows x HPT heads
+// (QR = 128 / H: HPT = 4 for H = 32, 8 for H = 64), and a wave owns NT = 8
+// such tiles: all H heads of its QR query rows, held in registers (64 VGPRs of
+// q, 32 of w') for the whole launch.  Lane l then accumulates heads of query
+// (4 (l / 16)) / HPT for key l % 16, so the head sum is an in-lane FMA chain
+// plus, for H = 64, one v_permlane16_swap add.
+//
+// Keys stream through LDS in 8 KiB tiles (64 fp8 keys or 128 MXFP4 keys),
+// double buffered: each thread fetches its 16-byte chunks of tile i + 2 into
+// registers while tile i is scored and writes them to LDS after it (coalesced
+// 128/64-byte key rows).  16-byte chunks are XOR-swizzled inside a key row so
+// that the 16 lanes reading one chunk column hit distinct banks.  (Direct
+// global_load_lds staging is not used: the compiler cannot tell the prefetch
+// buffer from the one being read and drains every DMA before each LDS read.)
+// Output stores go through a buffer resource; lanes with nothing to store get
+// an out-of-range offset, so stores never branch.
+//
+// Grid: (row blocks of RPW = 16 rows) x (nsplit key splits).  Workgroup b
+// takes split b % nsplit, row block b / nsplit; when nsplit is a multiple of
+// 8 every split's workgroups land on one XCD (round-robin dispatch), so each
+// XCD's L2 only ever holds 1/8 of the keys.
+#include "kernels.h"
+
+#include <climits>
+
+namespace idx {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int OOB = (int)0x80000000;  // buffer offset past any num_records: the store is dropped
+constexpr int RSRC3 = 0x00020000;     // raw buffer, 32-bit elements
+
+// Chunk swizzle inside a key row.  fp8 rows hold 8 chunks of 16 bytes; MXFP4 rows 4.
+__device__ __forceinline__ int swz8(int n) { return (n & 7) ^ ((n >> 3) & 1); }
+__device__ __forceinline__ int swz4(int n) { return ((n >> 1) ^ (n >> 3)) & 3; }
+
+template <int KF, int H, int MODE, int NW>
+__global__ __launch_bounds__(NW * 64) void logits_kernel(LogitsArgs a) {
+  constexpr int QR = 128 / H;            // query rows per wave
+  constexpr int HPT = 16 / QR;           // heads of one row in a 16-row A tile
+  constexpr int NT = H / HPT;            // A tiles per wave (8)
+  constexpr int RPW = NW * QR;           // rows per workgroup
+  constexpr int KB = KF == 0 ? 128 : 64; // key bytes
+  constexpr int TK = KF == 0 ? 64 : 128; // keys per LDS stage (8 KiB either way)
+  constexpr int STAGE = TK * KB;
+  constexpr int LPT = STAGE / 16 / (NW * 64);  // 16-byte chunks per thread per stage
+  static_assert(LPT * NW * 64 * 16 == STAGE, "stage must split evenly over the workgroup");
+  static_assert(RPW <= 64 && TK <= NW * 64, "layout limits");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][STAGE];
+  __shared__ __attribute__((aligned(256))) uint32_t sbuf[2][TK];
+  __shared__ int32_t wg_range[2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (keeps buffer resources scalar)
+  const int split_i = blockIdx.x % a.nsplit;
+  const int rb = blockIdx.x / a.nsplit;
+  const int r_begin = a.row0 + rb * RPW;
+  const int r_end = min(r_begin + RPW, a.row0 + a.nrows);
+
+  // ---- key range of this workgroup: its split, clipped to the union of its rows' windows
+  if (wave == 0) {
+    int lo = INT_MAX, hi = INT_MIN;
+    if (lane < RPW && r_begin + lane < r_end) {
+      const int kst = max(a.ks[r_begin + lane], 0), ket = min(a.ke[r_begin + lane], a.L);
+      if (ket > kst) { lo = kst; hi = ket; }
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+      lo = min(lo, __shfl_xor(lo, off));
+      hi = max(hi, __shfl_xor(hi, off));
+    }
+    if (lane == 0) { wg_range[0] = lo; wg_range[1] = hi; }
+  }
+  __syncthreads();
+  const int split_lo = a.key_lo + split_i * a.split;
+  const int split_hi = min(split_lo + a.split, a.key_hi);
+  const int s_lo = max(split_lo, wg_range[0]);
+  const int s_hi = min(split_hi, wg_range[1]);
+  if (s_lo >= s_hi) return;  // uniform over the workgroup
+  const int tile0 = s_lo & ~(TK - 1);
+  const int ntiles = (s_hi - tile0 + TK - 1) / TK;
+
+  // ---- this wave's query rows: A fragments (q) and weights in registers
+  const int g = lane >> 4;        // lane group: k block of A/B, row group of C
+  const int n16 = lane & 15;      // A row (load) / C column (key)
+  const int wr = r_begin + wave * QR;
+  v8i qa[NT];
+  {
+    const int qi = n16 / HPT, hh = n16 % HPT;
+    const int t = min(wr + qi, r_end - 1);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const uint8_t *src = a.q + ((int64_t)t * H + HPT * i + hh) * 128;
+      const v4i lo = *(const v4i *)(src + 16 * g);       // k = 16 g .. 16 g + 15
+      const v4i hi = *(const v4i *)(src + 64 + 16 * g);  // k = 64 + 16 g .. 64 + 16 g + 15
+      qa[i] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    }
+  }
+  const int qo = (4 * g) / HPT;          // query of the C rows this lane holds
+  const int hbase = (4 * g) % HPT;
+  const int t_out = wr + qo;
+  const bool row_ok = t_out < r_end;
+  float wv[NT][4];
+  int kst, ket;
+  {
+    const int t = min(t_out, r_end - 1);
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int h = HPT * i + hbase + j;
+        wv[i][j] = a.w[(int64_t)t * H + h] * a.q_scale[(int64_t)t * H + h] * a.scale;
+      }
+    kst = max(a.ks[t], 0);
+    ket = min(a.ke[t], a.L);
+  }
+  // keys this lane may store: inside its row's window and inside the workgroup range
+  const int v_lo = max(kst, s_lo), v_hi = min(ket, s_hi);
+  const bool writer = row_ok && (QR == 4 || (g & 1) == 0);
+  // one buffer resource per wave over its QR output rows
+  const int wrow = min(wr, a.row0 + a.nrows - 1) - a.row0;
+  const int64_t ld = a.ld;
+  __amdgpu_buffer_rsrc_t orsrc =
+      __builtin_amdgcn_make_buffer_rsrc(a.out + (int64_t)wrow * ld, 0, (int)(QR * ld * 4), RSRC3);
+  const int obase = (t_out - a.row0 - wrow) * (int)ld;   // element offset of this lane's row
+
+  // ---- key stages: thread `tid` owns 16-byte LDS slots tid, tid + NW*64, ...
+  v4i kreg[LPT];
+  uint32_t sreg = 0;
+  auto fetch = [&](int tile) {
+    const int ts = tile0 + tile * TK;
+#pragma unroll
+    for (int it = 0; it < LPT; ++it) {
+      const int slot = it * NW * 64 + tid;
+      int key, chunk;
+      if (KF == 0) { key = slot >> 3; chunk = (slot & 7) ^ swz8(key); }
+      else { key = slot >> 2; chunk = (slot & 3) ^ swz4(key); }
+      const int gk = min(ts + key, a.L - 1);
+      kreg[it] = *(const v4i *)(a.k + (int64_t)gk * KB + chunk * 16);
+    }
+    if (tid < TK) sreg = *(const uint32_t *)(a.k_scale + (int64_t)min(ts + tid, a.L - 1) * 4);
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < LPT; ++it) *(v4i *)&kbuf[buf][(it * NW * 64 + tid) * 16] = kreg[it];
+    if (tid < TK) sbuf[buf][tid] = sreg;
+  };
+
+  fetch(0);
+  stash(0);
+  if (ntiles > 1) fetch(1);
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const int ts = tile0 + it * TK;
+#pragma unroll
+    for (int grp = 0; grp < TK / 16; ++grp) {
+      const int n = grp * 16 + n16;     // key within the tile
+      v8i bk;
+      int bscale = 0;
+      if (KF == 0) {
+        const int sw = swz8(n);
+        const v4i lo = *(const v4i *)&kbuf[buf][n * 128 + ((g ^ sw) << 4)];
+        const v4i hi = *(const v4i *)&kbuf[buf][n * 128 + (((4 + g) ^ sw) << 4)];
+        bk = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      } else {
+        const v4i v = *(const v4i *)&kbuf[buf][n * 64 + ((g ^ swz4(n)) << 4)];
+        bk = (v8i){v.x, v.y, v.z, v.w, 0, 0, 0, 0};
+        bscale = (sbuf[buf][n] >> (8 * g)) & 0xFF;
+      }
+      v4f c[NT];
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        if (KF == 0)
+          c[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[i], bk, (v4f){0, 0, 0, 0}, 0, 0, 0, 0, 0, 0);
+        else
+          c[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[i], bk, (v4f){0, 0, 0, 0}, 0, 4, 0, 127, 0,
+                                                                  bscale);
+      }
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = __builtin_fmaf(__builtin_fmaxf(c[i][j], 0.f), wv[i][j], acc);
+      if (QR == 2) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc), __float_as_uint(acc), false, false);
+        acc = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      }
+      const int s = ts + n;
+      float val = acc;
+      if (KF == 0) val *= __uint_as_float(sbuf[buf][n]);
+      const bool ok = writer && s >= v_lo && s < v_hi;
+      if (MODE == STORE_DENSE) {
+        const int col = s - kst;
+        const int off = (ok && col < a.wcols) ? (obase + col) * 4 : OOB;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), orsrc, off, 0, 0);
+      } else if (MODE == STORE_BLOCK) {
+        const int off = ok ? (obase + s - a.key_lo) * 4 : OOB;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), orsrc, off, 0, 0);
+      } else {
+        // max over the 8 aligned keys of this lane's half-row (quad swaps, then half-row mirror)
+        float m = ok ? val : -__builtin_inff();
+        m = __builtin_fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, false)));
+        m = __builtin_fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, false)));
+        m = __builtin_fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x141, 0xF, 0xF, false)));
+        const int col = (s - a.key_lo) >> 3;
+        const bool st = writer && (n16 & 7) == 0 && m != -__builtin_inff() && col < a.wcols;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), orsrc, st ? (obase + col) * 4 : OOB, 0, 0);
+      }
+    }
+    if (it + 1 < ntiles) {
+      stash(buf ^ 1);
+      if (it + 2 < ntiles) fetch(it + 2);
+    }
+    __syncthreads();
+  }
+}
+
+template <int KF, int H, int MODE>
+hipError_t launch3(const LogitsArgs &a, hipStream_t s) {
+  constexpr int NW = H == 32 ? 4 : 8;
+  constexpr int RPW = NW * (128 / H);
+  const int nrb = (a.nrows + RPW - 1) / RPW;
+  const int64_t grid = (int64_t)nrb * a.nsplit;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((logits_kernel<KF, H, MODE, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int KF, int H>
+hipError_t launch2(const LogitsArgs &a, int mode, hipStream_t s) {
+  switch (mode) {
+    case STORE_DENSE: return launch3<KF, H, STORE_DENSE>(a, s);
+    case STORE_BLOCK: return launch3<KF, H, STORE_BLOCK>(a, s);
+    default: return launch3<KF, H, STORE_POOL8>(a, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_logits(const LogitsArgs &a, int k_fmt, int H, int mode, hipStream_t s) {
+  if (k_fmt == 0) return H == 32 ? launch2<0, 32>(a, mode, s) : launch2<0, 64>(a, mode, s);
+  return H == 32 ? launch2<1, 32>(a, mode, s) : launch2<1, 64>(a, mode, s);
+}
+
+}  // namespace idx

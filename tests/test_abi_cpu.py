@@ -1,0 +1,116 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/idx.h declares, and rejects bad arguments on the host before any HIP
+call (so these calls never touch a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mqa_logits_top_amd as idx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return idx.load_library()
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "idx.h")).read()
+    return sorted(set(re.findall(r"^(?:idx_status|const char \*)\s*(idx_\w+)\(", src, re.M)))
+
+
+def test_exports_match_header(lib):
+    names = _declared()
+    assert set(names) == set(idx.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert idx.status_str(0) == "ok"
+    for s in range(1, 9):
+        assert idx.status_str(s) not in ("ok", "unknown status")
+    assert idx.status_str(99) == "unknown status"
+
+
+def _problem(**kw):
+    fake = 1 << 20   # 16-byte aligned, never dereferenced: every call below fails host checks
+    base = dict(q=fake, q_scale=fake, k=fake, k_scale=fake, k_fmt=0, w=fake, ks=fake, ke=fake,
+                T=4, H=32, D=128, L=1024, scale=1.0)
+    base.update(kw)
+    return idx.idx_problem(**base)
+
+
+def _fused(lib, p, K=64, block_k=1024, row_chunk=0, ws=1 << 20, ws_bytes=1 << 30, out_idx=1 << 20):
+    return lib.idx_logits_topk_fused(ctypes.byref(p), K, block_k, row_chunk, None, 0, out_idx, None, ws, ws_bytes,
+                                     None)
+
+
+def test_problem_validation(lib):
+    assert _fused(lib, _problem(D=64)) == 6            # UNSUPPORTED
+    assert _fused(lib, _problem(H=48)) == 6
+    assert _fused(lib, _problem(k_fmt=2)) == 4         # FORMAT
+    assert _fused(lib, _problem(q=None)) == 1          # NULL
+    assert _fused(lib, _problem(ks=None)) == 1
+    assert _fused(lib, _problem(T=-1)) == 2            # SHAPE
+    assert _fused(lib, _problem(scale=0.0)) == 3       # PARAM
+    assert _fused(lib, _problem(scale=float("nan"))) == 3
+    assert _fused(lib, _problem(q=(1 << 20) + 4)) == 8  # ALIGN
+    assert _fused(lib, _problem(), K=0) == 3
+    assert _fused(lib, _problem(), K=2049) == 3
+    assert _fused(lib, _problem(), block_k=300) == 3
+    assert _fused(lib, _problem(), block_k=65536) == 3
+    assert _fused(lib, _problem(), out_idx=None) == 1
+    assert _fused(lib, _problem(), ws=None) == 1
+    assert _fused(lib, _problem(), ws_bytes=100) == 5   # WORKSPACE
+    assert _fused(lib, _problem(), ws=(1 << 20) + 16) == 8
+
+
+def test_other_entry_validation(lib):
+    p = _problem()
+    f = 1 << 20
+    assert lib.idx_mqa_logits(ctypes.byref(p), None, 1024, 1024, None) == 1
+    assert lib.idx_mqa_logits(ctypes.byref(p), f, 100, 1024, None) == 2          # ld < W
+    assert lib.idx_mqa_logits(ctypes.byref(_problem(H=16)), f, 1024, 1024, None) == 6
+    assert lib.idx_mqa_logits_block(ctypes.byref(p), 0, 5, 0, 256, f, 256, None) == 2   # rows past T
+    assert lib.idx_mqa_logits_block(ctypes.byref(p), 0, 4, 100, 256, f, 256, None) == 3  # key0 % 256
+    assert lib.idx_topk(f, 1024, 1024, f, f, None, 0, 4, 0, 0, f, None, None, 0, None) == 3      # K = 0
+    assert lib.idx_topk(f, 100, 1024, f, f, None, 0, 4, 8, 0, f, None, None, 0, None) == 2       # ld < W
+    assert lib.idx_topk(f, 1024, 1024, f, f, f, 10, 4, 8, 0, f, None, None, 0, None) == 2        # ld_mask < W
+    assert lib.idx_topk(None, 1024, 1024, f, f, None, 0, 4, 8, 0, f, None, None, 0, None) == 1
+    assert lib.idx_topk(f, 1024, 1024, f, f, None, 0, 4, 8, 40000, f, None, None, 0, None) == 3  # block_k
+    assert lib.idx_block_candidates(ctypes.byref(p), None, 0, 4, 16, 1024, 0, f, 1024, 1024, None, f,
+                                    1 << 30, None) == 6    # pool != 8
+    assert lib.idx_block_candidates(ctypes.byref(p), None, 0, 8, 4096, 1024, 0, f, 1024, 1024, None, f,
+                                    1 << 30, None) == 3    # n_blocks > 2048
+    assert lib.idx_block_candidates(ctypes.byref(p), None, 0, 8, 16, 1024, 0, None, 1024, 1024, None, f,
+                                    1 << 30, None) == 1    # mask NULL
+    assert lib.idx_block_candidates(ctypes.byref(p), None, 0, 8, 16, 1024, 0, f, 10, 1024, None, f,
+                                    1 << 30, None) == 2    # ld_mask < W
+    assert lib.idx_ragged_windows(None, f, 2, 4, f, f, None) == 1
+    assert lib.idx_ragged_windows(f, f, -1, 4, f, f, None) == 2
+
+
+def test_workspace_sizes(lib):
+    p = _problem(T=2048, L=65536)
+    n = ctypes.c_size_t()
+    assert lib.idx_workspace_size(2, ctypes.byref(p), 2048, 32768, 0, 0, 0, 0, ctypes.byref(n)) == 0
+    assert n.value == 2048 * 32768 * 4 + 2048 * 2048 * 4
+    # row chunk bounds the workspace; the key count does not enter
+    p2 = _problem(T=16384, L=487936)
+    assert lib.idx_workspace_size(2, ctypes.byref(p2), 512, 32768, 4096, 0, 0, 0, ctypes.byref(n)) == 0
+    assert n.value == 4096 * 32768 * 4 + 4096 * 512 * 4
+    p3 = _problem(T=16384, L=65536)
+    m = ctypes.c_size_t()
+    assert lib.idx_workspace_size(2, ctypes.byref(p3), 512, 32768, 4096, 0, 0, 0, ctypes.byref(m)) == 0
+    assert m.value == n.value
+    assert lib.idx_workspace_size(3, ctypes.byref(p), 0, 32768, 0, 8, 2048, 0, ctypes.byref(n)) == 0
+    assert n.value == 2048 * 4096 * 4 + 2 * 2048 * 2048 * 4
+    assert lib.idx_workspace_size(4, ctypes.byref(p), 0, 0, 1024, 8, 2048, 65536, ctypes.byref(n)) == 0
+    assert n.value == 1024 * 8192 * 4 + 2 * 1024 * 2048 * 4
+    assert lib.idx_workspace_size(0, ctypes.byref(p), 0, 0, 0, 0, 0, 0, ctypes.byref(n)) == 0 and n.value == 0
+    assert lib.idx_workspace_size(2, ctypes.byref(p), 0, 32768, 0, 0, 0, 0, ctypes.byref(n)) == 3
+    assert lib.idx_workspace_size(9, ctypes.byref(p), 1, 256, 0, 0, 0, 0, ctypes.byref(n)) == 3

@@ -1,0 +1,212 @@
+"""HIP path vs the fp64 oracle on seeded inputs small enough for the oracle to
+score every row: several tiles and a ragged tail in rows and keys, both key
+formats and both head counts, every output mode of the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import mqa_logits_top_amd as idx
+import oracle
+import synth
+from checks import logits_ok, topk_ok
+
+pytestmark = pytest.mark.gpu
+
+
+def dev(p):
+    return idx.Inputs.from_host(p)
+
+
+def _rows_windows(T, L, kind, seed=0):
+    rng = np.random.default_rng(seed)
+    if kind == "causal":
+        return synth.causal_windows(T, L)
+    if kind == "random":
+        ks = rng.integers(0, L, T).astype(np.int32)
+        ke = np.minimum(ks + rng.integers(0, L, T), L).astype(np.int32)
+        ke[::7] = ks[::7]          # some empty windows
+        return ks, ke
+    raise ValueError(kind)
+
+
+CASES = [
+    # (T, L, H, k_fmt, windows)
+    (37, 1500, 32, synth.K_FP8, "causal"),
+    (37, 1500, 64, synth.K_FP8, "causal"),
+    (29, 1333, 64, synth.K_MXFP4, "causal"),
+    (21, 1100, 32, synth.K_MXFP4, "random"),
+    (45, 2000, 64, synth.K_FP8, "random"),
+]
+
+
+@pytest.fixture(scope="module", params=CASES, ids=lambda c: f"T{c[0]}-L{c[1]}-H{c[2]}-f{c[3]}-{c[4]}")
+def case(request):
+    T, L, H, fmt, win = request.param
+    ks, ke = _rows_windows(T, L, win, seed=T)
+    p = synth.make_problem(T, L, H, k_fmt=fmt, seed=T + H, ks=ks, ke=ke,
+                           dup_rows=(L // 20 if fmt == synth.K_MXFP4 else 0))
+    dq = oracle.Dequantised(p)
+    o = [oracle.row_logits(dq, t) for t in range(T)]
+    return p, dev(p), o
+
+
+def test_dense_logits(case):
+    p, d, o = case
+    W = max(p.W, 1)
+    g = idx.idx_mqa_logits(d, W).cpu().numpy()
+    ref = np.full((p.T, W), -np.inf)
+    for t, v in enumerate(o):
+        ref[t, :len(v)] = v
+    logits_ok(g, ref)
+
+
+def test_logits_block_rectangle(case):
+    p, d, o = case
+    row0, nrows, key0, nkeys = 3, p.T - 5, 256, 768
+    g = idx.idx_mqa_logits_block(d, row0, nrows, key0, nkeys).cpu().numpy()
+    for r in range(nrows):
+        t = row0 + r
+        lo, hi = max(int(p.ks[t]), key0), min(int(p.ke[t]), key0 + nkeys, p.L)
+        inw = np.zeros(nkeys, bool)
+        if hi > lo:
+            inw[lo - key0:hi - key0] = True
+            logits_ok(g[r, inw], o[t][lo - p.ks[t]:hi - p.ks[t]])
+        assert np.isnan(g[r, ~inw]).all(), "wrote outside the window"
+
+
+@pytest.mark.parametrize("K,block_k", [(1, 32768), (17, 256), (256, 1024), (700, 32768)])
+def test_topk_dense_vs_oracle(case, K, block_k):
+    p, d, o = case
+    W = max(p.W, 1)
+    lg = idx.idx_mqa_logits(d, W)
+    gi, gv = idx.idx_topk(lg, d.ks, d.ke, K, block_k=block_k)
+    topk_ok(gi.cpu().numpy(), gv.cpu().numpy(), o, p.ks, K)
+
+
+@pytest.mark.parametrize("block_k,row_chunk", [(256, 0), (1024, 8), (32768, 16), (512, 1)])
+def test_fused_equals_dense_bitwise(case, block_k, row_chunk):
+    p, d, o = case
+    K = 64
+    W = max(p.W, 1)
+    lg = idx.idx_mqa_logits(d, W)
+    di, dv = idx.idx_topk(lg, d.ks, d.ke, K)
+    fi, fv = idx.idx_logits_topk_fused(d, K, block_k=block_k, row_chunk=row_chunk)
+    assert torch.equal(di, fi)
+    assert torch.equal(dv.view(torch.int32), fv.view(torch.int32))
+    topk_ok(fi.cpu().numpy(), fv.cpu().numpy(), o, p.ks, K)
+
+
+def test_fused_masked_consumer(case):
+    p, d, o = case
+    K = 40
+    W = max(p.W, 1)
+    rng = np.random.default_rng(5)
+    mask = (rng.random((p.T, W)) < 0.3).astype(np.uint8)
+    fi, fv = idx.idx_logits_topk_fused(d, K, block_k=512, mask=torch.from_numpy(mask).cuda())
+    allowed = [mask[t, :len(o[t])].astype(bool) for t in range(p.T)]
+    topk_ok(fi.cpu().numpy(), fv.cpu().numpy(), o, p.ks, K, allowed=allowed)
+    # dense path with the same mask agrees bitwise
+    lg = idx.idx_mqa_logits(d, W)
+    di, dv = idx.idx_topk(lg, d.ks, d.ke, K, mask=torch.from_numpy(mask).cuda())
+    assert torch.equal(di, fi)
+
+
+def _check_candidates(p, o, mask_g, blocks_g, n_blocks, pool=8):
+    """GPU mask/blocks vs the oracle's block selection (near-ties within 1e-6 may swap)."""
+    W = mask_g.shape[1]
+    for t, v in enumerate(o):
+        P = oracle.pool_row(v, pool)
+        gb = blocks_g[t][blocks_g[t] >= 0] if blocks_g is not None else np.nonzero(mask_g[t, ::pool][:len(P)])[0]
+        # the GPU mask must be exactly the expansion of its own block set
+        want = np.zeros(W, np.uint8)
+        for b in gb:
+            want[b * pool:min((b + 1) * pool, len(v))] = 1
+        assert np.array_equal(mask_g[t], want), f"row {t}: mask is not the expansion of the kept blocks"
+        topk_ok(np.concatenate([gb, -np.ones(n_blocks - len(gb), np.int64)])[None], None, [P], [0], n_blocks,
+                what=f"blocks row {t}")
+
+
+@pytest.mark.parametrize("n_blocks", [5, 64])
+def test_candidates_dense_and_fused(case, n_blocks):
+    p, d, o = case
+    W = max(p.W, 1)
+    lg = idx.idx_mqa_logits(d, W)
+    blocks_d = torch.empty((p.T, n_blocks), dtype=torch.int32, device="cuda")
+    mask_d, _ = idx.idx_block_candidates(d, W, n_blocks=n_blocks, logits=lg, row_chunk=7, out_blocks=blocks_d)
+    _check_candidates(p, o, mask_d.cpu().numpy(), blocks_d.cpu().numpy(), n_blocks)
+    if (p.ks % 8).any():
+        return  # the fused pooling path requires windows that start on a multiple of 8
+    blocks_f = torch.empty((p.T, n_blocks), dtype=torch.int32, device="cuda")
+    mask_f, _ = idx.idx_block_candidates(d, W, n_blocks=n_blocks, block_k=512, row_chunk=16, out_blocks=blocks_f)
+    assert torch.equal(mask_d, mask_f) and torch.equal(blocks_d, blocks_f)
+
+
+def test_deterministic(case):
+    p, d, o = case
+    a = idx.idx_logits_topk_fused(d, 33, block_k=256)
+    b = idx.idx_logits_topk_fused(d, 33, block_k=256)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))
+    W = max(p.W, 1)
+    assert torch.equal(idx.idx_mqa_logits(d, W).view(torch.int32), idx.idx_mqa_logits(d, W).view(torch.int32))
+
+
+# ------------------------------------------------------------- selection alone, exact
+def _crafted_rows(W):
+    rng = np.random.default_rng(7)
+    rows = [
+        rng.normal(size=W),
+        np.full(W, 2.5),                                   # all equal
+        np.round(rng.normal(size=W), 1),                   # heavy ties
+        rng.normal(size=W) * 1e30,                         # huge range
+        1.0 + rng.integers(0, 3, W) * 2.0 ** -23,          # three adjacent fp32 values
+        np.where(rng.random(W) < 0.5, 0.0, -0.0),          # signed zeros only
+        -np.abs(rng.normal(size=W)),                       # all negative
+        np.concatenate([[1e38], np.full(W - 1, 1e-38)]),   # one outlier
+    ]
+    return np.stack(rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("K,block_k", [(1, 32768), (100, 256), (2048, 32768), (2048, 1024)])
+def test_topk_selection_exact(K, block_k):
+    W = 5000
+    vals = _crafted_rows(W)
+    T = vals.shape[0]
+    ks = np.array([0, 3, 0, 100, 0, 7, 0, 0], np.int32)
+    ke = np.array([W, W, 4000, W, W, 2000, 50, W], np.int32)   # row 6: window < K for K > 50
+    g = torch.from_numpy(np.ascontiguousarray(vals)).cuda()
+    gi, gv = idx.idx_topk(g, torch.from_numpy(ks).cuda(), torch.from_numpy(ke).cuda(), K, block_k=block_k)
+    gi, gv = gi.cpu().numpy(), gv.cpu().numpy()
+    for t in range(T):
+        win = vals[t, :ke[t] - ks[t]].astype(np.float64)
+        oi, ov = oracle.topk_row(win, int(ks[t]), K)
+        assert np.array_equal(gi[t], oi), f"row {t}"
+        assert np.array_equal(gv[t], ov.astype(np.float32)) or np.array_equal(np.abs(gv[t]), np.abs(ov)), f"row {t}"
+
+
+def test_ragged_windows_kernel():
+    cu_q = np.array([0, 3, 10, 10, 30], np.int32)
+    cu_k = np.array([0, 5, 15, 20, 70], np.int32)
+    T = 33
+    ks, ke = idx.idx_ragged_windows(torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda(), T)
+    rks, rke = synth.ragged_windows(cu_q, cu_k)
+    assert ks.cpu().numpy()[:30].tolist() == rks.tolist() and ke.cpu().numpy()[:30].tolist() == rke.tolist()
+    assert (ks.cpu().numpy()[30:] == 0).all() and (ke.cpu().numpy()[30:] == 0).all()
+
+
+def test_edge_shapes():
+    # one row, keys fewer than a tile, K larger than the window, empty and full windows
+    for T, L in [(1, 10), (3, 63), (17, 129)]:
+        ks = np.zeros(T, np.int32)
+        ke = np.minimum(np.arange(T, dtype=np.int32) * 5, L)
+        p = synth.make_problem(T, L, 32, seed=L, ks=ks, ke=ke)
+        d = dev(p)
+        dq = oracle.Dequantised(p)
+        o = [oracle.row_logits(dq, t) for t in range(T)]
+        fi, fv = idx.idx_logits_topk_fused(d, 8, block_k=256)
+        topk_ok(fi.cpu().numpy(), fv.cpu().numpy(), o, p.ks, 8)
+        W = max(p.W, 1)
+        g = idx.idx_mqa_logits(d, W).cpu().numpy()
+        ref = np.full((T, W), -np.inf)
+        for t, v in enumerate(o):
+            ref[t, :len(v)] = v
+        logits_ok(g, ref)
