@@ -1,0 +1,241 @@
+"""Benchmark of the dense prefill indexer on one MI355X.
+
+A step is one pass of the indexer's hot path over one batch: the per-row key
+windows are built from the batch's cu_seqlens on the device, then the fused
+key-blocked logits + top-K runs (scoring on fp8 MFMA with the ReLU-weighted
+head sum in registers, per-block exact top-K with a running merge, exact
+boundary refinement).  Workload: the GLM-5.1-shaped chunk, T = 2048 query rows
+against L = 65536 keys, H = 32, D = 128, fp8 q and k with per-row scales, causal
+windows, K = 2048, key blocks of 32768 (the pages' H200 microbenchmark shape).
+
+Printed: one JSON line.  value = scored in-window (row, key) pairs per second
+(inputs resident in HBM).  roofline: the scoring kernel's algorithmic fp8
+FLOPs (2 H D per in-window pair) per launch over its average launch duration
+(HIP events on the launch stream) against the fp8 dense MFMA peak.
+cpu_baseline: the fp64 CPU oracle on a bounded row sample of the same
+workload.  Extra fields: the MXFP4 logits stage at T = 2048, L = 102400, H = 64
+and the ragged candidate-source pipeline.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import mqa_logits_top_amd as idx  # noqa: E402
+import synth  # noqa: E402
+
+METRIC = "indexer (row,key) pairs/s fused logits+top-K; % fp8 MFMA peak; peak bytes"
+FP8_PEAK = 5.0e15      # MI355X dense fp8 MFMA, FLOP/s
+HBM_PEAK = 8.0e12
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def block_pairs(p, kb, nk):
+    lo = np.maximum(p.ks.astype(np.int64), kb)
+    hi = np.minimum(p.ke.astype(np.int64), kb + nk)
+    return int(np.maximum(hi - lo, 0).sum())
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("logits.hip", "kernels.h"):
+        with open(os.path.join(ROOT, "mqa_logits_top_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM bytes per scoring launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "logits_hbm_traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+        e = d.get(workload)
+        if e and e.get("kernel_source_hash") == kernel_source_hash():
+            return e["bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
+
+
+def time_events(fn, n, stream):
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def scoring_launch_ms(p, d, block_k, reps, stream):
+    """Average duration of the scoring kernel as the fused path launches it (key-block layout)."""
+    scratch = torch.empty((p.T, block_k), dtype=torch.float32, device="cuda")
+    blocks = [(kb, min(block_k, p.L - kb)) for kb in range(0, p.L, block_k)]
+    times, flops = [], 0
+    for _ in range(reps):
+        for kb, nk in blocks:
+            t = time_events(lambda: idx.idx_mqa_logits_block(d, 0, p.T, kb, nk, out=scratch, stream=stream), 1,
+                            stream)
+            times.append(t[0])
+    for kb, nk in blocks:
+        flops += 2 * p.H * p.D * block_pairs(p, kb, nk)
+    del scratch
+    avg_ms = float(np.mean(times))
+    return avg_ms, flops / len(blocks), len(blocks)
+
+
+def cpu_baseline(p, K, budget_s):
+    """The fp64 oracle (numpy, BLAS threads as configured) on a bounded row sample."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    t0 = time.perf_counter()
+    dq = oracle.Dequantised(p)
+    setup = time.perf_counter() - t0
+    order = np.random.default_rng(0).permutation(p.T)
+    pairs = 0
+    rows = 0
+    t1 = time.perf_counter()
+    for t in order:
+        v = oracle.row_logits(dq, int(t))
+        oracle.topk_row(v, int(p.ks[t]), K)
+        pairs += len(v)
+        rows += 1
+        if time.perf_counter() - t1 > budget_s and rows >= 4:
+            break
+    el = time.perf_counter() - t1
+    return {"value": pairs / el, "unit": "pairs/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows} of {p.T} rows (random order, seed 0), full windows, logits + top-{K}; "
+                      f"{pairs} pairs in {el:.1f} s (+{setup:.1f} s dequantisation, not counted)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the indexer shards by "
+              f"query rows with no exchange, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    name = "glm_chunk"
+    p = synth.make_config(name)
+    c = p.meta
+    K, Bk = c["K"], c["block_k"]
+    d = idx.Inputs.from_host(p, device=dev)
+    cu_q = torch.tensor([0, p.T], dtype=torch.int32, device=dev)
+    cu_k = torch.tensor([0, p.L], dtype=torch.int32, device=dev)
+    ws = torch.empty(idx.idx_workspace_size(idx.IDX_OP_LOGITS_TOPK_FUSED, d, K=K, block_k=Bk), dtype=torch.uint8,
+                     device=dev)
+    out_idx = torch.empty((p.T, K), dtype=torch.int32, device=dev)
+    out_val = torch.empty((p.T, K), dtype=torch.float32, device=dev)
+    ks = torch.empty(p.T, dtype=torch.int32, device=dev)
+    ke = torch.empty(p.T, dtype=torch.int32, device=dev)
+    lib = idx.load_library()
+    import ctypes
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    def step():
+        # windows from cu_seqlens (one request: the chunk is the tail of its prefix), then the fused indexer
+        st = lib.idx_ragged_windows(idx._ptr(cu_q), idx._ptr(cu_k), 1, p.T, idx._ptr(ks), idx._ptr(ke), sptr)
+        assert st == 0
+        dd = idx.Inputs(q=d.q, q_scale=d.q_scale, k=d.k, k_scale=d.k_scale, w=d.w, ks=ks, ke=ke, k_fmt=d.k_fmt)
+        idx.idx_logits_topk_fused(dd, K, block_k=Bk, out_idx=out_idx, out_val=out_val, ws=ws, stream=stream)
+
+    log(f"[bench] {name}: T={p.T} L={p.L} H={p.H} K={K} B_k={Bk} pairs={p.pairs}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert torch.equal(ks.cpu(), torch.from_numpy(p.ks)) and torch.equal(ke.cpu(), torch.from_numpy(p.ke))
+    assert idx.overflow_count(ws) == 0
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    value = p.pairs / (ms * 1e-3)
+    log(f"[bench] fused step {ms:.4f} ms ({wall / args.steps * 1e3:.4f} ms wall) -> {value:.4e} pairs/s")
+
+    # roofline of the dominant kernel (scoring), timed per launch on the launch stream
+    avg_ms, flops_per_launch, nblk = scoring_launch_ms(p, d, Bk, max(args.steps // 2, 3), stream)
+    achieved = flops_per_launch / (avg_ms * 1e-3)
+    traffic = load_traffic(name)
+    roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": FP8_PEAK / 1e12, "unit": "TFLOP/s",
+            "frac": achieved / FP8_PEAK, "traffic": traffic,
+            "kernel": "logits_kernel (fp8 keys, H=32, key-block store)", "avg_launch_ms": avg_ms,
+            "launches_per_step": nblk, "flop_per_launch": flops_per_launch}
+    log(f"[bench] scoring kernel {avg_ms:.4f} ms/launch -> {achieved / 1e12:.1f} TFLOP/s "
+        f"({100 * achieved / FP8_PEAK:.1f}% of fp8 peak)")
+
+    peak_bytes = int(ws.numel())
+    out = {"metric": METRIC, "value": value, "unit": "pairs/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "fp8", "data": "synthetic (seeded N(0,1) q/k quantised to fp8, w U(0,1))",
+           "config": {"workload": "glm_chunk: T=2048 L=65536 H=32 D=128 fp8 q/k per-row scales, causal windows, "
+                                  "top-K=2048, fused key blocks B_k=32768",
+                      "T": p.T, "L": p.L, "H": p.H, "D": p.D, "K": K, "block_k": Bk, "pairs_per_step": p.pairs},
+           "tflops": 2 * p.H * p.D * p.pairs / (ms * 1e-3) / 1e12,
+           "fp8_peak_frac_step": 2 * p.H * p.D * p.pairs / (ms * 1e-3) / FP8_PEAK,
+           "peak_transient_bytes": peak_bytes,
+           "roofline": roof}
+    del ws
+
+    if not args.no_extra:
+        extra = {}
+        # MXFP4-key logits stage at the DeepSeek-V4-like shape (T=2048, L=102400, H=64)
+        p3 = synth.make_config("dsv4_mxfp4")
+        d3 = idx.Inputs.from_host(p3, device=dev)
+        a3, f3, n3 = scoring_launch_ms(p3, d3, p3.meta["block_k"], 3, stream)
+        extra["dsv4_mxfp4_logits_stage"] = {"avg_launch_ms": a3, "tflops": f3 / (a3 * 1e-3) / 1e12,
+                                            "fp8_peak_frac": f3 / (a3 * 1e-3) / FP8_PEAK}
+        K3 = p3.meta["K"]
+        ws3 = torch.empty(idx.idx_workspace_size(idx.IDX_OP_LOGITS_TOPK_FUSED, d3, K=K3, block_k=p3.meta["block_k"]),
+                          dtype=torch.uint8, device=dev)
+        ft = time_events(lambda: idx.idx_logits_topk_fused(d3, K3, block_k=p3.meta["block_k"], ws=ws3,
+                                                           stream=stream), 5, stream)
+        extra["dsv4_mxfp4_fused"] = {"ms": float(np.median(ft)), "pairs_per_s": p3.pairs / (np.median(ft) * 1e-3),
+                                     "peak_transient_bytes": int(ws3.numel())}
+        log(f"[bench] dsv4_mxfp4 scoring {extra['dsv4_mxfp4_logits_stage']['tflops']:.1f} TFLOP/s, fused "
+            f"{np.median(ft):.3f} ms")
+        del d3, ws3
+        out["extra"] = extra
+
+    if not args.no_cpu:
+        log(f"[bench] cpu baseline (oracle, ~{args.cpu_budget:.0f} s)")
+        out["cpu_baseline"] = cpu_baseline(p, K, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -32,7 +32,7 @@ IDX_OP_BLOCK_CANDIDATES_DENSE = 4
 STATUS = {0: "IDX_OK", 1: "IDX_E_NULL", 2: "IDX_E_SHAPE", 3: "IDX_E_PARAM", 4: "IDX_E_FORMAT",
           5: "IDX_E_WORKSPACE", 6: "IDX_E_UNSUPPORTED", 7: "IDX_E_LAUNCH", 8: "IDX_E_ALIGN"}
 
-EXPORTS = ("idx_mqa_logits", "idx_mqa_logits_block", "idx_topk", "idx_logits_topk_fused",
+EXPORTS = ("idx_mqa_logits", "idx_mqa_logits_block", "idx_topk", "idx_logits_topk_fused", "idx_refine_topk",
            "idx_block_candidates", "idx_workspace_size", "idx_ragged_windows", "idx_status_str")
 
 
@@ -66,6 +66,7 @@ def load_library():
     lib.idx_mqa_logits_block.argtypes = [P, i32, i32, i32, i32, VP, i64, VP]
     lib.idx_topk.argtypes = [VP, i64, i32, VP, VP, VP, i64, i32, i32, i32, VP, VP, VP, sz, VP]
     lib.idx_logits_topk_fused.argtypes = [P, i32, i32, i32, VP, i64, VP, VP, VP, sz, VP]
+    lib.idx_refine_topk.argtypes = [P, VP, VP, i64, i32, i32, i32, VP, VP, VP, sz, VP]
     lib.idx_block_candidates.argtypes = [P, VP, i64, i32, i32, i32, i32, VP, i64, i32, VP, VP, sz, VP]
     lib.idx_workspace_size.argtypes = [i32, P, i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
     lib.idx_ragged_windows.argtypes = [VP, VP, i32, i32, VP, VP, VP]
@@ -211,6 +212,37 @@ def idx_logits_topk_fused(p: Inputs, K: int, block_k: int = 32768, row_chunk: in
         ctypes.byref(s), K, block_k, row_chunk, _ptr(mask), mask.stride(0) if mask is not None else 0,
         _ptr(out_idx), _ptr(out_val), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
     return out_idx, out_val
+
+
+RESERVE = 512   # extra candidates the exact boundary refinement keeps per row
+REFINE_WS = 1280
+
+
+def candidate_capacity(K: int) -> int:
+    return min(K + RESERVE, 2560)
+
+
+def idx_refine_topk(p: Inputs, cand_idx: torch.Tensor, cand_val: torch.Tensor, K: int, pool: int = 1,
+                    out_idx: Optional[torch.Tensor] = None, out_val: Optional[torch.Tensor] = None,
+                    ws: Optional[torch.Tensor] = None, with_values: bool = True, stream=None):
+    dev = cand_idx.device
+    T, Kc = int(cand_idx.shape[0]), int(cand_idx.shape[1])
+    if out_idx is None:
+        out_idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    if out_val is None and with_values:
+        out_val = torch.empty((T, K), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = _workspace(REFINE_WS, dev)
+    s = p.struct()
+    _check("idx_refine_topk", load_library().idx_refine_topk(
+        ctypes.byref(s), _ptr(cand_idx), _ptr(cand_val), cand_idx.stride(0), Kc, K, pool, _ptr(out_idx),
+        _ptr(out_val), _ptr(ws), ws.numel(), _stream(stream)))
+    return out_idx, out_val
+
+
+def overflow_count(ws: torch.Tensor) -> int:
+    """Rows of the last call on this workspace whose candidate list could not settle the boundary."""
+    return int(ws[:4].view(torch.int32).item())
 
 
 def idx_block_candidates(p: Inputs, W: int, pool: int = 8, n_blocks: int = 2048,

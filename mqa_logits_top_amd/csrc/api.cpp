@@ -14,6 +14,8 @@
 namespace {
 
 constexpr int32_t MAX_K = 2048;
+constexpr int32_t RESERVE = 512;   // extra candidates kept for the exact boundary refinement
+constexpr int32_t MAX_KC = 2560;
 constexpr int32_t MAX_BLOCK = 32768;
 constexpr int32_t MAX_W = 1 << 22;
 constexpr int32_t KEY_ALIGN = 256;
@@ -102,11 +104,66 @@ struct Carve {
   }
 };
 
+int32_t cand_cap(int32_t K) { return K + RESERVE < MAX_KC ? K + RESERVE : MAX_KC; }
+
+// Workspace layout (every region 256-byte aligned):
+//   [0, 256)            uint32 overflow counter of the last call, then free
+//   key-bound partials  256 floats
+//   candidate ids/vals  [Tc, Kc] each
+//   scratch             [Tc, Bk] fp32 scores (or [Tc, Bk / pool] pooled maxima)
+constexpr size_t HEAD = 256 + 1024;
+size_t refine_ws(int32_t Tc, int32_t Kc) { return HEAD + 2 * round_up_sz((size_t)Tc * Kc * 4, 256); }
 size_t fused_ws(int32_t Tc, int32_t Bk, int32_t K) {
-  return round_up_sz((size_t)Tc * Bk * 4, 256) + round_up_sz((size_t)Tc * K * 4, 256);
+  return refine_ws(Tc, cand_cap(K)) + round_up_sz((size_t)Tc * Bk * 4, 256);
 }
 size_t cand_ws(int32_t Tc, int32_t pooled_cols, int32_t n_blocks) {
-  return round_up_sz((size_t)Tc * pooled_cols * 4, 256) + 2 * round_up_sz((size_t)Tc * n_blocks * 4, 256);
+  return refine_ws(Tc, cand_cap(n_blocks)) + round_up_sz((size_t)Tc * pooled_cols * 4, 256) +
+         round_up_sz((size_t)Tc * n_blocks * 4, 256);
+}
+
+struct RefineWs {
+  uint32_t *overflow;
+  float *kpart;
+  int32_t *cidx;
+  float *cval;
+};
+RefineWs carve_refine(Carve &cv, int32_t Tc, int32_t Kc) {
+  RefineWs w;
+  w.overflow = cv.take<uint32_t>(64);
+  w.kpart = cv.take<float>(256);
+  w.cidx = cv.take<int32_t>((size_t)Tc * Kc);
+  w.cval = cv.take<float>((size_t)Tc * Kc);
+  return w;
+}
+
+idx::RefineArgs refine_args(const idx_problem *p, const RefineWs &w, int32_t row0, int32_t nrows, int32_t Kc,
+                            int32_t K, int32_t pool, int32_t *out_idx, float *out_val) {
+  idx::RefineArgs r{};
+  r.q = p->q;
+  r.q_scale = p->q_scale;
+  r.k = (const uint8_t *)p->k;
+  r.k_scale = (const uint8_t *)p->k_scale;
+  r.k_fmt = p->k_fmt;
+  r.w = p->w;
+  r.ks = p->ks;
+  r.ke = p->ke;
+  r.H = p->H;
+  r.L = p->L;
+  r.scale = p->scale;
+  r.row0 = row0;
+  r.nrows = nrows;
+  r.cand_idx = w.cidx;
+  r.cand_val = w.cval;
+  r.ld_cand = Kc;
+  r.Kc = Kc;
+  r.K = K;
+  r.pool = pool;
+  r.kmax_part = w.kpart;
+  r.npart = idx::key_bound_parts(p->L);
+  r.overflow = w.overflow;
+  r.out_idx = out_idx;
+  r.out_val = out_val;
+  return r;
 }
 
 }  // namespace
@@ -202,7 +259,7 @@ idx_status idx_topk(const float *logits, int64_t ld, int32_t W, const int32_t *k
   if (!logits || !ks || !ke || !out_idx) return IDX_E_NULL;
   if (T < 0 || W < 0 || ld < W) return IDX_E_SHAPE;
   if (mask && ld_mask < W) return IDX_E_SHAPE;
-  if (K < 1 || K > MAX_K) return IDX_E_PARAM;
+  if (K < 1 || K > MAX_KC) return IDX_E_PARAM;  // up to the refinement's candidate capacity
   if (block_k <= 0) block_k = MAX_BLOCK;
   if (block_k > MAX_BLOCK) return IDX_E_PARAM;
   if (!aligned(logits, 4) || !aligned(out_idx, 4) || (out_val && !aligned(out_val, 4))) return IDX_E_ALIGN;
@@ -248,12 +305,15 @@ idx_status idx_logits_topk_fused(const idx_problem *p, int32_t K, int32_t block_
   if (ws_bytes < need) return IDX_E_WORKSPACE;
   if (!aligned(ws, 256)) return IDX_E_ALIGN;
   hipStream_t s = (hipStream_t)stream;
+  const int32_t Kc = cand_cap(K);
   Carve cv{(uint8_t *)ws};
+  RefineWs rw = carve_refine(cv, Tc, Kc);
   float *scratch = cv.take<float>((size_t)Tc * Bk);
-  float *vbuf = cv.take<float>((size_t)Tc * K);
+  if ((st = launched(idx::launch_key_bound((const uint8_t *)p->k, (const uint8_t *)p->k_scale, p->k_fmt, p->L,
+                                           rw.kpart, rw.overflow, s))))
+    return st;
   for (int32_t r0 = 0; r0 < p->T; r0 += Tc) {
     const int32_t nr = std::min(Tc, p->T - r0);
-    float *vals = out_val ? out_val + (int64_t)r0 * K : vbuf;
     int32_t kb = 0;
     do {
       const int32_t nk = std::min(Bk, p->L - kb);
@@ -276,15 +336,48 @@ idx_status idx_logits_topk_fused(const idx_problem *p, int32_t K, int32_t block_
       b.mask = mask;
       b.ld_mask = ld_mask;
       b.mask_w = ld_mask;
-      b.K = K;
-      b.out_idx = out_idx + (int64_t)r0 * K;
-      b.out_val = vals;
+      b.K = Kc;
+      b.out_idx = rw.cidx;
+      b.out_val = rw.cval;
       b.first = kb == 0;
       if ((st = launched(idx::launch_topk(b, s)))) return st;
       kb += Bk;
     } while (kb < p->L);
+    idx::RefineArgs r = refine_args(p, rw, r0, nr, Kc, K, 1, out_idx + (int64_t)r0 * K,
+                                    out_val ? out_val + (int64_t)r0 * K : nullptr);
+    if ((st = launched(idx::launch_refine(r, s)))) return st;
   }
   return IDX_OK;
+}
+
+idx_status idx_refine_topk(const idx_problem *p, const int32_t *cand_idx, const float *cand_val, int64_t ld_cand,
+                           int32_t Kc, int32_t K, int32_t pool, int32_t *out_idx, float *out_val, void *ws,
+                           size_t ws_bytes, void *stream) {
+  idx_status st = check_problem(p, true);
+  if (st) return st;
+  if (!cand_idx || !cand_val || !out_idx) return IDX_E_NULL;
+  if (K < 1 || K > MAX_K || Kc < K || Kc > MAX_KC) return IDX_E_PARAM;
+  if (pool != 1 && pool != 8) return IDX_E_UNSUPPORTED;
+  if (ld_cand < Kc) return IDX_E_SHAPE;
+  if (!aligned(cand_idx, 4) || !aligned(cand_val, 4) || !aligned(out_idx, 4) || (out_val && !aligned(out_val, 4)))
+    return IDX_E_ALIGN;
+  if (p->T == 0) return IDX_OK;
+  if (!ws) return IDX_E_NULL;
+  if (ws_bytes < HEAD) return IDX_E_WORKSPACE;
+  if (!aligned(ws, 256)) return IDX_E_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  Carve cv{(uint8_t *)ws};
+  RefineWs rw;
+  rw.overflow = cv.take<uint32_t>(64);
+  rw.kpart = cv.take<float>(256);
+  rw.cidx = const_cast<int32_t *>(cand_idx);
+  rw.cval = const_cast<float *>(cand_val);
+  if ((st = launched(idx::launch_key_bound((const uint8_t *)p->k, (const uint8_t *)p->k_scale, p->k_fmt, p->L,
+                                           rw.kpart, rw.overflow, s))))
+    return st;
+  idx::RefineArgs r = refine_args(p, rw, 0, p->T, Kc, K, pool, out_idx, out_val);
+  r.ld_cand = ld_cand;
+  return launched(idx::launch_refine(r, s));
 }
 
 idx_status idx_block_candidates(const idx_problem *p, const float *logits, int64_t ld, int32_t pool,
@@ -311,12 +404,18 @@ idx_status idx_block_candidates(const idx_problem *p, const float *logits, int64
   if (!aligned(ws, 256)) return IDX_E_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   Carve cv{(uint8_t *)ws};
+  const int32_t Kc = logits ? n_blocks : cand_cap(n_blocks);
+  RefineWs rw = carve_refine(cv, Tc, cand_cap(n_blocks));
   float *pooled = cv.take<float>((size_t)Tc * pooled_cols);
-  int32_t *bbuf = cv.take<int32_t>((size_t)Tc * n_blocks);
-  float *vbuf = cv.take<float>((size_t)Tc * n_blocks);
+  int32_t *kept = cv.take<int32_t>((size_t)Tc * n_blocks);
+  if (!logits) {
+    if ((st = launched(idx::launch_key_bound((const uint8_t *)p->k, (const uint8_t *)p->k_scale, p->k_fmt, p->L,
+                                             rw.kpart, rw.overflow, s))))
+      return st;
+  }
   for (int32_t r0 = 0; r0 < p->T; r0 += Tc) {
     const int32_t nr = std::min(Tc, p->T - r0);
-    int32_t *blocks = out_blocks ? out_blocks + (int64_t)r0 * n_blocks : bbuf;
+    int32_t *blocks = out_blocks ? out_blocks + (int64_t)r0 * n_blocks : kept;
     idx::TopkArgs b{};
     b.ks = p->ks;
     b.ke = p->ke;
@@ -324,10 +423,11 @@ idx_status idx_block_candidates(const idx_problem *p, const float *logits, int64
     b.nrows = nr;
     b.pool = pool;
     b.mask = nullptr;
-    b.K = n_blocks;
-    b.out_idx = blocks;
-    b.out_val = vbuf;
+    b.K = Kc;
     if (logits) {
+      // selection is exact on the given logits
+      b.out_idx = blocks;
+      b.out_val = rw.cval;
       if ((st = launched(idx::launch_pool_dense(logits + (int64_t)r0 * ld, ld, W, p->ks, p->ke, r0, nr, pool, pooled,
                                                 pooled_cols, pooled_cols, s))))
         return st;
@@ -340,6 +440,8 @@ idx_status idx_block_candidates(const idx_problem *p, const float *logits, int64
       b.first = 1;
       if ((st = launched(idx::launch_topk(b, s)))) return st;
     } else {
+      b.out_idx = rw.cidx;
+      b.out_val = rw.cval;
       int32_t kb = 0;
       do {
         const int32_t nk = std::min(Bk, p->L - kb);
@@ -357,6 +459,9 @@ idx_status idx_block_candidates(const idx_problem *p, const float *logits, int64
         if ((st = launched(idx::launch_topk(b, s)))) return st;
         kb += Bk;
       } while (kb < p->L);
+      // exact boundary: blocks scored by the max of their keys' exact scores
+      idx::RefineArgs r = refine_args(p, rw, r0, nr, Kc, n_blocks, pool, blocks, nullptr);
+      if ((st = launched(idx::launch_refine(r, s)))) return st;
     }
     if ((st = launched(idx::launch_expand_mask(blocks, n_blocks, p->ks, p->ke, r0, nr, pool, W, mask, ld_mask, s))))
       return st;

@@ -58,6 +58,34 @@ struct TopkArgs {
 };
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
 
+// Exact boundary refinement of per-row candidate lists (see refine.hip).
+struct RefineArgs {
+  const uint8_t *q;
+  const float *q_scale;
+  const uint8_t *k;
+  const uint8_t *k_scale;
+  int32_t k_fmt;
+  const float *w;
+  const int32_t *ks, *ke;
+  int32_t H, L;
+  float scale;
+  int32_t row0, nrows;
+  const int32_t *cand_idx;  // row r at cand_idx + r * ld_cand: ids ascending, -1 padded
+  const float *cand_val;
+  int64_t ld_cand;
+  int32_t Kc, K;
+  int32_t pool;             // 1: ids are keys; > 1: ids are pooled blocks of `pool` keys from ks
+  const float *kmax_part;   // partial maxima of |k| (launch_key_bound)
+  int32_t npart;
+  uint32_t *overflow;       // rows whose band may extend below the list
+  int32_t *out_idx;         // row r at out_idx + r * K
+  float *out_val;
+};
+int key_bound_parts(int L);
+hipError_t launch_key_bound(const uint8_t *k, const uint8_t *k_scale, int k_fmt, int L, float *part,
+                            uint32_t *overflow, hipStream_t s);
+hipError_t launch_refine(const RefineArgs &a, hipStream_t s);
+
 // Dense-logits helpers
 hipError_t launch_fill_tail(float *logits, int64_t ld, int32_t W, const int32_t *ks, const int32_t *ke,
                             int32_t row0, int32_t nrows, hipStream_t s);

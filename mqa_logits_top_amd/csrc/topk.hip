@@ -5,22 +5,28 @@
 //
 // One workgroup (512 threads) owns one row.  The running top-K (ids ascending,
 // fp32 values) lives in LDS while the row's columns are consumed in passes of
-// up to 32768 values held in registers (64 per thread).  Each pass:
+// up to 32768 values held in registers.  Thread `tid` owns the contiguous
+// columns P + 64 tid .. P + 64 tid + 63 of a pass starting at column P and the
+// contiguous running slots 5 tid .. 5 tid + 4, so id order is thread-major and
+// every ordered compaction is one per-thread count plus one block-wide
+// exclusive scan (all register indices are compile-time constants).  A pass:
 //   1. map fp32 values to order-preserving uint32 keys (0 is reserved for
-//      "not a candidate": excluded by window, mask or padding);
+//      "not a candidate": excluded by window, mask, padding, or -- once the
+//      running list is full -- by not beating its smallest entry, which wins
+//      every tie because running ids precede the pass's ids);
 //   2. find the key of the K-th largest candidate (running + pass), counting
 //      multiplicity.  The candidate key interval [lo, hi] is narrowed by
 //      histogram levels: bins are (key - lo) >> s with the smallest s that
 //      gives < 2048 bins, so each level consumes >= 11 bits of the interval and
 //      at most three levels are needed; once <= 512 candidates remain they are
 //      ranked directly in LDS;
-//   3. select keys above the threshold and, among keys equal to it, the ones
-//      with the lowest ids (total order: value desc, id asc), writing them in
-//      id order with ordered ballot scans.  Running ids precede the pass's ids,
-//      so the merged list stays ascending.
+//   3. keep keys above the threshold and, among keys equal to it, the ones
+//      with the lowest ids (total order: value desc, id asc), written in id
+//      order.  Running ids precede the pass's ids, so the list stays ascending.
 // All steps are integer/comparison work on exact keys, so the result is the
 // unique top-K under the total order, independent of how rows or columns are
 // split into launches and passes.
+#include "common.h"
 #include "kernels.h"
 
 namespace idx {
@@ -28,29 +34,20 @@ namespace {
 
 constexpr int NTH = 512;
 constexpr int NWV = NTH / 64;
-constexpr int VPT = 64;           // pass values per thread
-constexpr int RS = 4;             // running slots per thread (K <= 2048)
+constexpr int VPT = 64;           // pass values per thread (contiguous columns)
+constexpr int SPAN = NTH * VPT;   // columns one pass can hold
+constexpr int RS = 5;             // running slots per thread (K <= 2560)
 constexpr int KMAX = RS * NTH;
 constexpr int NB = 2048;          // histogram bins
 constexpr int CAP = 512;          // direct ranking threshold
-constexpr int NSEG = (RS + VPT) * NWV;
-
-__device__ __forceinline__ uint32_t fkey(float v) {
-  uint32_t u = __float_as_uint(v);
-  if (u == 0x80000000u) u = 0;  // -0 ranks as +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float kval(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
 
 struct Smem {
   int run_id[2][KMAX];
   float run_val[2][KMAX];
   uint32_t hist[NB];
   uint32_t cand[CAP];
-  int seg[NSEG + 1];
   uint32_t red[3][NWV];
+  uint32_t wsum[2][NWV];
   uint32_t bcast[4];
 };
 
@@ -68,7 +65,7 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
 }
 
 // Block-wide sum / min / max of one value per thread (all threads must call).
-__device__ uint32_t block_sum(Smem &sm, uint32_t x, int lane, int wave) {
+__device__ __forceinline__ uint32_t block_sum(Smem &sm, uint32_t x, int lane, int wave) {
   x = wave_sum(x);
   __syncthreads();
   if (lane == 0) sm.red[0][wave] = x;
@@ -78,7 +75,7 @@ __device__ uint32_t block_sum(Smem &sm, uint32_t x, int lane, int wave) {
   for (int w = 0; w < NWV; ++w) s += sm.red[0][w];
   return s;
 }
-__device__ void block_minmax(Smem &sm, uint32_t &lo, uint32_t &hi, int lane, int wave) {
+__device__ __forceinline__ void block_minmax(Smem &sm, uint32_t &lo, uint32_t &hi, int lane, int wave) {
   lo = wave_min(lo);
   hi = wave_max(hi);
   __syncthreads();
@@ -90,54 +87,29 @@ __device__ void block_minmax(Smem &sm, uint32_t &lo, uint32_t &hi, int lane, int
   for (int w = 0; w < NWV; ++w) { lo = min(lo, sm.red[1][w]); hi = max(hi, sm.red[2][w]); }
 }
 
-__device__ __forceinline__ uint64_t lanemask_lt(int lane) { return lane ? (~0ull >> (64 - lane)) : 0ull; }
-
-// Exclusive ordered scan of per-element flags.  Element order: running stripe
-// j (slot j*NTH + tid), j < RS, then pass stripe j (column c0 + j*NTH + tid).
-// flag(s) gives this thread's flag for stripe s; emit(s, pos) is called for
-// flagged elements with their rank.  Returns the total count.
-template <class Flag, class Emit>
-__device__ int ordered_scan(Smem &sm, int lane, int wave, Flag flag, Emit emit) {
-  __syncthreads();
-#pragma unroll
-  for (int s = 0; s < RS + VPT; ++s) {
-    const uint64_t b = __ballot(flag(s));
-    if (lane == 0) sm.seg[s * NWV + wave] = __popcll(b);
+// Two simultaneous block-wide exclusive scans in thread order, with their totals.
+__device__ __forceinline__ void block_scan2(Smem &sm, uint32_t a, uint32_t b, uint32_t &ea, uint32_t &eb,
+                                            uint32_t &ta, uint32_t &tb, int lane, int wave) {
+  uint32_t ia = a, ib = b;
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t ya = __shfl_up(ia, o), yb = __shfl_up(ib, o);
+    if (lane >= o) { ia += ya; ib += yb; }
   }
   __syncthreads();
-  if (wave == 0) {
-    constexpr int PER = (NSEG + 63) / 64;
-    int local[PER];
-    int tot = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = lane * PER + i;
-      local[i] = e < NSEG ? sm.seg[e] : 0;
-      tot += local[i];
-    }
-    int incl = tot;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    int run = incl - tot;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = lane * PER + i;
-      if (e < NSEG) sm.seg[e] = run;
-      run += local[i];
-    }
-    if (lane == 63) sm.seg[NSEG] = incl;
-  }
+  if (lane == 63) { sm.wsum[0][wave] = ia; sm.wsum[1][wave] = ib; }
   __syncthreads();
-  const uint64_t lt = lanemask_lt(lane);
+  uint32_t pa = 0, pb = 0;
+  ta = 0;
+  tb = 0;
 #pragma unroll
-  for (int s = 0; s < RS + VPT; ++s) {
-    const bool f = flag(s);
-    const uint64_t b = __ballot(f);
-    if (f) emit(s, sm.seg[s * NWV + wave] + (int)__popcll(b & lt));
+  for (int w = 0; w < NWV; ++w) {
+    const uint32_t sa = sm.wsum[0][w], sb = sm.wsum[1][w];
+    if (w < wave) { pa += sa; pb += sb; }
+    ta += sa;
+    tb += sb;
   }
-  return sm.seg[NSEG];
+  ea = pa + ia - a;
+  eb = pb + ib - b;
 }
 
 __global__ __launch_bounds__(NTH) void topk_kernel(TopkArgs a) {
@@ -180,35 +152,58 @@ __global__ __launch_bounds__(NTH) void topk_kernel(TopkArgs a) {
   const float *vrow = a.vals + (int64_t)r * a.ld;
   const uint8_t *mrow = a.mask ? a.mask + (int64_t)t * a.ld_mask : nullptr;
   const int mshift = (a.mode == TOPK_DENSE || a.mode == TOPK_BLOCK) ? off - ks : 0;  // mask byte = c + mshift
+  // 16-byte loads when every row and every thread's first column are 16-byte aligned
+  const bool vec = ((a.ld & 3) == 0) && (((uintptr_t)a.vals & 15) == 0);
+  const int span = min(a.block, SPAN) & ~3;   // a.block is a multiple of 4 or >= SPAN
+  const int pbase = vec ? (c_lo & ~3) : c_lo;
 
-  for (int c0 = c_lo; c0 < c_hi; c0 += a.block) {
-    const int c1 = min(c0 + a.block, c_hi);
-    uint32_t key[VPT];
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int c = c0 + j * NTH + tid;
-      uint32_t k = 0;
-      if (c < c1) {
-        const int64_t mj = (int64_t)c + mshift;
-        const bool allowed = !mrow || (mj < a.mask_w && mrow[mj]);
-        if (allowed) k = fkey(vrow[c]);
-      }
-      key[j] = k;
-    }
+  for (int P = pbase; P < c_hi; P += span) {
+    const int c0 = max(P, c_lo), c1 = min(P + span, c_hi);  // valid columns of this pass
+    // running slots of this thread: RS consecutive entries
     uint32_t rkey[RS];
-    int rid[RS];
-#pragma unroll
-    for (int j = 0; j < RS; ++j) {
-      const int p = j * NTH + tid;
+    uint32_t rmin = 0xFFFFFFFFu, rmax = 0;
+    static_for<RS>([&](auto j) __attribute__((always_inline)) {
+      const int p = tid * RS + j;
       const bool ok = p < run_n;
       rkey[j] = ok ? fkey(sm.run_val[cur][p]) : 0u;
-      rid[j] = ok ? sm.run_id[cur][p] : -1;
+      if (ok) { rmin = min(rmin, rkey[j]); rmax = max(rmax, rkey[j]); }
+    });
+    // once the list is full, a pass value must beat its smallest entry (which wins ties by id)
+    uint32_t floor_key = 0;
+    if (run_n == K) {
+      block_minmax(sm, rmin, rmax, lane, wave);
+      floor_key = rmin;
     }
-    auto keyof = [&](int s) -> uint32_t { return s < RS ? rkey[s] : key[s - RS]; };
+    // pass columns of this thread: cb .. cb + VPT - 1
+    const int cb = P + tid * VPT;
+    uint32_t key[VPT];
+    if (vec && cb >= c0 && cb + VPT <= c1) {
+      static_for<VPT / 4>([&](auto q) __attribute__((always_inline)) {
+        const float4 v = *(const float4 *)(vrow + cb + 4 * q);
+        key[4 * q + 0] = fkey(v.x);
+        key[4 * q + 1] = fkey(v.y);
+        key[4 * q + 2] = fkey(v.z);
+        key[4 * q + 3] = fkey(v.w);
+      });
+    } else {
+      static_for<VPT>([&](auto j) __attribute__((always_inline)) {
+        const int c = cb + j;
+        key[j] = (c >= c0 && c < c1) ? fkey(vrow[c]) : 0u;
+      });
+    }
+    static_for<VPT>([&](auto j) __attribute__((always_inline)) {
+      uint32_t k = key[j];
+      if (mrow) {
+        const int c = cb + j;
+        const int64_t mj = (int64_t)c + mshift;
+        if (!(c >= c0 && c < c1 && mj < a.mask_w && mrow[mj])) k = 0;
+      }
+      key[j] = k > floor_key ? k : 0u;
+    });
 
     uint32_t nloc = 0;
-#pragma unroll
-    for (int s = 0; s < RS + VPT; ++s) nloc += keyof(s) != 0;
+    static_for<RS>([&](auto j) __attribute__((always_inline)) { nloc += rkey[j] != 0; });
+    static_for<VPT>([&](auto j) __attribute__((always_inline)) { nloc += key[j] != 0; });
     const int total = (int)block_sum(sm, nloc, lane, wave);
 
     uint32_t thk = 0;   // threshold key (0: take every candidate)
@@ -219,11 +214,11 @@ __global__ __launch_bounds__(NTH) void topk_kernel(TopkArgs a) {
       bool done = false;
       for (int level = 0; level < 4 && !done; ++level) {
         uint32_t lo = 0xFFFFFFFFu, hi = 0;
-#pragma unroll
-        for (int s = 0; s < RS + VPT; ++s) {
-          const uint32_t k = keyof(s);
+        auto mm = [&](uint32_t k) __attribute__((always_inline)) {
           if (k >= clo && k <= chi) { lo = min(lo, k); hi = max(hi, k); }
-        }
+        };
+        static_for<RS>([&](auto j) __attribute__((always_inline)) { mm(rkey[j]); });
+        static_for<VPT>([&](auto j) __attribute__((always_inline)) { mm(key[j]); });
         block_minmax(sm, lo, hi, lane, wave);
         if (lo == hi) { thk = lo; done = true; break; }
         if (cnt <= CAP) {
@@ -231,14 +226,14 @@ __global__ __launch_bounds__(NTH) void topk_kernel(TopkArgs a) {
           __syncthreads();
           if (tid == 0) sm.bcast[0] = 0;
           __syncthreads();
-#pragma unroll
-          for (int s = 0; s < RS + VPT; ++s) {
-            const uint32_t k = keyof(s);
+          auto put = [&](uint32_t k) __attribute__((always_inline)) {
             if (k >= lo && k <= hi) {
               const uint32_t slot = atomicAdd(&sm.bcast[0], 1u);
               if (slot < CAP) sm.cand[slot] = k;
             }
-          }
+          };
+          static_for<RS>([&](auto j) __attribute__((always_inline)) { put(rkey[j]); });
+          static_for<VPT>([&](auto j) __attribute__((always_inline)) { put(key[j]); });
           __syncthreads();
           if (tid < cnt) {
             const uint32_t mine = sm.cand[tid];
@@ -260,11 +255,11 @@ __global__ __launch_bounds__(NTH) void topk_kernel(TopkArgs a) {
         __syncthreads();
         for (int i = tid; i < NB; i += NTH) sm.hist[i] = 0;
         __syncthreads();
-#pragma unroll
-        for (int s = 0; s < RS + VPT; ++s) {
-          const uint32_t k = keyof(s);
+        auto bin = [&](uint32_t k) __attribute__((always_inline)) {
           if (k >= lo && k <= hi) atomicAdd(&sm.hist[(k - lo) >> sh], 1u);
-        }
+        };
+        static_for<RS>([&](auto j) __attribute__((always_inline)) { bin(rkey[j]); });
+        static_for<VPT>([&](auto j) __attribute__((always_inline)) { bin(key[j]); });
         __syncthreads();
         // bin b* with (count above b*) < need <= (count at or above b*); thread i owns bins 4i..4i+3
         {
@@ -273,7 +268,6 @@ __global__ __launch_bounds__(NTH) void topk_kernel(TopkArgs a) {
           uint32_t tot = 0;
 #pragma unroll
           for (int i = 0; i < BPT; ++i) { h[i] = sm.hist[tid * BPT + i]; tot += h[i]; }
-          // suffix sum over threads: exclusive sum of totals of higher threads
           uint32_t incl = tot;  // inclusive suffix within the wave (lanes >= this one)
           for (int o = 1; o < 64; o <<= 1) {
             const uint32_t y = __shfl_down(incl, o);
@@ -284,7 +278,6 @@ __global__ __launch_bounds__(NTH) void topk_kernel(TopkArgs a) {
           __syncthreads();
           uint32_t above = incl - tot;
           for (int w = wave + 1; w < NWV; ++w) above += sm.red[0][w];
-          // walk my bins from high to low
 #pragma unroll
           for (int i = BPT - 1; i >= 0; --i) {
             if (above < (uint32_t)need && (uint32_t)need <= above + h[i]) {
@@ -303,47 +296,62 @@ __global__ __launch_bounds__(NTH) void topk_kernel(TopkArgs a) {
         const uint64_t top = (uint64_t)lo + ((uint64_t)(bstar + 1) << sh) - 1;
         chi = (uint32_t)min<uint64_t>(top, (uint64_t)hi);
       }
-      if (!done) {
-        // unreachable: each level narrows the interval by >= 11 bits of 32
-        thk = clo;
-      }
+      if (!done) thk = clo;  // unreachable: each level narrows the interval by >= 11 of 32 bits
       uint32_t gt = 0;
-#pragma unroll
-      for (int s = 0; s < RS + VPT; ++s) gt += keyof(s) > thk;
+      static_for<RS>([&](auto j) __attribute__((always_inline)) { gt += rkey[j] > thk; });
+      static_for<VPT>([&](auto j) __attribute__((always_inline)) { gt += key[j] > thk; });
       need_eq = K - (int)block_sum(sm, gt, lane, wave);
     }
 
-    // ---- selection in id order: keys above thk, then the first need_eq keys equal to it
-    uint64_t eqp = 0;   // pass stripes whose equal-to-threshold key is taken
-    uint32_t eqr = 0;   // running stripes whose equal-to-threshold key is taken
+    // ---- selection in id order: keys above thk, then the first need_eq keys equal to it.
+    // Running slots (ids below every pass id) come first, each group in thread order.
+    uint32_t eq_r = 0, eq_p = 0;
     if (need_eq > 0) {
-      ordered_scan(sm, lane, wave, [&](int s) { return keyof(s) == thk; },
-                   [&](int s, int pos) {
-                     if (pos < need_eq) {
-                       if (s < RS) eqr |= 1u << s;
-                       else eqp |= 1ull << (s - RS);
-                     }
-                   });
+      static_for<RS>([&](auto j) __attribute__((always_inline)) { eq_r += rkey[j] == thk; });
+      static_for<VPT>([&](auto j) __attribute__((always_inline)) { eq_p += key[j] == thk; });
     }
-    auto take = [&](int s) -> bool {
-      const uint32_t k = keyof(s);
+    uint32_t eo_r, eo_p, et_r, et_p;
+    block_scan2(sm, eq_r, eq_p, eo_r, eo_p, et_r, et_p, lane, wave);
+    // equal keys are taken in id order: running ones first (ranks 0 .. et_r - 1), then the pass's
+    const uint32_t eqrank_r = eo_r, eqrank_p = et_r + eo_p;
+    auto taken = [&](uint32_t k, uint32_t &eqrank) __attribute__((always_inline)) -> bool {
       if (k == 0) return false;
       if (k > thk) return true;
-      if (k != thk || need_eq <= 0) return false;
-      return s < RS ? ((eqr >> s) & 1u) : ((eqp >> (s - RS)) & 1ull);
+      if (k == thk && need_eq > 0) return eqrank++ < (uint32_t)need_eq;
+      return false;
     };
+    uint32_t tk_r = 0, tk_p = 0;
+    {
+      uint32_t e1 = eqrank_r, e2 = eqrank_p;
+      static_for<RS>([&](auto j) __attribute__((always_inline)) { tk_r += taken(rkey[j], e1); });
+      static_for<VPT>([&](auto j) __attribute__((always_inline)) { tk_p += taken(key[j], e2); });
+    }
+    uint32_t po_r, po_p, pt_r, pt_p;
+    block_scan2(sm, tk_r, tk_p, po_r, po_p, pt_r, pt_p, lane, wave);
     const int nxt = cur ^ 1;
-    run_n = ordered_scan(sm, lane, wave, take, [&](int s, int pos) {
-      if (pos >= KMAX) return;
-      if (s < RS) {
-        sm.run_id[nxt][pos] = rid[s];
-        sm.run_val[nxt][pos] = kval(rkey[s]);
-      } else {
-        sm.run_id[nxt][pos] = off + c0 + (s - RS) * NTH + tid;
-        sm.run_val[nxt][pos] = kval(key[s - RS]);
-      }
-    });
-    run_n = min(run_n, K);
+    {
+      uint32_t e1 = eqrank_r, e2 = eqrank_p;
+      uint32_t pr = po_r, pp = pt_r + po_p;
+      static_for<RS>([&](auto j) __attribute__((always_inline)) {
+        if (taken(rkey[j], e1)) {
+          if (pr < (uint32_t)KMAX) {
+            sm.run_id[nxt][pr] = sm.run_id[cur][tid * RS + j];
+            sm.run_val[nxt][pr] = kval(rkey[j]);
+          }
+          ++pr;
+        }
+      });
+      static_for<VPT>([&](auto j) __attribute__((always_inline)) {
+        if (taken(key[j], e2)) {
+          if (pp < (uint32_t)KMAX) {
+            sm.run_id[nxt][pp] = off + cb + j;
+            sm.run_val[nxt][pp] = kval(key[j]);
+          }
+          ++pp;
+        }
+      });
+    }
+    run_n = min((int)(pt_r + pt_p), K);
     cur = nxt;
     __syncthreads();
   }

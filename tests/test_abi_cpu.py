@@ -78,6 +78,7 @@ def test_other_entry_validation(lib):
     assert lib.idx_mqa_logits_block(ctypes.byref(p), 0, 5, 0, 256, f, 256, None) == 2   # rows past T
     assert lib.idx_mqa_logits_block(ctypes.byref(p), 0, 4, 100, 256, f, 256, None) == 3  # key0 % 256
     assert lib.idx_topk(f, 1024, 1024, f, f, None, 0, 4, 0, 0, f, None, None, 0, None) == 3      # K = 0
+    assert lib.idx_topk(f, 1024, 1024, f, f, None, 0, 4, 2561, 0, f, None, None, 0, None) == 3   # K > 2560
     assert lib.idx_topk(f, 100, 1024, f, f, None, 0, 4, 8, 0, f, None, None, 0, None) == 2       # ld < W
     assert lib.idx_topk(f, 1024, 1024, f, f, f, 10, 4, 8, 0, f, None, None, 0, None) == 2        # ld_mask < W
     assert lib.idx_topk(None, 1024, 1024, f, f, None, 0, 4, 8, 0, f, None, None, 0, None) == 1
@@ -94,23 +95,40 @@ def test_other_entry_validation(lib):
     assert lib.idx_ragged_windows(f, f, -1, 4, f, f, None) == 2
 
 
+def _r(x):
+    return (x + 255) // 256 * 256
+
+
 def test_workspace_sizes(lib):
+    head = 1280
+    kc = lambda K: min(K + 512, 2560)
     p = _problem(T=2048, L=65536)
     n = ctypes.c_size_t()
     assert lib.idx_workspace_size(2, ctypes.byref(p), 2048, 32768, 0, 0, 0, 0, ctypes.byref(n)) == 0
-    assert n.value == 2048 * 32768 * 4 + 2048 * 2048 * 4
-    # row chunk bounds the workspace; the key count does not enter
+    assert n.value == head + 2 * _r(2048 * kc(2048) * 4) + 2048 * 32768 * 4
+    # the row chunk bounds the workspace; the number of keys does not enter
     p2 = _problem(T=16384, L=487936)
     assert lib.idx_workspace_size(2, ctypes.byref(p2), 512, 32768, 4096, 0, 0, 0, ctypes.byref(n)) == 0
-    assert n.value == 4096 * 32768 * 4 + 4096 * 512 * 4
+    assert n.value == head + 2 * _r(4096 * kc(512) * 4) + 4096 * 32768 * 4
     p3 = _problem(T=16384, L=65536)
     m = ctypes.c_size_t()
     assert lib.idx_workspace_size(2, ctypes.byref(p3), 512, 32768, 4096, 0, 0, 0, ctypes.byref(m)) == 0
     assert m.value == n.value
     assert lib.idx_workspace_size(3, ctypes.byref(p), 0, 32768, 0, 8, 2048, 0, ctypes.byref(n)) == 0
-    assert n.value == 2048 * 4096 * 4 + 2 * 2048 * 2048 * 4
+    assert n.value == head + 2 * _r(2048 * kc(2048) * 4) + 2048 * 4096 * 4 + 2048 * 2048 * 4
     assert lib.idx_workspace_size(4, ctypes.byref(p), 0, 0, 1024, 8, 2048, 65536, ctypes.byref(n)) == 0
-    assert n.value == 1024 * 8192 * 4 + 2 * 1024 * 2048 * 4
+    assert n.value == head + 2 * _r(1024 * kc(2048) * 4) + 1024 * 8192 * 4 + 1024 * 2048 * 4
     assert lib.idx_workspace_size(0, ctypes.byref(p), 0, 0, 0, 0, 0, 0, ctypes.byref(n)) == 0 and n.value == 0
     assert lib.idx_workspace_size(2, ctypes.byref(p), 0, 32768, 0, 0, 0, 0, ctypes.byref(n)) == 3
     assert lib.idx_workspace_size(9, ctypes.byref(p), 1, 256, 0, 0, 0, 0, ctypes.byref(n)) == 3
+
+
+def test_refine_validation(lib):
+    p = _problem()
+    f = 1 << 20
+    assert lib.idx_refine_topk(ctypes.byref(p), None, f, 600, 600, 64, 1, f, None, f, 4096, None) == 1
+    assert lib.idx_refine_topk(ctypes.byref(p), f, f, 600, 600, 700, 1, f, None, f, 4096, None) == 3   # K > Kc
+    assert lib.idx_refine_topk(ctypes.byref(p), f, f, 3000, 3000, 64, 1, f, None, f, 4096, None) == 3  # Kc > 2560
+    assert lib.idx_refine_topk(ctypes.byref(p), f, f, 600, 600, 64, 4, f, None, f, 4096, None) == 6   # pool
+    assert lib.idx_refine_topk(ctypes.byref(p), f, f, 500, 600, 64, 1, f, None, f, 4096, None) == 2   # ld < Kc
+    assert lib.idx_refine_topk(ctypes.byref(p), f, f, 600, 600, 64, 1, f, None, f, 100, None) == 5    # ws

@@ -74,22 +74,42 @@ def test_logits_block_rectangle(case):
         assert np.isnan(g[r, ~inw]).all(), "wrote outside the window"
 
 
+def _oracle_on(g_logits, p):
+    """Oracle windows taken from given (GPU) logits: the selection stage on identical inputs."""
+    return [g_logits[t, :int(p.ke[t]) - int(p.ks[t])].astype(np.float64) for t in range(p.T)]
+
+
 @pytest.mark.parametrize("K,block_k", [(1, 32768), (17, 256), (256, 1024), (700, 32768)])
-def test_topk_dense_vs_oracle(case, K, block_k):
+def test_topk_dense_exact_on_given_logits(case, K, block_k):
     p, d, o = case
     W = max(p.W, 1)
     lg = idx.idx_mqa_logits(d, W)
     gi, gv = idx.idx_topk(lg, d.ks, d.ke, K, block_k=block_k)
-    topk_ok(gi.cpu().numpy(), gv.cpu().numpy(), o, p.ks, K)
+    gi, gv = gi.cpu().numpy(), gv.cpu().numpy()
+    for t, win in enumerate(_oracle_on(lg.cpu().numpy(), p)):
+        oi, ov = oracle.topk_row(win, int(p.ks[t]), K)
+        assert np.array_equal(gi[t], oi), f"row {t}"
+        assert np.array_equal(gv[t], ov), f"row {t}"
+
+
+@pytest.mark.parametrize("K", [1, 64, 700])
+def test_fused_vs_oracle(case, K):
+    p, d, o = case
+    ws = torch.empty(idx.idx_workspace_size(idx.IDX_OP_LOGITS_TOPK_FUSED, d, K=K, block_k=512), dtype=torch.uint8,
+                     device="cuda")
+    fi, fv = idx.idx_logits_topk_fused(d, K, block_k=512, ws=ws)
+    assert idx.overflow_count(ws) == 0
+    topk_ok(fi.cpu().numpy(), fv.cpu().numpy(), o, p.ks, K)
 
 
 @pytest.mark.parametrize("block_k,row_chunk", [(256, 0), (1024, 8), (32768, 16), (512, 1)])
-def test_fused_equals_dense_bitwise(case, block_k, row_chunk):
+def test_fused_equals_dense_refined_bitwise(case, block_k, row_chunk):
     p, d, o = case
     K = 64
     W = max(p.W, 1)
     lg = idx.idx_mqa_logits(d, W)
-    di, dv = idx.idx_topk(lg, d.ks, d.ke, K)
+    ci, cv = idx.idx_topk(lg, d.ks, d.ke, idx.candidate_capacity(K))
+    di, dv = idx.idx_refine_topk(d, ci, cv, K)
     fi, fv = idx.idx_logits_topk_fused(d, K, block_k=block_k, row_chunk=row_chunk)
     assert torch.equal(di, fi)
     assert torch.equal(dv.view(torch.int32), fv.view(torch.int32))
@@ -102,12 +122,14 @@ def test_fused_masked_consumer(case):
     W = max(p.W, 1)
     rng = np.random.default_rng(5)
     mask = (rng.random((p.T, W)) < 0.3).astype(np.uint8)
-    fi, fv = idx.idx_logits_topk_fused(d, K, block_k=512, mask=torch.from_numpy(mask).cuda())
+    mt = torch.from_numpy(mask).cuda()
+    fi, fv = idx.idx_logits_topk_fused(d, K, block_k=512, mask=mt)
     allowed = [mask[t, :len(o[t])].astype(bool) for t in range(p.T)]
     topk_ok(fi.cpu().numpy(), fv.cpu().numpy(), o, p.ks, K, allowed=allowed)
-    # dense path with the same mask agrees bitwise
+    # dense path with the same mask, refined, agrees bitwise
     lg = idx.idx_mqa_logits(d, W)
-    di, dv = idx.idx_topk(lg, d.ks, d.ke, K, mask=torch.from_numpy(mask).cuda())
+    ci, cv = idx.idx_topk(lg, d.ks, d.ke, idx.candidate_capacity(K), mask=mt)
+    di, dv = idx.idx_refine_topk(d, ci, cv, K)
     assert torch.equal(di, fi)
 
 
@@ -131,14 +153,23 @@ def test_candidates_dense_and_fused(case, n_blocks):
     p, d, o = case
     W = max(p.W, 1)
     lg = idx.idx_mqa_logits(d, W)
+    # dense: exact selection on the given logits
     blocks_d = torch.empty((p.T, n_blocks), dtype=torch.int32, device="cuda")
     mask_d, _ = idx.idx_block_candidates(d, W, n_blocks=n_blocks, logits=lg, row_chunk=7, out_blocks=blocks_d)
-    _check_candidates(p, o, mask_d.cpu().numpy(), blocks_d.cpu().numpy(), n_blocks)
+    g_on = _oracle_on(lg.cpu().numpy(), p)
+    md, bd = mask_d.cpu().numpy(), blocks_d.cpu().numpy()
+    for t, win in enumerate(g_on):
+        om, ob = oracle.block_candidates_row(win, 8, n_blocks, W)
+        assert np.array_equal(md[t], om), f"dense mask row {t}"
+        assert bd[t][bd[t] >= 0].tolist() == ob.tolist(), f"dense blocks row {t}"
     if (p.ks % 8).any():
         return  # the fused pooling path requires windows that start on a multiple of 8
+    # fused: scored from q/k with an exact boundary, against the fp64 oracle
     blocks_f = torch.empty((p.T, n_blocks), dtype=torch.int32, device="cuda")
     mask_f, _ = idx.idx_block_candidates(d, W, n_blocks=n_blocks, block_k=512, row_chunk=16, out_blocks=blocks_f)
-    assert torch.equal(mask_d, mask_f) and torch.equal(blocks_d, blocks_f)
+    _check_candidates(p, o, mask_f.cpu().numpy(), blocks_f.cpu().numpy(), n_blocks)
+    mask_f2, _ = idx.idx_block_candidates(d, W, n_blocks=n_blocks, block_k=1024, row_chunk=0)
+    assert torch.equal(mask_f, mask_f2)
 
 
 def test_deterministic(case):
