@@ -5,8 +5,8 @@
 //
 // One workgroup (512 threads) owns one row.  The running top-K (ids ascending,
 // fp32 values) lives in LDS while the row's columns are consumed in passes of
-// up to 32768 values held in registers.  Thread `tid` owns the contiguous
-// columns P + 64 tid .. P + 64 tid + 63 of a pass starting at column P and the
+// up to 8192 values held in registers.  Thread `tid` owns the contiguous
+// columns P + 16 tid .. P + 16 tid + 15 of a pass starting at column P and the
 // contiguous running slots 5 tid .. 5 tid + 4, so id order is thread-major and
 // every ordered compaction is one per-thread count plus one block-wide
 // exclusive scan (all register indices are compile-time constants).  A pass:
@@ -34,7 +34,7 @@ namespace {
 
 constexpr int NTH = 512;
 constexpr int NWV = NTH / 64;
-constexpr int VPT = 64;           // pass values per thread (contiguous columns)
+constexpr int VPT = 16;           // pass values per thread (contiguous columns); small code, fits the I-cache
 constexpr int SPAN = NTH * VPT;   // columns one pass can hold
 constexpr int RS = 5;             // running slots per thread (K <= 2560)
 constexpr int KMAX = RS * NTH;
