@@ -81,19 +81,21 @@ def time_events(fn, n, stream):
 
 
 def scoring_launch_ms(p, d, block_k, reps, stream):
-    """Average duration of the scoring kernel as the fused path launches it (key-block layout)."""
+    """Average duration of the scoring kernel as the fused path launches it (key-block layout):
+    reps x (one launch per key block), back to back on `stream` between one pair of events."""
     scratch = torch.empty((p.T, block_k), dtype=torch.float32, device="cuda")
     blocks = [(kb, min(block_k, p.L - kb)) for kb in range(0, p.L, block_k)]
-    times, flops = [], 0
-    for _ in range(reps):
-        for kb, nk in blocks:
-            t = time_events(lambda: idx.idx_mqa_logits_block(d, 0, p.T, kb, nk, out=scratch, stream=stream), 1,
-                            stream)
-            times.append(t[0])
-    for kb, nk in blocks:
-        flops += 2 * p.H * p.D * block_pairs(p, kb, nk)
+
+    def run():
+        for _ in range(reps):
+            for kb, nk in blocks:
+                idx.idx_mqa_logits_block(d, 0, p.T, kb, nk, out=scratch, stream=stream)
+
+    run()  # warm
+    t = time_events(run, 3, stream)
+    flops = sum(2 * p.H * p.D * block_pairs(p, kb, nk) for kb, nk in blocks)
     del scratch
-    avg_ms = float(np.mean(times))
+    avg_ms = float(np.median(t)) / (reps * len(blocks))
     return avg_ms, flops / len(blocks), len(blocks)
 
 

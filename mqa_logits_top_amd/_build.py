@@ -12,6 +12,9 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
     # packed fp32 VALU ops are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results go straight to VGPRs: the scoring epilogue reads every
+    # accumulator once, so AGPR destinations would cost one v_accvgpr_read each
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 

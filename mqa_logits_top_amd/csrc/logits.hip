@@ -47,6 +47,11 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
+// ReLU as one integer max: a float with the sign bit set is a negative int32
+// and becomes +0, a non-negative float keeps its bits (fmaxf would add a NaN
+// canonicalisation, a second VALU op per value).
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 constexpr int OOB = (int)0x80000000;  // buffer offset past any num_records: the store is dropped
 constexpr int RSRC3 = 0x00020000;     // raw buffer, 32-bit elements
 
@@ -203,7 +208,7 @@ __global__ __launch_bounds__(NW * 64) void logits_kernel(LogitsArgs a) {
 #pragma unroll
       for (int i = 0; i < NT; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc = __builtin_fmaf(__builtin_fmaxf(c[i][j], 0.f), wv[i][j], acc);
+        for (int j = 0; j < 4; ++j) acc = __builtin_fmaf(relu(c[i][j]), wv[i][j], acc);
       if (QR == 2) {
         const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc), __float_as_uint(acc), false, false);
         acc = __uint_as_float(r[0]) + __uint_as_float(r[1]);
