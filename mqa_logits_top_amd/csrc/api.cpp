@@ -58,12 +58,13 @@ idx_status check_block(int32_t block_k) {
 }
 
 // Workgroup key splits for one scoring launch over n keys: a multiple of 8 splits
-// when possible (one XCD per split residue), each a multiple of 128 keys.
+// when possible (one XCD per split residue), each a multiple of 256 keys (whole
+// scoring stages).
 void plan_splits(int32_t n, int32_t &split, int32_t &nsplit) {
   if (n <= 0) { split = 128; nsplit = 0; return; }
   const int32_t target = 4096;
   int32_t ns = 8 * ((n + 8 * target - 1) / (8 * target));
-  split = round_up((n + ns - 1) / ns, 128);
+  split = round_up((n + ns - 1) / ns, 256);
   if (split < 512) split = 512;
   nsplit = (n + split - 1) / split;
 }
@@ -110,14 +111,18 @@ int32_t cand_cap(int32_t K) { return K + RESERVE < MAX_KC ? K + RESERVE : MAX_KC
 //   [0, 256)            uint32 overflow counter of the last call, then free
 //   key-bound partials  256 floats
 //   candidate ids/vals  [Tc, Kc] each
-//   scratch             [Tc, Bk] fp32 scores (or [Tc, Bk / pool] pooled maxima)
+//   scratch             [Tc, pitch(Bk)] fp32 scores (or [Tc, pitch(Bk / pool)] pooled maxima)
 constexpr size_t HEAD = 256 + 1024;
+// Row pitch of scratch rows: 256 bytes beyond the row, so that the rows that
+// the selection kernel streams at the same time start on different HBM channels
+// instead of all sitting a power of two apart.
+int32_t pitch(int32_t cols) { return cols + 64; }
 size_t refine_ws(int32_t Tc, int32_t Kc) { return HEAD + 2 * round_up_sz((size_t)Tc * Kc * 4, 256); }
 size_t fused_ws(int32_t Tc, int32_t Bk, int32_t K) {
-  return refine_ws(Tc, cand_cap(K)) + round_up_sz((size_t)Tc * Bk * 4, 256);
+  return refine_ws(Tc, cand_cap(K)) + round_up_sz((size_t)Tc * pitch(Bk) * 4, 256);
 }
 size_t cand_ws(int32_t Tc, int32_t pooled_cols, int32_t n_blocks) {
-  return refine_ws(Tc, cand_cap(n_blocks)) + round_up_sz((size_t)Tc * pooled_cols * 4, 256) +
+  return refine_ws(Tc, cand_cap(n_blocks)) + round_up_sz((size_t)Tc * pitch(pooled_cols) * 4, 256) +
          round_up_sz((size_t)Tc * n_blocks * 4, 256);
 }
 
@@ -308,7 +313,8 @@ idx_status idx_logits_topk_fused(const idx_problem *p, int32_t K, int32_t block_
   const int32_t Kc = cand_cap(K);
   Carve cv{(uint8_t *)ws};
   RefineWs rw = carve_refine(cv, Tc, Kc);
-  float *scratch = cv.take<float>((size_t)Tc * Bk);
+  const int32_t sld = pitch(Bk);
+  float *scratch = cv.take<float>((size_t)Tc * sld);
   if ((st = launched(idx::launch_key_bound((const uint8_t *)p->k, (const uint8_t *)p->k_scale, p->k_fmt, p->L,
                                            rw.kpart, rw.overflow, s))))
     return st;
@@ -318,12 +324,12 @@ idx_status idx_logits_topk_fused(const idx_problem *p, int32_t K, int32_t block_
     do {
       const int32_t nk = std::min(Bk, p->L - kb);
       if (nk > 0) {
-        idx::LogitsArgs a = logits_args(p, r0, nr, kb, kb + nk, scratch, Bk, nk);
+        idx::LogitsArgs a = logits_args(p, r0, nr, kb, kb + nk, scratch, sld, nk);
         if ((st = launched(idx::launch_logits(a, p->k_fmt, p->H, idx::STORE_BLOCK, s)))) return st;
       }
       idx::TopkArgs b{};
       b.vals = scratch;
-      b.ld = Bk;
+      b.ld = sld;
       b.ncols = nk > 0 ? nk : 0;
       b.block = Bk;
       b.ks = p->ks;
@@ -406,7 +412,8 @@ idx_status idx_block_candidates(const idx_problem *p, const float *logits, int64
   Carve cv{(uint8_t *)ws};
   const int32_t Kc = logits ? n_blocks : cand_cap(n_blocks);
   RefineWs rw = carve_refine(cv, Tc, cand_cap(n_blocks));
-  float *pooled = cv.take<float>((size_t)Tc * pooled_cols);
+  const int32_t pld = pitch(pooled_cols);
+  float *pooled = cv.take<float>((size_t)Tc * pld);
   int32_t *kept = cv.take<int32_t>((size_t)Tc * n_blocks);
   if (!logits) {
     if ((st = launched(idx::launch_key_bound((const uint8_t *)p->k, (const uint8_t *)p->k_scale, p->k_fmt, p->L,
@@ -429,10 +436,10 @@ idx_status idx_block_candidates(const idx_problem *p, const float *logits, int64
       b.out_idx = blocks;
       b.out_val = rw.cval;
       if ((st = launched(idx::launch_pool_dense(logits + (int64_t)r0 * ld, ld, W, p->ks, p->ke, r0, nr, pool, pooled,
-                                                pooled_cols, pooled_cols, s))))
+                                                pld, pooled_cols, s))))
         return st;
       b.vals = pooled;
-      b.ld = pooled_cols;
+      b.ld = pld;
       b.ncols = pooled_cols;
       b.block = MAX_BLOCK;
       b.mode = idx::TOPK_POOL_DENSE;
@@ -446,11 +453,11 @@ idx_status idx_block_candidates(const idx_problem *p, const float *logits, int64
       do {
         const int32_t nk = std::min(Bk, p->L - kb);
         if (nk > 0) {
-          idx::LogitsArgs a = logits_args(p, r0, nr, kb, kb + nk, pooled, pooled_cols, (nk + pool - 1) / pool);
+          idx::LogitsArgs a = logits_args(p, r0, nr, kb, kb + nk, pooled, pld, (nk + pool - 1) / pool);
           if ((st = launched(idx::launch_logits(a, p->k_fmt, p->H, idx::STORE_POOL8, s)))) return st;
         }
         b.vals = pooled;
-        b.ld = pooled_cols;
+        b.ld = pld;
         b.ncols = nk > 0 ? (nk + pool - 1) / pool : 0;
         b.block = MAX_BLOCK;
         b.mode = idx::TOPK_POOL_BLOCK;

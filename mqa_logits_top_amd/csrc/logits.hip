@@ -45,6 +45,7 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 // ReLU as one integer max: a float with the sign bit set is a negative int32
@@ -66,11 +67,11 @@ __global__ __launch_bounds__(NW * 64) void logits_kernel(LogitsArgs a) {
   constexpr int NT = H / HPT;            // A tiles per wave (8)
   constexpr int RPW = NW * QR;           // rows per workgroup
   constexpr int KB = KF == 0 ? 128 : 64; // key bytes
-  constexpr int TK = KF == 0 ? 64 : 128; // keys per LDS stage (8 KiB either way)
+  constexpr int TK = KF == 0 ? 128 : 256; // keys per LDS stage (16 KiB either way)
   constexpr int STAGE = TK * KB;
   constexpr int LPT = STAGE / 16 / (NW * 64);  // 16-byte chunks per thread per stage
   static_assert(LPT * NW * 64 * 16 == STAGE, "stage must split evenly over the workgroup");
-  static_assert(RPW <= 64 && TK <= NW * 64, "layout limits");
+  static_assert(RPW <= 64 && TK <= NW * 64 && TK % 64 == 0, "layout limits");
 
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][STAGE];
   __shared__ __attribute__((aligned(256))) uint32_t sbuf[2][TK];
@@ -151,6 +152,9 @@ __global__ __launch_bounds__(NW * 64) void logits_kernel(LogitsArgs a) {
   const int obase = (t_out - a.row0 - wrow) * (int)ld;   // element offset of this lane's row
 
   // ---- key stages: thread `tid` owns 16-byte LDS slots tid, tid + NW*64, ...
+  // LDS row p of a stage holds tile key 64 (p / 64) + 4 (p % 16) + (p / 16) % 4, so
+  // group j of batch b (rows 16 (4 b + j) .. + 15) hands lane n16 the key
+  // 64 b + 4 n16 + j: after a batch's four groups each lane holds 4 consecutive keys.
   v4i kreg[LPT];
   uint32_t sreg = 0;
   auto fetch = [&](int tile) {
@@ -158,9 +162,9 @@ __global__ __launch_bounds__(NW * 64) void logits_kernel(LogitsArgs a) {
 #pragma unroll
     for (int it = 0; it < LPT; ++it) {
       const int slot = it * NW * 64 + tid;
-      int key, chunk;
-      if (KF == 0) { key = slot >> 3; chunk = (slot & 7) ^ swz8(key); }
-      else { key = slot >> 2; chunk = (slot & 3) ^ swz4(key); }
+      const int p = KF == 0 ? slot >> 3 : slot >> 2;
+      const int chunk = KF == 0 ? (slot & 7) ^ swz8(p) : (slot & 3) ^ swz4(p);
+      const int key = (p & ~63) | ((p & 15) << 2) | ((p >> 4) & 3);
       const int gk = min(ts + key, a.L - 1);
       kreg[it] = *(const v4i *)(a.k + (int64_t)gk * KB + chunk * 16);
     }
@@ -177,61 +181,82 @@ __global__ __launch_bounds__(NW * 64) void logits_kernel(LogitsArgs a) {
   if (ntiles > 1) fetch(1);
   __syncthreads();
 
+  // 16-byte stores need a 16-byte aligned element offset
+  const bool row_al = (((uintptr_t)a.out & 15) == 0) && ((ld & 3) == 0) &&
+                      ((MODE == STORE_DENSE ? kst : a.key_lo) & 3) == 0;
+  // exclusive key limit of this lane's stores
+  const int lim = MODE == STORE_DENSE ? min(v_hi, kst + a.wcols) : v_hi;
+
   for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1;
     const int ts = tile0 + it * TK;
 #pragma unroll
-    for (int grp = 0; grp < TK / 16; ++grp) {
-      const int n = grp * 16 + n16;     // key within the tile
-      v8i bk;
-      int bscale = 0;
+    for (int b = 0; b < TK / 64; ++b) {
+      const int s0 = ts + 64 * b + 4 * n16;                       // this lane's first key
+      const v4i sc = *(const v4i *)&sbuf[buf][64 * b + 4 * n16];  // its 4 keys' scale words
+      float val[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int p = (4 * b + j) * 16 + n16;   // LDS row of key s0 + j
+        v8i bk;
+        int bscale = 0;
+        if (KF == 0) {
+          const int sw = swz8(p);
+          const v4i lo = *(const v4i *)&kbuf[buf][p * 128 + ((g ^ sw) << 4)];
+          const v4i hi = *(const v4i *)&kbuf[buf][p * 128 + (((4 + g) ^ sw) << 4)];
+          bk = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        } else {
+          const v4i v = *(const v4i *)&kbuf[buf][p * 64 + ((g ^ swz4(p)) << 4)];
+          bk = (v8i){v.x, v.y, v.z, v.w, 0, 0, 0, 0};
+          bscale = (sc[j] >> (8 * g)) & 0xFF;
+        }
+        v4f c[NT];
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+          if (KF == 0)
+            c[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[i], bk, (v4f){0, 0, 0, 0}, 0, 0, 0, 0, 0, 0);
+          else
+            c[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[i], bk, (v4f){0, 0, 0, 0}, 0, 4, 0, 127, 0,
+                                                                    bscale);
+        }
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) acc = __builtin_fmaf(relu(c[i][jj]), wv[i][jj], acc);
+        if (QR == 2) {
+          const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc), __float_as_uint(acc), false, false);
+          acc = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+        val[j] = acc;
+      }
       if (KF == 0) {
-        const int sw = swz8(n);
-        const v4i lo = *(const v4i *)&kbuf[buf][n * 128 + ((g ^ sw) << 4)];
-        const v4i hi = *(const v4i *)&kbuf[buf][n * 128 + (((4 + g) ^ sw) << 4)];
-        bk = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) val[j] *= __int_as_float(sc[j]);
+      }
+      if (MODE == STORE_DENSE || MODE == STORE_BLOCK) {
+        const int col = MODE == STORE_DENSE ? s0 - kst : s0 - a.key_lo;   // column of key s0
+        if (writer && row_al && s0 >= v_lo && s0 + 4 <= lim) {
+          const v4u d = {__float_as_uint(val[0]), __float_as_uint(val[1]), __float_as_uint(val[2]),
+                         __float_as_uint(val[3])};
+          __builtin_amdgcn_raw_buffer_store_b128(d, orsrc, (obase + col) * 4, 0, 0);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool ok = writer && s0 + j >= v_lo && s0 + j < lim;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val[j]), orsrc, ok ? (obase + col + j) * 4 : OOB,
+                                                  0, 0);
+          }
+        }
       } else {
-        const v4i v = *(const v4i *)&kbuf[buf][n * 64 + ((g ^ swz4(n)) << 4)];
-        bk = (v8i){v.x, v.y, v.z, v.w, 0, 0, 0, 0};
-        bscale = (sbuf[buf][n] >> (8 * g)) & 0xFF;
-      }
-      v4f c[NT];
+        // max over the 8 aligned keys s0 & ~7 .. + 7: this lane's 4, then its neighbour's
+        float m = -__builtin_inff();
 #pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        if (KF == 0)
-          c[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[i], bk, (v4f){0, 0, 0, 0}, 0, 0, 0, 0, 0, 0);
-        else
-          c[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[i], bk, (v4f){0, 0, 0, 0}, 0, 4, 0, 127, 0,
-                                                                  bscale);
-      }
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < NT; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc = __builtin_fmaf(relu(c[i][j]), wv[i][j], acc);
-      if (QR == 2) {
-        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc), __float_as_uint(acc), false, false);
-        acc = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-      }
-      const int s = ts + n;
-      float val = acc;
-      if (KF == 0) val *= __uint_as_float(sbuf[buf][n]);
-      const bool ok = writer && s >= v_lo && s < v_hi;
-      if (MODE == STORE_DENSE) {
-        const int col = s - kst;
-        const int off = (ok && col < a.wcols) ? (obase + col) * 4 : OOB;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), orsrc, off, 0, 0);
-      } else if (MODE == STORE_BLOCK) {
-        const int off = ok ? (obase + s - a.key_lo) * 4 : OOB;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), orsrc, off, 0, 0);
-      } else {
-        // max over the 8 aligned keys of this lane's half-row (quad swaps, then half-row mirror)
-        float m = ok ? val : -__builtin_inff();
+        for (int j = 0; j < 4; ++j)
+          if (s0 + j >= v_lo && s0 + j < v_hi) m = __builtin_fmaxf(m, val[j]);
         m = __builtin_fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, false)));
-        m = __builtin_fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, false)));
-        m = __builtin_fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x141, 0xF, 0xF, false)));
-        const int col = (s - a.key_lo) >> 3;
-        const bool st = writer && (n16 & 7) == 0 && m != -__builtin_inff() && col < a.wcols;
+        const int col = (s0 - a.key_lo) >> 3;
+        const bool st = writer && (n16 & 1) == 0 && m != -__builtin_inff() && col < a.wcols;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), orsrc, st ? (obase + col) * 4 : OOB, 0, 0);
       }
     }

@@ -4,28 +4,25 @@
 // selected buffer).
 //
 // One workgroup (512 threads) owns one row.  The running top-K (ids ascending,
-// fp32 values) lives in LDS while the row's columns are consumed in passes of
-// up to 8192 values held in registers.  Thread `tid` owns the contiguous
-// columns P + 16 tid .. P + 16 tid + 15 of a pass starting at column P and the
-// contiguous running slots 5 tid .. 5 tid + 4, so id order is thread-major and
-// every ordered compaction is one per-thread count plus one block-wide
-// exclusive scan (all register indices are compile-time constants).  A pass:
-//   1. map fp32 values to order-preserving uint32 keys (0 is reserved for
-//      "not a candidate": excluded by window, mask, padding, or -- once the
-//      running list is full -- by not beating its smallest entry, which wins
-//      every tie because running ids precede the pass's ids);
-//   2. find the key of the K-th largest candidate (running + pass), counting
-//      multiplicity.  The candidate key interval [lo, hi] is narrowed by
-//      histogram levels: bins are (key - lo) >> s with the smallest s that
-//      gives < 2048 bins, so each level consumes >= 11 bits of the interval and
-//      at most three levels are needed; once <= 512 candidates remain they are
-//      ranked directly in LDS;
-//   3. keep keys above the threshold and, among keys equal to it, the ones
-//      with the lowest ids (total order: value desc, id asc), written in id
-//      order.  Running ids precede the pass's ids, so the list stays ascending.
-// All steps are integer/comparison work on exact keys, so the result is the
-// unique top-K under the total order, independent of how rows or columns are
-// split into launches and passes.
+// fp32 values) lives in LDS; the row's columns are consumed in segments of up to
+// 32768 columns, each merged into the running list.  A segment is read from
+// memory once, into registers: thread `tid` holds columns 8192 c + 16 tid + j
+// (c < 4, j < 16) as order-preserving uint32 keys (0 is reserved for "not a
+// candidate": excluded by window, mask or -- once the running list is full -- by
+// not beating its smallest entry, which wins every tie because running ids
+// precede the segment's ids).  Register sweeps then
+//   1. count the union of running and segment candidates and find its key range;
+//   2. histogram the union into 2048 bins anchored at the largest key (the first
+//      level covers 2^26 keys -- eight binades -- below it in bins of 2^15 keys,
+//      plus a catch-all bin under them), find the bin b* holding the K-th
+//      largest key, and narrow to that bin while the segment's candidates at or
+//      above it would not fit the LDS list;
+//   3. collect the segment's keys at or above the bin, in column order, into LDS.
+// The exact K-th key and the number of keys equal to it that are taken (lowest
+// ids first) are then found among the LDS-resident candidates of bin b*, and the
+// taken running and segment entries are written, in id order, as the new list.
+// All decisions are integer comparisons of exact keys, so the result is the
+// unique top-K under (value desc, id asc), whatever the segment boundaries.
 #include "common.h"
 #include "kernels.h"
 
@@ -34,67 +31,89 @@ namespace {
 
 constexpr int NTH = 512;
 constexpr int NWV = NTH / 64;
-constexpr int VPT = 16;           // pass values per thread (contiguous columns); small code, fits the I-cache
-constexpr int SPAN = NTH * VPT;   // columns one pass can hold
-constexpr int RS = 5;             // running slots per thread (K <= 2560)
-constexpr int KMAX = RS * NTH;
-constexpr int NB = 2048;          // histogram bins
-constexpr int CAP = 512;          // direct ranking threshold
+constexpr int VPT = 16;             // columns per thread per chunk (contiguous)
+constexpr int SPAN = NTH * VPT;     // columns per chunk
+constexpr int NCH = 4;              // chunks per segment
+constexpr int SEG = NCH * SPAN;     // columns per segment (segment offsets fit 16 bits)
+constexpr int KMAX = 2560;          // longest running list
+constexpr int NB = 2048;            // histogram bins
+constexpr int CAPK = 4608;          // segment candidates held in LDS
+constexpr int CAP = 512;            // direct ranking threshold
+constexpr int TOP_LOG2 = 26;        // level 0 resolves the 2^26 keys below the largest
+constexpr int TOP_SH = TOP_LOG2 - 11;
 
 struct Smem {
   int run_id[2][KMAX];
   float run_val[2][KMAX];
-  uint32_t hist[NB];
-  uint32_t cand[CAP];
+  uint32_t kkey[CAPK + 64];  // collected segment keys, column order (+ one spare slot per lane)
+  uint16_t kcol[CAPK + 64];  // their columns relative to the segment start
+  uint32_t hist[NB + 64]; // histogram bins (+ one spare slot per lane); the first CAP words
+                          // double as the ranking list
   uint32_t red[3][NWV];
   uint32_t wsum[2][NWV];
   uint32_t bcast[4];
 };
 
+// Wave-wide reductions and scans on DPP / permlane moves (no LDS traffic, no
+// lane-address registers): quad swaps, half-row and row mirrors pair the lanes
+// of a 16-lane row, then permlane16/32 swaps pair rows.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t x, Op op) {
+  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false));  // row half mirror
+  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, false));  // row mirror
+  const auto r16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = op(r16[0], r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return op(r32[0], r32[1]);
+}
 __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  return wave_reduce(x, [](uint32_t a, uint32_t b) { return a + b; });
 }
 __device__ __forceinline__ uint32_t wave_min(uint32_t x) {
-  for (int o = 32; o > 0; o >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, o));
-  return x;
+  return wave_reduce(x, [](uint32_t a, uint32_t b) { return min(a, b); });
 }
 __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
-  for (int o = 32; o > 0; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o));
+  return wave_reduce(x, [](uint32_t a, uint32_t b) { return max(a, b); });
+}
+// Inclusive prefix sum over the wave's lanes: shifts by 1, 2, 4, 8 inside each
+// 16-lane row, then the last lane of row 0 / 2 into rows 1 / 3 and of row 1 into
+// rows 2 and 3 (lanes without a source add 0).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return x;
 }
 
-// Block-wide sum / min / max of one value per thread (all threads must call).
-__device__ __forceinline__ uint32_t block_sum(Smem &sm, uint32_t x, int lane, int wave) {
-  x = wave_sum(x);
-  __syncthreads();
-  if (lane == 0) sm.red[0][wave] = x;
-  __syncthreads();
-  uint32_t s = 0;
-#pragma unroll
-  for (int w = 0; w < NWV; ++w) s += sm.red[0][w];
-  return s;
-}
-__device__ __forceinline__ void block_minmax(Smem &sm, uint32_t &lo, uint32_t &hi, int lane, int wave) {
+// Block-wide sum, min and max of one value per thread (all threads must call).
+__device__ __forceinline__ void block_sum_minmax(Smem &sm, uint32_t &s, uint32_t &lo, uint32_t &hi, int lane,
+                                                 int wave) {
+  s = wave_sum(s);
   lo = wave_min(lo);
   hi = wave_max(hi);
   __syncthreads();
-  if (lane == 0) { sm.red[1][wave] = lo; sm.red[2][wave] = hi; }
+  if (lane == 0) { sm.red[0][wave] = s; sm.red[1][wave] = lo; sm.red[2][wave] = hi; }
   __syncthreads();
+  s = 0;
   lo = 0xFFFFFFFFu;
   hi = 0;
 #pragma unroll
-  for (int w = 0; w < NWV; ++w) { lo = min(lo, sm.red[1][w]); hi = max(hi, sm.red[2][w]); }
+  for (int w = 0; w < NWV; ++w) {
+    s += sm.red[0][w];
+    lo = min(lo, sm.red[1][w]);
+    hi = max(hi, sm.red[2][w]);
+  }
 }
 
 // Two simultaneous block-wide exclusive scans in thread order, with their totals.
 __device__ __forceinline__ void block_scan2(Smem &sm, uint32_t a, uint32_t b, uint32_t &ea, uint32_t &eb,
                                             uint32_t &ta, uint32_t &tb, int lane, int wave) {
-  uint32_t ia = a, ib = b;
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t ya = __shfl_up(ia, o), yb = __shfl_up(ib, o);
-    if (lane >= o) { ia += ya; ib += yb; }
-  }
+  const uint32_t ia = wave_incl_scan(a), ib = wave_incl_scan(b);
   __syncthreads();
   if (lane == 63) { sm.wsum[0][wave] = ia; sm.wsum[1][wave] = ib; }
   __syncthreads();
@@ -112,7 +131,13 @@ __device__ __forceinline__ void block_scan2(Smem &sm, uint32_t a, uint32_t b, ui
   eb = pb + ib - b;
 }
 
-__global__ __launch_bounds__(NTH) void topk_kernel(TopkArgs a) {
+// Bin of key k in a histogram anchored at chi: (chi - k) >> sh, the last bin
+// catching everything further down.
+__device__ __forceinline__ uint32_t bin_of(uint32_t k, uint32_t chi, int sh) {
+  return min((chi - k) >> sh, (uint32_t)(NB - 1));
+}
+
+__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) void topk_kernel(TopkArgs a) {
   __shared__ Smem sm;
   const int r = blockIdx.x;
   const int t = a.row0 + r;
@@ -139,14 +164,15 @@ __global__ __launch_bounds__(NTH) void topk_kernel(TopkArgs a) {
   int cur = 0;
   int run_n = 0;
   if (!a.first) {
-    uint32_t cnt = 0;
+    uint32_t cnt = 0, d0 = 0, d1 = 0;
     for (int p = tid; p < K; p += NTH) {
       const int id = oidx[p];
       sm.run_id[0][p] = id;
       sm.run_val[0][p] = oval[p];
       cnt += id >= 0;
     }
-    run_n = (int)block_sum(sm, cnt, lane, wave);
+    block_sum_minmax(sm, cnt, d0, d1, lane, wave);
+    run_n = (int)cnt;
   }
 
   const float *vrow = a.vals + (int64_t)r * a.ld;
@@ -154,206 +180,365 @@ __global__ __launch_bounds__(NTH) void topk_kernel(TopkArgs a) {
   const int mshift = (a.mode == TOPK_DENSE || a.mode == TOPK_BLOCK) ? off - ks : 0;  // mask byte = c + mshift
   // 16-byte loads when every row and every thread's first column are 16-byte aligned
   const bool vec = ((a.ld & 3) == 0) && (((uintptr_t)a.vals & 15) == 0);
-  const int span = min(a.block, SPAN) & ~3;   // a.block is a multiple of 4 or >= SPAN
-  const int pbase = vec ? (c_lo & ~3) : c_lo;
+  const int seg = max(min(a.block, SEG) & ~3, 4);
+  const int sbase = vec ? (c_lo & ~3) : c_lo;
 
-  for (int P = pbase; P < c_hi; P += span) {
-    const int c0 = max(P, c_lo), c1 = min(P + span, c_hi);  // valid columns of this pass
-    // running slots of this thread: RS consecutive entries
-    uint32_t rkey[RS];
-    uint32_t rmin = 0xFFFFFFFFu, rmax = 0;
-    static_for<RS>([&](auto j) __attribute__((always_inline)) {
-      const int p = tid * RS + j;
-      const bool ok = p < run_n;
-      rkey[j] = ok ? fkey(sm.run_val[cur][p]) : 0u;
-      if (ok) { rmin = min(rmin, rkey[j]); rmax = max(rmax, rkey[j]); }
-    });
-    // once the list is full, a pass value must beat its smallest entry (which wins ties by id)
+  for (int S = sbase; S < c_hi; S += seg) {
+    const int s0 = max(S, c_lo), s1 = min(S + seg, c_hi);  // valid columns of this segment
+
+    auto run_key = [&](int p) __attribute__((always_inline)) -> uint32_t { return fkey(sm.run_val[cur][p]); };
     uint32_t floor_key = 0;
-    if (run_n == K) {
-      block_minmax(sm, rmin, rmax, lane, wave);
-      floor_key = rmin;
+    if (run_n == K) {  // a full list: segment keys must beat its smallest entry
+      uint32_t rlo = 0xFFFFFFFFu, rhi = 0, rn = 0;
+      for (int p = tid; p < run_n; p += NTH) rlo = min(rlo, run_key(p));
+      block_sum_minmax(sm, rn, rlo, rhi, lane, wave);
+      floor_key = rlo;
     }
-    // pass columns of this thread: cb .. cb + VPT - 1
-    const int cb = P + tid * VPT;
-    uint32_t key[VPT];
-    if (vec && cb >= c0 && cb + VPT <= c1) {
-      static_for<VPT / 4>([&](auto q) __attribute__((always_inline)) {
-        const float4 v = *(const float4 *)(vrow + cb + 4 * q);
-        key[4 * q + 0] = fkey(v.x);
-        key[4 * q + 1] = fkey(v.y);
-        key[4 * q + 2] = fkey(v.z);
-        key[4 * q + 3] = fkey(v.w);
-      });
-    } else {
-      static_for<VPT>([&](auto j) __attribute__((always_inline)) {
-        const int c = cb + j;
-        key[j] = (c >= c0 && c < c1) ? fkey(vrow[c]) : 0u;
-      });
-    }
-    static_for<VPT>([&](auto j) __attribute__((always_inline)) {
-      uint32_t k = key[j];
-      if (mrow) {
-        const int c = cb + j;
-        const int64_t mj = (int64_t)c + mshift;
-        if (!(c >= c0 && c < c1 && mj < a.mask_w && mrow[mj])) k = 0;
-      }
-      key[j] = k > floor_key ? k : 0u;
-    });
 
-    uint32_t nloc = 0;
-    static_for<RS>([&](auto j) __attribute__((always_inline)) { nloc += rkey[j] != 0; });
-    static_for<VPT>([&](auto j) __attribute__((always_inline)) { nloc += key[j] != 0; });
-    const int total = (int)block_sum(sm, nloc, lane, wave);
-
-    uint32_t thk = 0;   // threshold key (0: take every candidate)
-    int need_eq = 0;    // how many keys equal to thk to take, lowest ids first
-    if (total > K) {
-      uint32_t clo = 1, chi = 0xFFFFFFFFu;  // current candidate key interval
-      int need = K, cnt = total;
-      bool done = false;
-      for (int level = 0; level < 4 && !done; ++level) {
-        uint32_t lo = 0xFFFFFFFFu, hi = 0;
-        auto mm = [&](uint32_t k) __attribute__((always_inline)) {
-          if (k >= clo && k <= chi) { lo = min(lo, k); hi = max(hi, k); }
-        };
-        static_for<RS>([&](auto j) __attribute__((always_inline)) { mm(rkey[j]); });
-        static_for<VPT>([&](auto j) __attribute__((always_inline)) { mm(key[j]); });
-        block_minmax(sm, lo, hi, lane, wave);
-        if (lo == hi) { thk = lo; done = true; break; }
-        if (cnt <= CAP) {
-          // rank the remaining candidates directly
-          __syncthreads();
-          if (tid == 0) sm.bcast[0] = 0;
-          __syncthreads();
-          auto put = [&](uint32_t k) __attribute__((always_inline)) {
-            if (k >= lo && k <= hi) {
-              const uint32_t slot = atomicAdd(&sm.bcast[0], 1u);
-              if (slot < CAP) sm.cand[slot] = k;
-            }
-          };
-          static_for<RS>([&](auto j) __attribute__((always_inline)) { put(rkey[j]); });
-          static_for<VPT>([&](auto j) __attribute__((always_inline)) { put(key[j]); });
-          __syncthreads();
-          if (tid < cnt) {
-            const uint32_t mine = sm.cand[tid];
-            int gt = 0, ge = 0;
-            for (int j = 0; j < cnt; ++j) {
-              const uint32_t o = sm.cand[j];
-              gt += o > mine;
-              ge += o >= mine;
-            }
-            if (gt < need && need <= ge) sm.bcast[1] = mine;
-          }
-          __syncthreads();
-          thk = sm.bcast[1];
-          done = true;
-          break;
+    // ---- the segment's keys, in registers: key[c][j] is column S + 8192 c + 16 tid + j
+    uint32_t key[NCH][VPT];
+    {
+      float raw[NCH][VPT];
+      static_for<NCH>([&](auto c) __attribute__((always_inline)) {
+        const int cb = S + c * SPAN + tid * VPT;
+        if (vec && cb >= s0 && cb + VPT <= s1) {
+          static_for<VPT / 4>([&](auto q) __attribute__((always_inline)) {
+            const float4 v = *(const float4 *)(vrow + cb + 4 * q);
+            raw[c][4 * q + 0] = v.x;
+            raw[c][4 * q + 1] = v.y;
+            raw[c][4 * q + 2] = v.z;
+            raw[c][4 * q + 3] = v.w;
+          });
+        } else {
+          static_for<VPT>([&](auto j) __attribute__((always_inline)) {
+            const int col = cb + j;
+            raw[c][j] = (col >= s0 && col < s1) ? vrow[col] : 0.f;
+          });
         }
+      });
+      static_for<NCH>([&](auto c) __attribute__((always_inline)) {
+        const int cb = S + c * SPAN + tid * VPT;
+        static_for<VPT>([&](auto j) __attribute__((always_inline)) {
+          const int col = cb + j;
+          const bool inside = col >= s0 && col < s1;
+          uint32_t k = inside ? fkey(raw[c][j]) : 0u;
+          if (mrow) {
+            const int64_t mj = (int64_t)col + mshift;
+            if (!(inside && mj < a.mask_w && mrow[mj])) k = 0;
+          }
+          key[c][j] = k > floor_key ? k : 0u;
+        });
+      });
+    }
+
+    // ---- sweep 1: size and key range of the union
+    uint32_t total = 0, umin = 0xFFFFFFFFu, umax = 0;
+    {
+      uint32_t n = 0;
+      for (int p = tid; p < run_n; p += NTH) {
+        const uint32_t k = run_key(p);
+        ++n;
+        umin = min(umin, k);
+        umax = max(umax, k);
+      }
+      static_for<NCH>([&](auto c) __attribute__((always_inline)) {
+        static_for<VPT>([&](auto j) __attribute__((always_inline)) {
+          const uint32_t k = key[c][j];
+          n += k != 0u;
+          umin = min(umin, k != 0u ? k : 0xFFFFFFFFu);
+          umax = max(umax, k);
+        });
+      });
+      total = n;
+      block_sum_minmax(sm, total, umin, umax, lane, wave);
+    }
+
+    // ---- passes 2..: the bin holding the K-th largest key
+    uint32_t clo = umin, chi = umax;  // candidate interval
+    int need = K;                     // picks still to make inside [clo, chi]
+    uint32_t sel = 0;                 // union entries above the interval (all taken)
+    uint32_t icnt = total;            // union entries inside the interval
+    uint32_t theta = 1;               // collect segment keys >= theta
+    uint32_t thk = 0;                 // final: keys > thk taken, then need_eq keys == thk by id
+    int need_eq = 0;
+    bool decided = false;             // thk / need_eq known before the LDS stage
+    if ((int)total <= K) {
+      decided = true;                 // everything is taken
+    } else {
+      for (int level = 0;; ++level) {
+        if (clo == chi) { thk = clo; need_eq = need; decided = true; break; }
+        // segment entries at or above clo: union entries there minus running ones
+        uint32_t rge = (uint32_t)run_n;
+        if (level > 0) {
+          uint32_t d0 = 0, d1 = 0;
+          rge = 0;
+          for (int p = tid; p < run_n; p += NTH) rge += run_key(p) >= clo;
+          block_sum_minmax(sm, rge, d0, d1, lane, wave);
+        }
+        if (sel + icnt - rge <= (uint32_t)CAPK) { theta = clo; break; }
+        const uint32_t span = chi - clo;
         int sh = 0;
-        while (((hi - lo) >> sh) >= (uint32_t)NB) ++sh;
+        if (level == 0 && (span >> TOP_LOG2) != 0) sh = TOP_SH;
+        else while ((span >> sh) >= (uint32_t)NB) ++sh;
         __syncthreads();
         for (int i = tid; i < NB; i += NTH) sm.hist[i] = 0;
         __syncthreads();
-        auto bin = [&](uint32_t k) __attribute__((always_inline)) {
-          if (k >= lo && k <= hi) atomicAdd(&sm.hist[(k - lo) >> sh], 1u);
-        };
-        static_for<RS>([&](auto j) __attribute__((always_inline)) { bin(rkey[j]); });
-        static_for<VPT>([&](auto j) __attribute__((always_inline)) { bin(key[j]); });
+        for (int p = tid; p < run_n; p += NTH) {
+          const uint32_t k = run_key(p);
+          if (k >= clo && k <= chi) atomicAdd(&sm.hist[bin_of(k, chi, sh)], 1u);
+        }
+        static_for<NCH>([&](auto c) __attribute__((always_inline)) {
+          static_for<VPT>([&](auto j) __attribute__((always_inline)) {
+            const uint32_t k = key[c][j];
+            const bool in = k >= clo && k <= chi;  // others count into this lane's spare slot
+            atomicAdd(&sm.hist[in ? bin_of(k, chi, sh) : (uint32_t)(NB + lane)], 1u);
+          });
+          __builtin_amdgcn_sched_barrier(0);  // one chunk at a time: bounded live ranges
+        });
         __syncthreads();
-        // bin b* with (count above b*) < need <= (count at or above b*); thread i owns bins 4i..4i+3
+        // b*: (entries in bins before b*) < need <= (entries in bins up to b*); thread i owns bins 4i..4i+3
         {
           constexpr int BPT = NB / NTH;
-          uint32_t h[BPT];
-          uint32_t tot = 0;
+          uint32_t h[BPT], tot = 0;
 #pragma unroll
           for (int i = 0; i < BPT; ++i) { h[i] = sm.hist[tid * BPT + i]; tot += h[i]; }
-          uint32_t incl = tot;  // inclusive suffix within the wave (lanes >= this one)
-          for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t y = __shfl_down(incl, o);
-            if (lane + o < 64) incl += y;
-          }
-          __syncthreads();
-          if (lane == 0) sm.red[0][wave] = incl;  // wave total
-          __syncthreads();
-          uint32_t above = incl - tot;
-          for (int w = wave + 1; w < NWV; ++w) above += sm.red[0][w];
+          uint32_t before, d0, t0, t1;
+          block_scan2(sm, tot, 0u, before, d0, t0, t1, lane, wave);
 #pragma unroll
-          for (int i = BPT - 1; i >= 0; --i) {
-            if (above < (uint32_t)need && (uint32_t)need <= above + h[i]) {
+          for (int i = 0; i < BPT; ++i) {
+            if (before < (uint32_t)need && (uint32_t)need <= before + h[i]) {
               sm.bcast[0] = tid * BPT + i;
-              sm.bcast[1] = above;
+              sm.bcast[1] = before;
               sm.bcast[2] = h[i];
             }
-            above += h[i];
+            before += h[i];
+          }
+        }
+        __syncthreads();
+        const uint32_t bstar = sm.bcast[0];
+        const uint32_t above = sm.bcast[1];
+        icnt = sm.bcast[2];
+        need -= (int)above;
+        sel += above;
+        const int64_t hi64 = (int64_t)chi - ((int64_t)bstar << sh);
+        const int64_t lo64 = bstar == NB - 1 ? (int64_t)clo : (int64_t)chi - ((int64_t)(bstar + 1) << sh) + 1;
+        clo = (uint32_t)max(lo64, (int64_t)clo);
+        chi = (uint32_t)hi64;
+      }
+    }
+
+    // ---- pass: collect the segment's keys at or above theta (or, with thk decided,
+    // those that are taken), in column order.  Entries equal to thk are taken
+    // running ones first, then the segment's in column order.
+    uint32_t eq_run = 0;  // running entries equal to thk (taken first among equals)
+    if (decided && need_eq > 0) {
+      uint32_t e = 0, d0 = 0, d1 = 0;
+      for (int p = tid; p < run_n; p += NTH) e += run_key(p) == thk;
+      block_sum_minmax(sm, e, d0, d1, lane, wave);
+      eq_run = e;
+    }
+    const uint32_t eq_budget = need_eq > (int)eq_run ? (uint32_t)need_eq - eq_run : 0u;
+    const bool ties = decided && eq_budget > 0;   // block-uniform
+    auto kind_of = [&](uint32_t k) __attribute__((always_inline)) -> int {  // 1: taken, 2: equal to thk
+      if (!decided) return k >= theta ? 1 : 0;
+      if (k > thk) return 1;
+      return (k == thk && k != 0) ? 2 : 0;
+    };
+    // Ordered compaction in column order (chunk, thread, j): per-chunk counts of
+    // each thread, packed two 16-bit fields to a word, go through one block scan.
+    auto scan4 = [&](const uint32_t (&cnt)[NCH], uint32_t (&base)[NCH]) __attribute__((always_inline)) -> uint32_t {
+      uint32_t e0, e1, t0, t1;
+      block_scan2(sm, cnt[0] | (cnt[1] << 16), cnt[2] | (cnt[3] << 16), e0, e1, t0, t1, lane, wave);
+      const uint32_t tot[NCH] = {t0 & 0xFFFFu, t0 >> 16, t1 & 0xFFFFu, t1 >> 16};
+      const uint32_t ex[NCH] = {e0 & 0xFFFFu, e0 >> 16, e1 & 0xFFFFu, e1 >> 16};
+      uint32_t acc = 0;
+      static_for<NCH>([&](auto c) __attribute__((always_inline)) {
+        base[c] = acc + ex[c];
+        acc += tot[c];
+      });
+      return acc;
+    };
+    uint32_t eqb[NCH] = {0u, 0u, 0u, 0u};   // equal keys before this thread's chunk-c entries
+    if (ties) {
+      uint32_t ne[NCH];
+      static_for<NCH>([&](auto c) __attribute__((always_inline)) {
+        ne[c] = 0;
+        static_for<VPT>([&](auto j) __attribute__((always_inline)) { ne[c] += kind_of(key[c][j]) == 2; });
+      });
+      scan4(ne, eqb);
+    }
+    // taken entries of chunk c as a 16-bit mask (bit j: column 8192 c + 16 tid + j)
+    uint32_t tb[NCH], nt[NCH], posb[NCH];
+    if (!ties) {
+      // keys >= X: theta while the K-th key is still open, thk + 1 once it is known
+      const bool none = decided && thk == 0xFFFFFFFFu;
+      const uint32_t X = decided ? thk + 1u : theta;
+      static_for<NCH>([&](auto c) __attribute__((always_inline)) {
+        tb[c] = 0;
+        static_for<VPT>([&](auto j) __attribute__((always_inline)) {
+          tb[c] |= (uint32_t)(key[c][j] >= X && !none) << j;
+        });
+        nt[c] = __builtin_popcount(tb[c]);
+      });
+    } else {
+      static_for<NCH>([&](auto c) __attribute__((always_inline)) {
+        uint32_t e = eqb[c];
+        tb[c] = 0;
+        static_for<VPT>([&](auto j) __attribute__((always_inline)) {
+          const int kd = kind_of(key[c][j]);
+          const bool tk = kd == 1 || (kd == 2 && e++ < eq_budget);
+          tb[c] |= (uint32_t)tk << j;
+        });
+        nt[c] = __builtin_popcount(tb[c]);
+      });
+    }
+    const int M_all = (int)scan4(nt, posb);
+    // every entry is written: taken ones to their slot, the rest to this lane's spare slot
+    static_for<NCH>([&](auto c) __attribute__((always_inline)) {
+      uint32_t pos = posb[c];
+      static_for<VPT>([&](auto j) __attribute__((always_inline)) {
+        const bool tk = (tb[c] >> j) & 1u;
+        const uint32_t slot = tk && pos < (uint32_t)CAPK ? pos : (uint32_t)(CAPK + lane);
+        sm.kkey[slot] = key[c][j];
+        sm.kcol[slot] = (uint16_t)(c * SPAN + tid * VPT + j);
+        pos += tk;
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    int M = M_all;
+    M = min(M, CAPK);
+    __syncthreads();
+
+    // ---- exact K-th key among the LDS-resident entries of [clo, chi]
+    const int N = run_n + M;
+    auto item_key = [&](int i) __attribute__((always_inline)) -> uint32_t {
+      return i < run_n ? run_key(i) : sm.kkey[i - run_n];
+    };
+    if (!decided) {
+      for (;;) {
+        if (clo == chi) { thk = clo; need_eq = need; break; }
+        if (icnt <= (uint32_t)CAP) {
+          // rank the interval's entries directly
+          __syncthreads();
+          if (tid == 0) sm.bcast[0] = 0;
+          __syncthreads();
+          for (int i = tid; i < N; i += NTH) {
+            const uint32_t k = item_key(i);
+            if (k >= clo && k <= chi) {
+              const uint32_t slot = atomicAdd(&sm.bcast[0], 1u);
+              if (slot < (uint32_t)CAP) sm.hist[slot] = k;
+            }
+          }
+          __syncthreads();
+          const int n = (int)min(sm.bcast[0], (uint32_t)CAP);
+          if (tid < n) {
+            const uint32_t mine = sm.hist[tid];
+            int gt = 0, ge = 0;
+            for (int j = 0; j < n; ++j) {
+              const uint32_t o = sm.hist[j];
+              gt += o > mine;
+              ge += o >= mine;
+            }
+            if (gt < need && need <= ge) { sm.bcast[1] = mine; sm.bcast[2] = (uint32_t)(need - gt); }
+          }
+          __syncthreads();
+          thk = sm.bcast[1];
+          need_eq = (int)sm.bcast[2];
+          break;
+        }
+        const uint32_t span = chi - clo;
+        int sh = 0;
+        while ((span >> sh) >= (uint32_t)NB) ++sh;
+        __syncthreads();
+        for (int i = tid; i < NB; i += NTH) sm.hist[i] = 0;
+        __syncthreads();
+        for (int i = tid; i < N; i += NTH) {
+          const uint32_t k = item_key(i);
+          if (k >= clo && k <= chi) atomicAdd(&sm.hist[bin_of(k, chi, sh)], 1u);
+        }
+        __syncthreads();
+        {
+          constexpr int BPT = NB / NTH;
+          uint32_t h[BPT], tot = 0;
+#pragma unroll
+          for (int i = 0; i < BPT; ++i) { h[i] = sm.hist[tid * BPT + i]; tot += h[i]; }
+          uint32_t before, d0, t0, t1;
+          block_scan2(sm, tot, 0u, before, d0, t0, t1, lane, wave);
+#pragma unroll
+          for (int i = 0; i < BPT; ++i) {
+            if (before < (uint32_t)need && (uint32_t)need <= before + h[i]) {
+              sm.bcast[0] = tid * BPT + i;
+              sm.bcast[1] = before;
+              sm.bcast[2] = h[i];
+            }
+            before += h[i];
           }
         }
         __syncthreads();
         const uint32_t bstar = sm.bcast[0];
         need -= (int)sm.bcast[1];
-        cnt = (int)sm.bcast[2];
-        clo = lo + (bstar << sh);
-        const uint64_t top = (uint64_t)lo + ((uint64_t)(bstar + 1) << sh) - 1;
-        chi = (uint32_t)min<uint64_t>(top, (uint64_t)hi);
+        icnt = sm.bcast[2];
+        const uint32_t nhi = chi - (bstar << sh);
+        clo = max(clo, nhi - min(nhi - clo, (1u << sh) - 1u));
+        chi = nhi;
       }
-      if (!done) thk = clo;  // unreachable: each level narrows the interval by >= 11 of 32 bits
-      uint32_t gt = 0;
-      static_for<RS>([&](auto j) __attribute__((always_inline)) { gt += rkey[j] > thk; });
-      static_for<VPT>([&](auto j) __attribute__((always_inline)) { gt += key[j] > thk; });
-      need_eq = K - (int)block_sum(sm, gt, lane, wave);
+    } else if ((int)total <= K) {
+      thk = 0;       // take every entry
+      need_eq = 0;
     }
 
-    // ---- selection in id order: keys above thk, then the first need_eq keys equal to it.
-    // Running slots (ids below every pass id) come first, each group in thread order.
-    uint32_t eq_r = 0, eq_p = 0;
-    if (need_eq > 0) {
-      static_for<RS>([&](auto j) __attribute__((always_inline)) { eq_r += rkey[j] == thk; });
-      static_for<VPT>([&](auto j) __attribute__((always_inline)) { eq_p += key[j] == thk; });
-    }
-    uint32_t eo_r, eo_p, et_r, et_p;
-    block_scan2(sm, eq_r, eq_p, eo_r, eo_p, et_r, et_p, lane, wave);
-    // equal keys are taken in id order: running ones first (ranks 0 .. et_r - 1), then the pass's
-    const uint32_t eqrank_r = eo_r, eqrank_p = et_r + eo_p;
-    auto taken = [&](uint32_t k, uint32_t &eqrank) __attribute__((always_inline)) -> bool {
-      if (k == 0) return false;
-      if (k > thk) return true;
-      if (k == thk && need_eq > 0) return eqrank++ < (uint32_t)need_eq;
-      return false;
-    };
-    uint32_t tk_r = 0, tk_p = 0;
+    // ---- new running list: taken entries of (running ++ collected), id order
     {
-      uint32_t e1 = eqrank_r, e2 = eqrank_p;
-      static_for<RS>([&](auto j) __attribute__((always_inline)) { tk_r += taken(rkey[j], e1); });
-      static_for<VPT>([&](auto j) __attribute__((always_inline)) { tk_p += taken(key[j], e2); });
-    }
-    uint32_t po_r, po_p, pt_r, pt_p;
-    block_scan2(sm, tk_r, tk_p, po_r, po_p, pt_r, pt_p, lane, wave);
-    const int nxt = cur ^ 1;
-    {
-      uint32_t e1 = eqrank_r, e2 = eqrank_p;
-      uint32_t pr = po_r, pp = pt_r + po_p;
-      static_for<RS>([&](auto j) __attribute__((always_inline)) {
-        if (taken(rkey[j], e1)) {
-          if (pr < (uint32_t)KMAX) {
-            sm.run_id[nxt][pr] = sm.run_id[cur][tid * RS + j];
-            sm.run_val[nxt][pr] = kval(rkey[j]);
+      constexpr int IPT = (KMAX + CAPK + NTH - 1) / NTH;
+      const int i0 = tid * IPT;
+      auto taken_kind = [&](uint32_t k) __attribute__((always_inline)) -> int {
+        if (k == 0) return 0;
+        if (k > thk) return 1;
+        return k == thk && need_eq > 0 ? 2 : 0;  // 2: equal, taken by rank
+      };
+      uint32_t neq = 0;
+#pragma unroll 2
+      for (int u = 0; u < IPT; ++u) {
+        const int i = i0 + u;
+        if (i < N) neq += taken_kind(item_key(i)) == 2;
+      }
+      uint32_t eo, d0, d1, d2;
+      block_scan2(sm, neq, 0u, eo, d0, d1, d2, lane, wave);
+      uint32_t ntk = 0;
+      {
+        uint32_t e = eo;
+        for (int u = 0; u < IPT; ++u) {
+          const int i = i0 + u;
+          if (i < N) {
+            const int kind = taken_kind(item_key(i));
+            ntk += kind == 1 || (kind == 2 && e++ < (uint32_t)need_eq);
           }
-          ++pr;
         }
-      });
-      static_for<VPT>([&](auto j) __attribute__((always_inline)) {
-        if (taken(key[j], e2)) {
-          if (pp < (uint32_t)KMAX) {
-            sm.run_id[nxt][pp] = off + cb + j;
-            sm.run_val[nxt][pp] = kval(key[j]);
+      }
+      uint32_t po, pt, d3, d4;
+      block_scan2(sm, ntk, 0u, po, d3, pt, d4, lane, wave);
+      const int nxt = cur ^ 1;
+      {
+        uint32_t e = eo, pos = po;
+        for (int u = 0; u < IPT; ++u) {
+          const int i = i0 + u;
+          if (i < N) {
+            const uint32_t k = item_key(i);
+            const int kind = taken_kind(k);
+            if (kind == 1 || (kind == 2 && e++ < (uint32_t)need_eq)) {
+              if (pos < (uint32_t)KMAX) {
+                sm.run_id[nxt][pos] = i < run_n ? sm.run_id[cur][i] : off + S + (int)sm.kcol[i - run_n];
+                sm.run_val[nxt][pos] = kval(k);
+              }
+              ++pos;
+            }
           }
-          ++pp;
         }
-      });
+      }
+      run_n = min((int)pt, K);
+      cur = nxt;
+      __syncthreads();
     }
-    run_n = min((int)(pt_r + pt_p), K);
-    cur = nxt;
-    __syncthreads();
   }
 
   // ---- write the running list

@@ -105,19 +105,19 @@ def test_workspace_sizes(lib):
     p = _problem(T=2048, L=65536)
     n = ctypes.c_size_t()
     assert lib.idx_workspace_size(2, ctypes.byref(p), 2048, 32768, 0, 0, 0, 0, ctypes.byref(n)) == 0
-    assert n.value == head + 2 * _r(2048 * kc(2048) * 4) + 2048 * 32768 * 4
+    assert n.value == head + 2 * _r(2048 * kc(2048) * 4) + 2048 * (32768 + 64) * 4
     # the row chunk bounds the workspace; the number of keys does not enter
     p2 = _problem(T=16384, L=487936)
     assert lib.idx_workspace_size(2, ctypes.byref(p2), 512, 32768, 4096, 0, 0, 0, ctypes.byref(n)) == 0
-    assert n.value == head + 2 * _r(4096 * kc(512) * 4) + 4096 * 32768 * 4
+    assert n.value == head + 2 * _r(4096 * kc(512) * 4) + 4096 * (32768 + 64) * 4
     p3 = _problem(T=16384, L=65536)
     m = ctypes.c_size_t()
     assert lib.idx_workspace_size(2, ctypes.byref(p3), 512, 32768, 4096, 0, 0, 0, ctypes.byref(m)) == 0
     assert m.value == n.value
     assert lib.idx_workspace_size(3, ctypes.byref(p), 0, 32768, 0, 8, 2048, 0, ctypes.byref(n)) == 0
-    assert n.value == head + 2 * _r(2048 * kc(2048) * 4) + 2048 * 4096 * 4 + 2048 * 2048 * 4
+    assert n.value == head + 2 * _r(2048 * kc(2048) * 4) + 2048 * (4096 + 64) * 4 + 2048 * 2048 * 4
     assert lib.idx_workspace_size(4, ctypes.byref(p), 0, 0, 1024, 8, 2048, 65536, ctypes.byref(n)) == 0
-    assert n.value == head + 2 * _r(1024 * kc(2048) * 4) + 1024 * 8192 * 4 + 1024 * 2048 * 4
+    assert n.value == head + 2 * _r(1024 * kc(2048) * 4) + 1024 * (8192 + 64) * 4 + 1024 * 2048 * 4
     assert lib.idx_workspace_size(0, ctypes.byref(p), 0, 0, 0, 0, 0, 0, ctypes.byref(n)) == 0 and n.value == 0
     assert lib.idx_workspace_size(2, ctypes.byref(p), 0, 32768, 0, 0, 0, 0, ctypes.byref(n)) == 3
     assert lib.idx_workspace_size(9, ctypes.byref(p), 1, 256, 0, 0, 0, 0, ctypes.byref(n)) == 3
