@@ -37,11 +37,14 @@
 namespace idx {
 namespace {
 
-constexpr int NTH = 512;
+constexpr int NTH = 256;
 constexpr int NWV = NTH / 64;
-constexpr int KC_MAX = 2560;
-constexpr int QSTRIDE = 129;   // padded fp32 q row in LDS (conflict-free per-head reads)
-constexpr int KB = 16;         // band keys scored per batch
+constexpr int PER = 10;                 // candidates per thread, contiguous
+constexpr int KC_MAX = NTH * PER;       // 2560
+constexpr int KB = 16;                  // band keys scored per batch
+constexpr int KPAD = 34;                // doubles per 32-element key chunk in LDS (chunks on distinct banks)
+constexpr int NB = 2048;                // selection histogram bins
+constexpr int RCAP = 256;               // direct ranking threshold
 constexpr float GAMMA = 2.0f;
 
 // OCP E4M3 ("FN") code -> float, exact.
@@ -59,28 +62,110 @@ __device__ __forceinline__ float e2m1(uint32_t c) {
   return (c & 8u) ? -v : v;
 }
 
+// Wave reductions on DPP / permlane moves (32-bit lanes; doubles move as two halves).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// sum over the 4 lanes of a quad
+__device__ __forceinline__ double quad_sum_f64(double x) {
+  x += dpp_f64<0xB1>(x);  // quad [1,0,3,2]
+  x += dpp_f64<0x4E>(x);  // quad [2,3,0,1]
+  return x;
+}
+// sum over the 16 lanes 4 i (i < 16) of a wave: quads already hold their sums
+__device__ __forceinline__ double quads_sum_f64(double x) {
+  x += dpp_f64<0x141>(x);  // row half mirror: pairs the two quads of each half row
+  x += dpp_f64<0x140>(x);  // row mirror: pairs the half rows
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const auto l16 = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+  const auto h16 = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+  x = __longlong_as_double((long long)(((uint64_t)h16[0] << 32) | l16[0])) +
+      __longlong_as_double((long long)(((uint64_t)h16[1] << 32) | l16[1]));
+  const uint64_t v = (uint64_t)__double_as_longlong(x);
+  const auto l32 = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  const auto h32 = __builtin_amdgcn_permlane32_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+  return __longlong_as_double((long long)(((uint64_t)h32[0] << 32) | l32[0])) +
+         __longlong_as_double((long long)(((uint64_t)h32[1] << 32) | l32[1]));
+}
+template <class T, class Op>
+__device__ __forceinline__ T wave_all(T x, Op op) {
+  for (int o = 32; o > 0; o >>= 1) x = op(x, __shfl_xor(x, o));
+  return x;
+}
+
+static_assert(KB * 4 * KPAD * 2 >= NB + 64 + RCAP && KB * 4 * KPAD * 2 >= KC_MAX, "key buffer overlays");
+
 struct Smem {
-  int32_t cid[KC_MAX];
-  float cval[KC_MAX];
-  uint8_t state[KC_MAX];        // 0 out, 1 certain, 2 band, 3 band selected
-  int16_t band[KC_MAX];         // band entry -> candidate slot
-  uint32_t bkey[KC_MAX];        // exact score key of band entries
-  float qf[64 * QSTRIDE];       // decoded q row (fp32, exact)
-  float kf[KB][128];            // decoded key batch (element values without MX block scales)
-  double ksc[KB][4];            // per-key scale: fp8: k_scale (all four); MXFP4: the four block scales
-  double dots[KB][64];          // exact raw dots of the batch
-  int32_t bk_key[KB];           // batch entry -> key row (-1: none)
-  int32_t bk_band[KB];          // batch entry -> band entry
-  uint32_t hist[256];
-  int seg[NWV + 1];
-  float red[NWV];
-  uint32_t ured[NWV];
+  uint8_t state[KC_MAX];       // per candidate slot: 0 out, 1 certain, 2 band, 3 band and taken
+  int16_t band[KC_MAX];        // band entry -> candidate slot
+  uint32_t bexact[KC_MAX];     // band entry -> key of its exact score (pooled: max over its keys)
+  int32_t bid[KC_MAX];         // band entry -> candidate id
+  double kd[KB][4][KPAD];      // decoded key rows of a batch by 32-element chunk (element values, no
+                               // MX block scale); also the selection's histogram, and at the end the
+                               // taken band entries' exact scores by slot
+  double ksc[KB][4];           // per key: k_scale (fp8, all four) or the four MX block scales
+  int32_t bk_key[KB];          // batch slot -> key row (-1: none)
+  int32_t bk_ent[KB];          // batch slot -> band entry
+  double part[KB][NWV];        // per key and wave: head-sum partials
+  uint32_t red[3][NWV];
+  float fred[NWV];
   uint32_t misc[8];
 };
 
-__device__ __forceinline__ uint32_t wave_sum_u(uint32_t x) {
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+// Block-wide sum / min / max helpers (all threads call).
+__device__ __forceinline__ uint32_t block_sum(Smem &sm, uint32_t x, int lane, int wave) {
+  x = wave_all(x, [](uint32_t a, uint32_t b) { return a + b; });
+  __syncthreads();
+  if (lane == 0) sm.red[0][wave] = x;
+  __syncthreads();
+  uint32_t s = 0;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) s += sm.red[0][w];
+  return s;
+}
+__device__ __forceinline__ void block_sum3(Smem &sm, uint32_t &a, uint32_t &b, uint32_t &c, int lane, int wave) {
+  auto add = [](uint32_t x, uint32_t y) { return x + y; };
+  a = wave_all(a, add);
+  b = wave_all(b, add);
+  c = wave_all(c, add);
+  __syncthreads();
+  if (lane == 0) { sm.red[0][wave] = a; sm.red[1][wave] = b; sm.red[2][wave] = c; }
+  __syncthreads();
+  a = b = c = 0;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) { a += sm.red[0][w]; b += sm.red[1][w]; c += sm.red[2][w]; }
+}
+
+__device__ __forceinline__ void block_minmax(Smem &sm, uint32_t &lo, uint32_t &hi, int lane, int wave) {
+  lo = wave_all(lo, [](uint32_t x, uint32_t y) { return min(x, y); });
+  hi = wave_all(hi, [](uint32_t x, uint32_t y) { return max(x, y); });
+  __syncthreads();
+  if (lane == 0) { sm.red[1][wave] = lo; sm.red[2][wave] = hi; }
+  __syncthreads();
+  lo = 0xFFFFFFFFu;
+  hi = 0;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) { lo = min(lo, sm.red[1][w]); hi = max(hi, sm.red[2][w]); }
+}
+// Exclusive prefix sum in thread order.
+__device__ __forceinline__ uint32_t block_excl_scan(Smem &sm, uint32_t x, int lane, int wave) {
+  uint32_t incl = x;
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  __syncthreads();
+  if (lane == 63) sm.red[0][wave] = incl;
+  __syncthreads();
+  uint32_t before = incl - x;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w)
+    if (w < wave) before += sm.red[0][w];
+  return before;
 }
 
 __global__ __launch_bounds__(NTH) void refine_kernel(RefineArgs a) {
@@ -95,242 +180,303 @@ __global__ __launch_bounds__(NTH) void refine_kernel(RefineArgs a) {
   int32_t *oidx = a.out_idx + (int64_t)r * K;
   float *oval = a.out_val ? a.out_val + (int64_t)r * K : nullptr;
 
-  // ---- candidates (ids ascending, -1 padded)
-  uint32_t cnt = 0;
-  for (int i = tid; i < Kc; i += NTH) {
-    const int id = cidx[i];
-    sm.cid[i] = id;
-    sm.cval[i] = cval[i];
-    sm.state[i] = 0;
-    cnt += id >= 0;
-  }
-  cnt = wave_sum_u(cnt);
-  if (lane == 0) sm.ured[wave] = cnt;
-  __syncthreads();
-  int n = 0;
+  // ---- candidates (ids ascending, -1 padded): thread tid holds slots PER tid .. PER tid + PER - 1
+  int32_t cid[PER];
+  float cv[PER];
+  uint32_t mine = 0;
 #pragma unroll
-  for (int w = 0; w < NWV; ++w) n += sm.ured[w];
+  for (int e = 0; e < PER; ++e) {
+    const int i = tid * PER + e;
+    cid[e] = i < Kc ? cidx[i] : -1;
+    cv[e] = i < Kc ? cval[i] : 0.f;
+    mine += cid[e] >= 0;
+  }
+  // ---- this lane's q slice: head h = 16 (wave % hw) + lane / 4, dims 32 (lane % 4) .. + 31
+  const int hw = H / 16;                        // waves covering all heads (2 or 4)
+  const int hq = 16 * (wave % hw) + (lane >> 2);
+  const int cc = lane & 3;
+  double qd[32];
+  {
+    const uint8_t *qp = a.q + ((int64_t)t * H + hq) * 128 + 32 * cc;
+    const uint4 u0 = *(const uint4 *)qp, u1 = *(const uint4 *)(qp + 16);
+    const uint32_t w8[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) qd[i] = (double)e4m3((w8[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+  }
+  const float wh = a.w[(int64_t)t * H + hq];
+  const float qsh = a.q_scale[(int64_t)t * H + hq];
+  const int n = (int)block_sum(sm, mine, lane, wave);
 
   if (n > K) {
-    // ---- theta: key of the K-th largest candidate (radix select, 4 x 8 bits)
-    uint32_t prefix = 0, pmask = 0;
+    // ---- theta: key of the K-th largest candidate.  Histograms over the candidates'
+    // key range [clo, chi] (bins anchored at chi) narrow it to one bin until at most
+    // RCAP candidates remain, which are ranked directly.
+    uint32_t *hist = (uint32_t *)&sm.kd[0][0][0];   // NB bins + one spare slot per lane
+    uint32_t *rl = hist + NB + 64;                   // ranking list
+    uint32_t ck[PER];
+    uint32_t clo = 0xFFFFFFFFu, chi = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      ck[e] = cid[e] >= 0 ? fkey(cv[e]) : 0u;
+      if (cid[e] >= 0) { clo = min(clo, ck[e]); chi = max(chi, ck[e]); }
+    }
+    block_minmax(sm, clo, chi, lane, wave);
     int need = K;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      __syncthreads();
-      if (tid < 256) sm.hist[tid] = 0;
-      __syncthreads();
-      for (int i = tid; i < n; i += NTH) {
-        const uint32_t k = fkey(sm.cval[i]);
-        if ((k & pmask) == prefix) atomicAdd(&sm.hist[(k >> shift) & 0xFF], 1u);
-      }
-      __syncthreads();
-      // threads 0..255 own bins; suffix sums give, per bin, the count strictly above it
-      uint32_t h = 0, incl = 0;
-      if (tid < 256) {
-        h = sm.hist[tid];
-        incl = h;
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t y = __shfl_down(incl, o);
-          if (lane + o < 64) incl += y;
+    uint32_t icnt = (uint32_t)n, thk;
+    for (;;) {
+      if (clo == chi) { thk = clo; break; }
+      if (icnt <= (uint32_t)RCAP) {
+        __syncthreads();
+        if (tid == 0) sm.misc[0] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          if (cid[e] >= 0 && ck[e] >= clo && ck[e] <= chi) {
+            const uint32_t slot = atomicAdd(&sm.misc[0], 1u);
+            if (slot < (uint32_t)RCAP) rl[slot] = ck[e];
+          }
         }
-        if (lane == 0) sm.ured[wave] = incl;
+        __syncthreads();
+        const int m = (int)min(sm.misc[0], (uint32_t)RCAP);
+        if (tid < m) {
+          const uint32_t me = rl[tid];
+          int gt = 0, ge = 0;
+          for (int j = 0; j < m; ++j) {
+            const uint32_t o = rl[j];
+            gt += o > me;
+            ge += o >= me;
+          }
+          if (gt < need && need <= ge) sm.misc[1] = me;
+        }
+        __syncthreads();
+        thk = sm.misc[1];
+        break;
+      }
+      int sh = 0;
+      while (((chi - clo) >> sh) >= (uint32_t)NB) ++sh;
+      __syncthreads();
+      for (int i = tid; i < NB; i += NTH) hist[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const bool in = cid[e] >= 0 && ck[e] >= clo && ck[e] <= chi;
+        atomicAdd(&hist[in ? (chi - ck[e]) >> sh : (uint32_t)(NB + lane)], 1u);
       }
       __syncthreads();
-      if (tid < 256) {
-        uint32_t above = incl - h;
-        for (int w = wave + 1; w < 4; ++w) above += sm.ured[w];
-        if (above < (uint32_t)need && (uint32_t)need <= above + h) {
-          sm.misc[0] = tid;
-          sm.misc[1] = above;
+      {
+        constexpr int BPT = NB / NTH;   // bins 8 tid .. 8 tid + 7
+        uint32_t h[BPT], tot = 0;
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) { h[i] = hist[tid * BPT + i]; tot += h[i]; }
+        uint32_t before = block_excl_scan(sm, tot, lane, wave);
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+          if (before < (uint32_t)need && (uint32_t)need <= before + h[i]) {
+            sm.misc[0] = tid * BPT + i;
+            sm.misc[1] = before;
+            sm.misc[2] = h[i];
+          }
+          before += h[i];
         }
       }
       __syncthreads();
-      prefix |= sm.misc[0] << shift;
-      pmask |= 0xFFu << shift;
+      const uint32_t bstar = sm.misc[0];
       need -= (int)sm.misc[1];
+      icnt = sm.misc[2];
+      const uint32_t nhi = chi - (bstar << sh);
+      clo = max(clo, nhi - min(nhi - clo, (1u << sh) - 1u));
+      chi = nhi;
     }
-    const float theta = kval(prefix);
+    const float theta = kval(thk);
 
-    // ---- per-row error bound: decode q into LDS and take per-head maxima
-    const uint8_t *qrow = a.q + (int64_t)t * H * 128;
-    for (int i = tid; i < H * 128; i += NTH) sm.qf[(i >> 7) * QSTRIDE + (i & 127)] = e4m3(qrow[i]);
-    __syncthreads();
-    float part = 0.f;
-    for (int h = wave; h < H; h += NWV) {
-      float mx = fmaxf(fabsf(sm.qf[h * QSTRIDE + lane]), fabsf(sm.qf[h * QSTRIDE + lane + 64]));
-      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-      part += fabsf(a.w[(int64_t)t * H + h] * a.q_scale[(int64_t)t * H + h] * a.scale) * mx;
-    }
-    if (lane == 0) sm.red[wave] = part;
+    // ---- per-row error bound D = GAMMA 2^-13 Kmax sum_h |w'_h| Mq_h (Mq_h: largest |q| of head h)
+    float mq = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) mq = fmaxf(mq, (float)fabs(qd[i]));
+    mq = fmaxf(mq, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mq), 0xB1, 0xF, 0xF, false)));
+    mq = fmaxf(mq, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mq), 0x4E, 0xF, 0xF, false)));
+    float part = (cc == 0 && wave < hw) ? fabsf(wh * qsh * a.scale) * mq : 0.f;
+    part = wave_all(part, [](float x, float y) { return x + y; });
     float kmax = 0.f;
     for (int i = lane; i < a.npart; i += 64) kmax = fmaxf(kmax, a.kmax_part[i]);
-    for (int o = 32; o > 0; o >>= 1) kmax = fmaxf(kmax, __shfl_xor(kmax, o));
+    kmax = wave_all(kmax, [](float x, float y) { return fmaxf(x, y); });
+    if (lane == 0) sm.fred[wave] = part;
+    if (tid == 0) sm.misc[2] = 0;
     __syncthreads();
     float S = 0.f;
 #pragma unroll
-    for (int w = 0; w < NWV; ++w) S += sm.red[w];
+    for (int w = 0; w < NWV; ++w) S += sm.fred[w];
     const double D = (double)GAMMA * 0.0001220703125 * (double)kmax * (double)S * 1.0000001;
     const double lo = (double)theta - 2.0 * D, hi = (double)theta + 2.0 * D;
 
-    // ---- classify, list the band, check that the list reaches below the band
-    if (tid == 0) sm.misc[2] = 0;
-    __syncthreads();
-    uint32_t nin = 0, below = 0;
-    for (int i = tid; i < n; i += NTH) {
-      const double v = (double)sm.cval[i];
+    // ---- classify; list the band; check that the list reaches below the band
+    uint32_t nin = 0, below = 0, nbm = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int i = tid * PER + e;
       uint8_t st = 0;
-      if (v > hi) { st = 1; ++nin; }
-      else if (v >= lo) {
-        st = 2;
-        const uint32_t slot = atomicAdd(&sm.misc[2], 1u);
-        sm.band[slot] = (int16_t)i;
-      } else {
-        ++below;
+      if (cid[e] >= 0) {
+        const double v = (double)cv[e];
+        if (v > hi) { st = 1; ++nin; }
+        else if (v >= lo) {
+          st = 2;
+          const uint32_t slot = atomicAdd(&sm.misc[2], 1u);
+          sm.band[slot] = (int16_t)i;
+          sm.bid[slot] = cid[e];
+          sm.bexact[slot] = 0;
+          ++nbm;
+        } else {
+          ++below;
+        }
       }
       sm.state[i] = st;
     }
-    nin = wave_sum_u(nin);
-    below = wave_sum_u(below);
-    __syncthreads();
-    if (lane == 0) { sm.ured[wave] = nin; sm.hist[wave] = below; }
-    __syncthreads();
-    int n_in = 0, n_below = 0;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) { n_in += sm.ured[w]; n_below += sm.hist[w]; }
-    const int nb = (int)sm.misc[2];
-    const int need_b = K - n_in;
-    if (tid == 0 && n == Kc && n_below == 0 && a.overflow) atomicAdd(a.overflow, 1u);
+    block_sum3(sm, nin, below, nbm, lane, wave);
+    const int nb = (int)nbm;
+    const int need_b = K - (int)nin;
+    if (tid == 0 && n == Kc && below == 0 && a.overflow) atomicAdd(a.overflow, 1u);
 
-    // ---- exact scores of the band, KB keys at a time
-    const int keys_per_entry = a.pool == 1 ? 1 : a.pool;
-    const int nkeys = nb * keys_per_entry;
+    // ---- exact scores of the band, KB keys per batch (raw bytes of batch b + 1 fetched early)
+    const int kpe = a.pool == 1 ? 1 : a.pool;   // keys per band entry
+    const int nkeys = nb * kpe;
     const int ks = max(a.ks[t], 0), ke = min(a.ke[t], a.L);
-    for (int j = tid; j < nb; j += NTH) sm.bkey[j] = 0;  // running max of exact values (key form)
+    const int kbytes = a.k_fmt == 0 ? 128 : 64;
+    // batch element of this thread: key slot j = tid / 16, 16-thread groups read 8 (fp8) / 4 (fp4) bytes each
+    const int jb = tid >> 4, part16 = tid & 15;
+    auto key_of = [&](int e) __attribute__((always_inline)) -> int {  // batch element e -> key row or -1
+      if (e >= nkeys) return -1;
+      const int be = e / kpe;
+      const int id = sm.bid[be];
+      int s = a.pool == 1 ? id : ks + id * a.pool + e % kpe;
+      if (s < 0 || s >= a.L || (a.pool > 1 && s >= ke)) s = -1;
+      return s;
+    };
+    uint2 raw = {0u, 0u};
+    uint32_t rsc = 0;
+    int rkey = -1;
+    auto fetch = [&](int base) __attribute__((always_inline)) {
+      rkey = key_of(base + jb);
+      raw = (uint2){0u, 0u};
+      rsc = 0;
+      if (rkey >= 0) {
+        if (a.k_fmt == 0) raw = *(const uint2 *)(a.k + (int64_t)rkey * 128 + 8 * part16);
+        else raw.x = *(const uint32_t *)(a.k + (int64_t)rkey * 64 + 4 * part16);
+        if (part16 == 0) rsc = *(const uint32_t *)(a.k_scale + (int64_t)rkey * 4);
+      }
+    };
+    __syncthreads();  // band lists complete
+    if (nkeys > 0) fetch(0);
     for (int base = 0; base < nkeys; base += KB) {
-      __syncthreads();
-      if (tid < KB) {
-        const int e = base + tid;
-        int s = -1, be = -1;
-        if (e < nkeys) {
-          be = e / keys_per_entry;
-          const int id = sm.cid[sm.band[be]];
-          s = a.pool == 1 ? id : ks + id * a.pool + e % keys_per_entry;
-          if (s < 0 || s >= a.L || (a.pool > 1 && s >= ke)) s = -1;
+      // decode the batch: thread (jb, part16) owns 8 elements of key slot jb
+      if (tid < KB * 16) {
+        if (part16 == 0) {
+          sm.bk_key[jb] = rkey;
+          sm.bk_ent[jb] = (base + jb) / kpe;
+          const float f = __uint_as_float(rsc);
+#pragma unroll
+          for (int blk = 0; blk < 4; ++blk)
+            sm.ksc[jb][blk] = rkey < 0 ? 0.0 : a.k_fmt == 0 ? (double)f : (double)e8m0((rsc >> (8 * blk)) & 0xFFu);
         }
-        sm.bk_key[tid] = s;
-        sm.bk_band[tid] = be;
-      }
-      __syncthreads();
-      // decode the batch's key rows (KB x 128 elements)
-      for (int i = tid; i < KB * 128; i += NTH) {
-        const int j = i >> 7, d = i & 127;
-        const int s = sm.bk_key[j];
-        float v = 0.f;
-        if (s >= 0) {
-          if (a.k_fmt == 0) {
-            v = e4m3(a.k[(int64_t)s * 128 + d]);
-          } else {
-            const uint32_t b = a.k[(int64_t)s * 64 + (d >> 1)];
-            v = e2m1((d & 1) ? (b >> 4) : (b & 0xF));
-          }
+        if (a.k_fmt == 0) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            sm.kd[jb][part16 >> 2][8 * (part16 & 3) + i] = (double)e4m3(((i < 4 ? raw.x : raw.y) >> (8 * (i & 3))) & 0xFFu);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sm.kd[jb][part16 >> 2][8 * (part16 & 3) + i] = (double)e2m1((raw.x >> (4 * i)) & 0xFu);
         }
-        sm.kf[j][d] = v;
-      }
-      if (tid < KB * 4) {
-        const int j = tid >> 2, blk = tid & 3;
-        const int s = sm.bk_key[j];
-        double sc = 0.0;
-        if (s >= 0)
-          sc = a.k_fmt == 0 ? (double)((const float *)a.k_scale)[s] : (double)e8m0(a.k_scale[(int64_t)s * 4 + blk]);
-        sm.ksc[j][blk] = sc;
       }
       __syncthreads();
-      // raw dots: thread -> (head h, keys j = jg, jg + NTH / H, ...); four 32-element block sums each
-      const int h = tid % H, jg = tid / H, jstep = NTH / H;
-      const float *qr = &sm.qf[h * QSTRIDE];
-      for (int j = jg; j < KB; j += jstep) {
+      if (base + KB < nkeys) fetch(base + KB);
+      // dots: waves of one head group share a key; lane (head, chunk) sums its 32 dims
+      const int kpw = NWV / hw;                       // keys in flight per step (1 for H = 64, 2 for H = 32)
+      for (int j0 = 0; j0 < KB; j0 += kpw) {
+        const int j = j0 + wave / hw;
         double acc = 0.0;
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-          double p0 = 0.0, p1 = 0.0, p2 = 0.0, p3 = 0.0;
-#pragma unroll 2
-          for (int d = blk * 32; d < blk * 32 + 32; d += 4) {
-            p0 += (double)qr[d] * (double)sm.kf[j][d];
-            p1 += (double)qr[d + 1] * (double)sm.kf[j][d + 1];
-            p2 += (double)qr[d + 2] * (double)sm.kf[j][d + 2];
-            p3 += (double)qr[d + 3] * (double)sm.kf[j][d + 3];
-          }
-          acc += ((p0 + p1) + (p2 + p3)) * sm.ksc[j][blk];  // fp8: all four scales equal k_scale
+        for (int i = 0; i < 32; i += 2) {
+          const double2 kk = *(const double2 *)&sm.kd[j][cc][i];
+          acc = fma(qd[i], kk.x, acc);
+          acc = fma(qd[i + 1], kk.y, acc);
         }
-        sm.dots[j][h] = acc;
+        // chunk sums are exact; MX block scales are powers of two, the fp8 k_scale
+        // multiplies the whole dot once
+        if (a.k_fmt != 0) acc *= sm.ksc[j][cc];
+        double dot = quad_sum_f64(acc);                // head hq, all 128 dims, in all 4 lanes
+        if (a.k_fmt == 0) dot *= sm.ksc[j][0];
+        const double dh = dot * (double)qsh * (double)a.scale;
+        const double term = (double)wh * (dh > 0.0 ? dh : 0.0);
+        const double ws = quads_sum_f64(term);         // 16 heads of this wave
+        if (lane == 0) sm.part[j][wave % hw] = ws;
       }
       __syncthreads();
-      // scores: one wave per key of the batch; lanes over heads
-      for (int j = wave; j < KB; j += NWV) {
-        const int s = sm.bk_key[j];
-        double term = 0.0;
-        if (s >= 0 && lane < H) {
-          const double dh = sm.dots[j][lane] * (double)a.q_scale[(int64_t)t * H + lane] * (double)a.scale;
-          term = (double)a.w[(int64_t)t * H + lane] * (dh > 0.0 ? dh : 0.0);
+      if (tid < KB) {
+        const int s = sm.bk_key[tid];
+        if (s >= 0) {
+          double sc = 0.0;
+          for (int w = 0; w < hw; ++w) sc += sm.part[tid][w];
+          atomicMax(&sm.bexact[sm.bk_ent[tid]], fkey((float)sc));
         }
-        for (int o = 32; o > 0; o >>= 1) term += __shfl_xor(term, o);
-        if (lane == 0 && s >= 0) atomicMax(&sm.bkey[sm.bk_band[j]], fkey((float)term));
       }
+      __syncthreads();
     }
-    __syncthreads();
-    // ---- order the band by (exact desc, id asc) and keep need_b of it
+    // ---- order the band by (exact desc, id asc) and take need_b of it
     for (int j = tid; j < nb; j += NTH) {
-      const uint32_t kj = sm.bkey[j];
-      const int idj = sm.cid[sm.band[j]];
+      const uint32_t kj = sm.bexact[j];
+      const int idj = sm.bid[j];
       int rank = 0;
       for (int m = 0; m < nb; ++m) {
-        const uint32_t km = sm.bkey[m];
-        rank += km > kj || (km == kj && sm.cid[sm.band[m]] < idj);
+        const uint32_t km = sm.bexact[m];
+        rank += km > kj || (km == kj && sm.bid[m] < idj);
       }
-      if (rank < need_b) {
-        const int i = sm.band[j];
-        sm.state[i] = 3;
-        sm.cval[i] = kval(kj);
-      }
+      if (rank < need_b) sm.state[sm.band[j]] = 3;
     }
     __syncthreads();
-  } else {
-    for (int i = tid; i < n; i += NTH) sm.state[i] = 1;
+    // taken band entries carry their exact score: per-slot values in the (now free) key buffer
+    float *sval = (float *)&sm.kd[0][0][0];
+    for (int j = tid; j < nb; j += NTH) {
+      const int i = sm.band[j];
+      if (sm.state[i] == 3) sval[i] = kval(sm.bexact[j]);
+    }
     __syncthreads();
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int i = tid * PER + e;
+      const uint8_t st = sm.state[i];
+      if (cid[e] >= 0 && st != 1 && st != 3) cid[e] = -2;   // not taken
+      if (st == 3) cv[e] = sval[i];
+    }
   }
 
   // ---- ordered compaction of kept candidates (ids ascending)
-  constexpr int PER = KC_MAX / NTH;  // candidates per thread, contiguous
-  int mine = 0;
+  uint32_t kept = 0;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int i = tid * PER + e;
-    mine += i < n && (sm.state[i] == 1 || sm.state[i] == 3);
-  }
-  int incl = mine;
+  for (int e = 0; e < PER; ++e) kept += cid[e] >= 0;
+  uint32_t incl = kept;
   for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o);
+    const uint32_t y = __shfl_up(incl, o);
     if (lane >= o) incl += y;
   }
-  if (lane == 63) sm.seg[wave] = incl;
   __syncthreads();
-  int pos = incl - mine;
-  for (int w = 0; w < wave; ++w) pos += sm.seg[w];
-  int total = 0;
+  if (lane == 63) sm.red[0][wave] = incl;
+  __syncthreads();
+  uint32_t pos = incl - kept, total = 0;
 #pragma unroll
-  for (int w = 0; w < NWV; ++w) total += sm.seg[w];
+  for (int w = 0; w < NWV; ++w) {
+    if (w < wave) pos += sm.red[0][w];
+    total += sm.red[0][w];
+  }
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    const int i = tid * PER + e;
-    if (i < n && (sm.state[i] == 1 || sm.state[i] == 3)) {
-      if (pos < K) {
-        oidx[pos] = sm.cid[i];
-        if (oval) oval[pos] = sm.cval[i];
+    if (cid[e] >= 0) {
+      if (pos < (uint32_t)K) {
+        oidx[pos] = cid[e];
+        if (oval) oval[pos] = cv[e];
       }
       ++pos;
     }
   }
-  for (int p = min(total, K) + tid; p < K; p += NTH) {
+  for (int p = (int)min(total, (uint32_t)K) + tid; p < K; p += NTH) {
     oidx[p] = -1;
     if (oval) oval[p] = -__builtin_inff();
   }
