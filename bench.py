@@ -48,10 +48,15 @@ def block_pairs(p, kb, nk):
 
 
 def kernel_source_hash():
+    """Hash of the scoring kernel's code (comments and blank lines excluded), to tell whether
+    committed counter figures were taken on the kernel as it stands."""
     h = hashlib.sha256()
     for f in ("logits.hip", "kernels.h"):
-        with open(os.path.join(ROOT, "mqa_logits_top_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "mqa_logits_top_amd", "csrc", f)) as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
@@ -128,6 +133,77 @@ def cpu_baseline(p, K, budget_s):
                       f"{pairs} pairs in {el:.1f} s (+{setup:.1f} s dequantisation, not counted)"}
 
 
+COPY_BYTES = 256 << 20   # calibration copy of the traffic probe
+
+
+def traffic_probe(dev):
+    """Launches for a rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE run: the scoring kernel on the
+    glm_chunk key blocks (as the fused path launches it), then a device-to-device copy of
+    COPY_BYTES that calibrates what those counters read for a known number of bytes."""
+    p = synth.make_config("glm_chunk")
+    d = idx.Inputs.from_host(p, device=dev)
+    Bk = p.meta["block_k"]
+    scratch = torch.empty((p.T, Bk), dtype=torch.float32, device=dev)
+    for rep in range(2):
+        for kb in range(0, p.L, Bk):
+            idx.idx_mqa_logits_block(d, 0, p.T, kb, min(Bk, p.L - kb), out=scratch)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for rep in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] traffic probe: {2 * ((p.L + Bk - 1) // Bk)} scoring launches, 2 copies of {COPY_BYTES} bytes")
+
+
+def traffic_summary(fetch_dir, write_dir):
+    """Per-launch HBM bytes of the glm_chunk scoring kernel from two traffic-probe counter runs,
+    each scaled by what the same counter reads for the calibration copy; writes
+    profiles/logits_hbm_traffic.json and prints a markdown summary."""
+    import csv
+
+    def read(dirname, counter):
+        rows = []
+        for r in csv.DictReader(open(os.path.join(dirname, "run_counter_collection.csv"))):
+            if r["Counter_Name"] == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0))  # KiB -> bytes
+        return rows
+
+    out = {}
+    for counter, dirname in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = read(dirname, counter)
+        lk = [v for n, v in rows if "logits_kernel" in n]
+        cp = [v for n, v in rows if "copyBuffer" in n]
+        calib = max(cp)                      # the 256 MiB copies are the largest copy dispatches
+        factor = COPY_BYTES / calib
+        out[counter] = {"raw_per_launch": lk, "copy_raw": calib, "factor": factor,
+                        "bytes_per_launch": [v * factor for v in lk]}
+    fetch, write = out["FETCH_SIZE"], out["WRITE_SIZE"]
+    nl = min(len(fetch["bytes_per_launch"]), len(write["bytes_per_launch"]))
+    per_launch = [fetch["bytes_per_launch"][i] + write["bytes_per_launch"][i] for i in range(nl)]
+    avg = float(np.mean(per_launch))
+    rec = {"kernel_source_hash": kernel_source_hash(), "bytes_per_launch": avg,
+           "fetch_bytes_per_launch": float(np.mean(fetch["bytes_per_launch"])),
+           "write_bytes_per_launch": float(np.mean(write["bytes_per_launch"])),
+           "fetch_factor": fetch["factor"], "write_factor": write["factor"], "launches": nl}
+    path = os.path.join(ROOT, "profiles", "logits_hbm_traffic.json")
+    try:
+        with open(path) as f:
+            allrec = json.load(f)
+    except (OSError, ValueError):
+        allrec = {}
+    allrec["glm_chunk"] = rec
+    with open(path, "w") as f:
+        json.dump(allrec, f, indent=1)
+    print("| counter | calibration copy read (bytes) | factor | scaled bytes per launch |")
+    print("|---|---|---|---|")
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        v = out[c]
+        print(f"| {c} | {v['copy_raw']:.4g} | {v['factor']:.4f} | "
+              + ", ".join(f"{x / 2**20:.1f} MiB" for x in v["bytes_per_launch"]) + " |")
+    print(f"\nAverage HBM traffic per scoring launch: {avg / 2**20:.1f} MiB "
+          f"(kernel source hash {rec['kernel_source_hash']}).")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,7 +212,13 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true", help="only the launches for a counter run")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two traffic-probe counter runs (no GPU)")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the indexer shards by "
               f"query rows with no exchange, see the design notes)", file=sys.stderr)
@@ -145,6 +227,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    if args.traffic_probe:
+        traffic_probe(dev)
+        return
 
     name = "glm_chunk"
     p = synth.make_config(name)

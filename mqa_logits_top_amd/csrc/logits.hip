@@ -22,15 +22,20 @@
 // (4 (l / 16)) / HPT for key l % 16, so the head sum is an in-lane FMA chain
 // plus, for H = 64, one v_permlane16_swap add.
 //
-// Keys stream through LDS in 8 KiB tiles (64 fp8 keys or 128 MXFP4 keys),
-// double buffered: each thread fetches its 16-byte chunks of tile i + 2 into
-// registers while tile i is scored and writes them to LDS after it (coalesced
-// 128/64-byte key rows).  16-byte chunks are XOR-swizzled inside a key row so
-// that the 16 lanes reading one chunk column hit distinct banks.  (Direct
-// global_load_lds staging is not used: the compiler cannot tell the prefetch
-// buffer from the one being read and drains every DMA before each LDS read.)
+// Keys stream through LDS in 16 KiB stages (128 fp8 keys or 256 MXFP4 keys),
+// double buffered: each thread fetches its 16-byte chunks of stage i + 2 into
+// registers while stage i is scored and writes them to LDS after it.  16-byte
+// chunks are XOR-swizzled inside an LDS row so that the 16 lanes reading one
+// chunk column hit distinct banks.  LDS row p holds key 64 (p / 64) + 4 (p % 16)
+// + (p / 16) % 4, so the 16-key group j of a 64-key batch gives lane n the key
+// 64 b + 4 n + j: after a batch every lane holds 4 consecutive keys of its query
+// row (one 16-byte store, one 16-byte k_scale read, an in-lane 8-key max).
+// (Direct global_load_lds staging is not used: the release fence of a workgroup
+// barrier drains every outstanding LDS DMA.)
 // Output stores go through a buffer resource; lanes with nothing to store get
-// an out-of-range offset, so stores never branch.
+// an out-of-range offset, so stores never branch.  The ReLU is one integer max
+// on the bits, and MFMA results land in VGPRs (built with VGPR-form MFMA), so
+// the epilogue costs 2 VALU ops per (t, h, s).
 //
 // Grid: (row blocks of RPW = 16 rows) x (nsplit key splits).  Workgroup b
 // takes split b % nsplit, row block b / nsplit; when nsplit is a multiple of
