@@ -23,15 +23,16 @@
 // plus, for H = 64, one v_permlane16_swap add.
 //
 // Keys stream through LDS in 16 KiB stages (128 fp8 keys or 256 MXFP4 keys),
-// double buffered: each thread fetches its 16-byte chunks of stage i + 2 into
-// registers while stage i is scored and writes them to LDS after it.  16-byte
-// chunks are XOR-swizzled inside an LDS row so that the 16 lanes reading one
-// chunk column hit distinct banks.  LDS row p holds key 64 (p / 64) + 4 (p % 16)
-// + (p / 16) % 4, so the 16-key group j of a 64-key batch gives lane n the key
-// 64 b + 4 n + j: after a batch every lane holds 4 consecutive keys of its query
-// row (one 16-byte store, one 16-byte k_scale read, an in-lane 8-key max).
-// (Direct global_load_lds staging is not used: the release fence of a workgroup
-// barrier drains every outstanding LDS DMA.)
+// triple buffered and written by the memory system directly
+// (global_load_lds_dwordx4): stage i + 2 is requested while stage i is scored.
+// Each wave waits only for its own requests (s_waitcnt vmcnt with the number of
+// memory operations it has issued since, at least) and then meets the others at
+// a barrier.  16-byte chunks are XOR-swizzled inside an LDS row so that the 16
+// lanes reading one chunk column hit distinct banks.  LDS row p holds key
+// 64 (p / 64) + 4 (p % 16) + (p / 16) % 4, so the 16-key group j of a 64-key
+// batch gives lane n the key 64 b + 4 n + j: after a batch every lane holds 4
+// consecutive keys of its query row (one 16-byte store, one 16-byte k_scale
+// read, an in-lane 8-key max).
 // Output stores go through a buffer resource; lanes with nothing to store get
 // an out-of-range offset, so stores never branch.  The ReLU is one integer max
 // on the bits, and MFMA results land in VGPRs (built with VGPR-form MFMA), so
@@ -58,6 +59,30 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // canonicalisation, a second VALU op per value).
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+__device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)(const lds_u8 *)p; }
+
+// Memory-to-LDS copies: lane l's 16 (4) bytes at g land at LDS byte lds + 16 l (4 l);
+// lds is wave-uniform.  m0 carries the LDS base into the copy.  The compiler reserves
+// m0 and never keeps a value of its own there across statements (it is not
+// preserved across asm either), and nothing else in these kernels uses it.
+__device__ __forceinline__ void lds_copy16(const void *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void lds_copy4(const void *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory");
+}
+// The value is in registers here (a use the compiler cannot move or drop).
+__device__ __forceinline__ void in_regs(v8i x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void in_regs(float x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void in_regs(int x) { asm volatile("" ::"v"(x)); }
+// Wait until at most N of this wave's memory operations are outstanding (they complete
+// in issue order), then meet the workgroup.  The memory clobber keeps LDS reads after it.
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 constexpr int OOB = (int)0x80000000;  // buffer offset past any num_records: the store is dropped
 constexpr int RSRC3 = 0x00020000;     // raw buffer, 32-bit elements
 
@@ -75,11 +100,12 @@ __global__ __launch_bounds__(NW * 64) void logits_kernel(LogitsArgs a) {
   constexpr int TK = KF == 0 ? 128 : 256; // keys per LDS stage (16 KiB either way)
   constexpr int STAGE = TK * KB;
   constexpr int LPT = STAGE / 16 / (NW * 64);  // 16-byte chunks per thread per stage
+  constexpr int ST = TK / 64;                  // stores per stage and wave, at least
   static_assert(LPT * NW * 64 * 16 == STAGE, "stage must split evenly over the workgroup");
   static_assert(RPW <= 64 && TK <= NW * 64 && TK % 64 == 0, "layout limits");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][STAGE];
-  __shared__ __attribute__((aligned(256))) uint32_t sbuf[2][TK];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[3][STAGE];
+  __shared__ __attribute__((aligned(256))) uint32_t sbuf[3][TK];
   __shared__ int32_t wg_range[2];
 
   const int tid = threadIdx.x;
@@ -111,6 +137,28 @@ __global__ __launch_bounds__(NW * 64) void logits_kernel(LogitsArgs a) {
   if (s_lo >= s_hi) return;  // uniform over the workgroup
   const int tile0 = s_lo & ~(TK - 1);
   const int ntiles = (s_hi - tile0 + TK - 1) / TK;
+
+  // ---- key stages: wave w's copy `it` of a stage fills its 1 KiB block it * NW + w;
+  // lane l brings 16-byte slot (it * NW + w) * 64 + l.  LDS row p of a stage holds tile
+  // key 64 (p / 64) + 4 (p % 16) + (p / 16) % 4, its chunks swizzled.
+  auto request = [&](int tile, int buf) {
+    const int ts = tile0 + tile * TK;
+#pragma unroll
+    for (int it = 0; it < LPT; ++it) {
+      const int slot = it * NW * 64 + tid;
+      const int p = KF == 0 ? slot >> 3 : slot >> 2;
+      const int chunk = KF == 0 ? (slot & 7) ^ swz8(p) : (slot & 3) ^ swz4(p);
+      const int key = (p & ~63) | ((p & 15) << 2) | ((p >> 4) & 3);
+      const int gk = min(ts + key, a.L - 1);
+      lds_copy16(a.k + (int64_t)gk * KB + chunk * 16,
+                 __builtin_amdgcn_readfirstlane(lds_addr(&kbuf[buf][(it * NW * 64 + wave * 64) * 16])));
+    }
+    if (wave < TK / 64)
+      lds_copy4(a.k_scale + (int64_t)min(ts + tid, a.L - 1) * 4,
+                __builtin_amdgcn_readfirstlane(lds_addr(&sbuf[buf][wave * 64])));
+  };
+  request(0, 0);
+  if (ntiles > 1) request(1, 1);
 
   // ---- this wave's query rows: A fragments (q) and weights in registers
   const int g = lane >> 4;        // lane group: k block of A/B, row group of C
@@ -156,35 +204,18 @@ __global__ __launch_bounds__(NW * 64) void logits_kernel(LogitsArgs a) {
       __builtin_amdgcn_make_buffer_rsrc(a.out + (int64_t)wrow * ld, 0, (int)(QR * ld * 4), RSRC3);
   const int obase = (t_out - a.row0 - wrow) * (int)ld;   // element offset of this lane's row
 
-  // ---- key stages: thread `tid` owns 16-byte LDS slots tid, tid + NW*64, ...
-  // LDS row p of a stage holds tile key 64 (p / 64) + 4 (p % 16) + (p / 16) % 4, so
-  // group j of batch b (rows 16 (4 b + j) .. + 15) hands lane n16 the key
-  // 64 b + 4 n16 + j: after a batch's four groups each lane holds 4 consecutive keys.
-  v4i kreg[LPT];
-  uint32_t sreg = 0;
-  auto fetch = [&](int tile) {
-    const int ts = tile0 + tile * TK;
+  // Every value the prologue loads is in registers before the loop, so that no wait
+  // for those loads is placed inside it; then stage 0 is complete.
 #pragma unroll
-    for (int it = 0; it < LPT; ++it) {
-      const int slot = it * NW * 64 + tid;
-      const int p = KF == 0 ? slot >> 3 : slot >> 2;
-      const int chunk = KF == 0 ? (slot & 7) ^ swz8(p) : (slot & 3) ^ swz4(p);
-      const int key = (p & ~63) | ((p & 15) << 2) | ((p >> 4) & 3);
-      const int gk = min(ts + key, a.L - 1);
-      kreg[it] = *(const v4i *)(a.k + (int64_t)gk * KB + chunk * 16);
-    }
-    if (tid < TK) sreg = *(const uint32_t *)(a.k_scale + (int64_t)min(ts + tid, a.L - 1) * 4);
-  };
-  auto stash = [&](int buf) {
+  for (int i = 0; i < NT; ++i) {
+    in_regs(qa[i]);
 #pragma unroll
-    for (int it = 0; it < LPT; ++it) *(v4i *)&kbuf[buf][(it * NW * 64 + tid) * 16] = kreg[it];
-    if (tid < TK) sbuf[buf][tid] = sreg;
-  };
-
-  fetch(0);
-  stash(0);
-  if (ntiles > 1) fetch(1);
-  __syncthreads();
+    for (int j = 0; j < 4; ++j) in_regs(wv[i][j]);
+  }
+  in_regs(kst);
+  in_regs(ket);
+  if (ntiles > 1) vm_wait_barrier<LPT>();
+  else vm_wait_barrier<0>();
 
   // 16-byte stores need a 16-byte aligned element offset
   const bool row_al = (((uintptr_t)a.out & 15) == 0) && ((ld & 3) == 0) &&
@@ -193,7 +224,8 @@ __global__ __launch_bounds__(NW * 64) void logits_kernel(LogitsArgs a) {
   const int lim = MODE == STORE_DENSE ? min(v_hi, kst + a.wcols) : v_hi;
 
   for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
+    const int buf = it % 3;
+    if (it + 2 < ntiles) request(it + 2, (it + 2) % 3);  // its buffer was last read in iteration it - 1
     const int ts = tile0 + it * TK;
 #pragma unroll
     for (int b = 0; b < TK / 64; ++b) {
@@ -265,11 +297,18 @@ __global__ __launch_bounds__(NW * 64) void logits_kernel(LogitsArgs a) {
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), orsrc, st ? (obase + col) * 4 : OOB, 0, 0);
       }
     }
+    // stage it + 1 is complete once no more than the memory operations issued after its
+    // request are outstanding: >= ST stores of iteration it - 1, stage it + 2's request
+    // (>= LPT copies), >= ST stores of this iteration
     if (it + 1 < ntiles) {
-      stash(buf ^ 1);
-      if (it + 2 < ntiles) fetch(it + 2);
+      if (it + 2 < ntiles) {
+        if (it > 0) vm_wait_barrier<2 * ST + LPT>();
+        else vm_wait_barrier<ST + LPT>();
+      } else {
+        if (it > 0) vm_wait_barrier<2 * ST>();
+        else vm_wait_barrier<ST>();
+      }
     }
-    __syncthreads();
   }
 }
 

@@ -340,7 +340,6 @@ __global__ __launch_bounds__(NTH) void refine_kernel(RefineArgs a) {
     const int kpe = a.pool == 1 ? 1 : a.pool;   // keys per band entry
     const int nkeys = nb * kpe;
     const int ks = max(a.ks[t], 0), ke = min(a.ke[t], a.L);
-    const int kbytes = a.k_fmt == 0 ? 128 : 64;
     // batch element of this thread: key slot j = tid / 16, 16-thread groups read 8 (fp8) / 4 (fp4) bytes each
     const int jb = tid >> 4, part16 = tid & 15;
     auto key_of = [&](int e) __attribute__((always_inline)) -> int {  // batch element e -> key row or -1
