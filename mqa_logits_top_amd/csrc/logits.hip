@@ -91,7 +91,7 @@ __device__ __forceinline__ int swz8(int n) { return (n & 7) ^ ((n >> 3) & 1); }
 __device__ __forceinline__ int swz4(int n) { return ((n >> 1) ^ (n >> 3)) & 3; }
 
 template <int KF, int H, int MODE, int NW>
-__global__ __launch_bounds__(NW * 64) void logits_kernel(LogitsArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) void logits_kernel(LogitsArgs a) {
   constexpr int QR = 128 / H;            // query rows per wave
   constexpr int HPT = 16 / QR;           // heads of one row in a 16-row A tile
   constexpr int NT = H / HPT;            // A tiles per wave (8)
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(NW * 64) void logits_kernel(LogitsArgs a) {
 
 template <int KF, int H, int MODE>
 hipError_t launch3(const LogitsArgs &a, hipStream_t s) {
-  constexpr int NW = H == 32 ? 4 : 8;
+  constexpr int NW = 4;   // 4 waves: up to 3 workgroups per CU, so a stage barrier never idles the CU
   constexpr int RPW = NW * (128 / H);
   const int nrb = (a.nrows + RPW - 1) / RPW;
   const int64_t grid = (int64_t)nrb * a.nsplit;
