@@ -17,6 +17,7 @@ workload.  Extra fields: the MXFP4 logits stage at T = 2048, L = 102400, H = 64
 and the ragged candidate-source pipeline.
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -128,9 +129,29 @@ def cpu_baseline(p, K, budget_s):
         if time.perf_counter() - t1 > budget_s and rows >= 4:
             break
     el = time.perf_counter() - t1
+    single = None
+    try:  # one BLAS thread, a few rows
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t2 = time.perf_counter()
+            sp = 0
+            for t in order[rows:rows + 4]:
+                v = oracle.row_logits(dq, int(t))
+                oracle.topk_row(v, int(p.ks[t]), K)
+                sp += len(v)
+            single = sp / (time.perf_counter() - t2)
+    except Exception:  # pragma: no cover
+        pass
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": pairs / el, "unit": "pairs/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{rows} of {p.T} rows (random order, seed 0), full windows, logits + top-{K}; "
-                      f"{pairs} pairs in {el:.1f} s (+{setup:.1f} s dequantisation, not counted)"}
+                      f"{pairs} pairs in {el:.1f} s (+{setup:.1f} s dequantisation, not counted)",
+            "single_core_value": single, "cpu_model": model, "host_cpus": os.cpu_count()}
 
 
 COPY_BYTES = 256 << 20   # calibration copy of the traffic probe
@@ -316,6 +337,24 @@ def main():
         log(f"[bench] dsv4_mxfp4 scoring {extra['dsv4_mxfp4_logits_stage']['tflops']:.1f} TFLOP/s, fused "
             f"{np.median(ft):.3f} ms")
         del d3, ws3
+        # the same logits stage with fp8 keys (T=2048, L=102400, H=64)
+        p4 = synth.make_problem(2048, 102400, 64, k_fmt=synth.K_FP8)
+        d4 = idx.Inputs.from_host(p4, device=dev)
+        a4, f4, _ = scoring_launch_ms(p4, d4, 32768, 3, stream)
+        extra["c3_shape_fp8_logits_stage"] = {"avg_launch_ms": a4, "tflops": f4 / (a4 * 1e-3) / 1e12,
+                                              "fp8_peak_frac": f4 / (a4 * 1e-3) / FP8_PEAK}
+        log(f"[bench] T=2048 L=102400 H=64 fp8 scoring {extra['c3_shape_fp8_logits_stage']['tflops']:.1f} TFLOP/s")
+        del d4
+        # peak transient of the fused path at the long-context shape: flat in L
+        flat = {}
+        for L in (65536, 131072, 262144, 487936):
+            s_ = idx.idx_problem(q=1 << 20, q_scale=1 << 20, k=1 << 20, k_scale=1 << 20, k_fmt=0, w=1 << 20,
+                                 ks=1 << 20, ke=1 << 20, T=16384, H=64, D=128, L=L, scale=1.0)
+            n_ = ctypes.c_size_t(0)
+            lib.idx_workspace_size(idx.IDX_OP_LOGITS_TOPK_FUSED, ctypes.byref(s_), 512, 32768, 4096,
+                                   0, 0, 0, ctypes.byref(n_))
+            flat[str(L)] = int(n_.value)
+        extra["long_ctx_peak_transient_bytes_by_L"] = flat
         out["extra"] = extra
 
     if not args.no_cpu:

@@ -118,8 +118,23 @@ constexpr size_t HEAD = 256 + 1024;
 // instead of all sitting a power of two apart.
 int32_t pitch(int32_t cols) { return cols + 64; }
 size_t refine_ws(int32_t Tc, int32_t Kc) { return HEAD + 2 * round_up_sz((size_t)Tc * Kc * 4, 256); }
+// Candidate slabs of the fused path: for key blocks from SLAB_FROM on, the scoring
+// kernel appends each row's values above its running list's smallest entry to one
+// slab of CAPS entries per key split; the top-K merges them instead of the block.
+constexpr int32_t CAPS = 512;
+constexpr int32_t SLAB_FROM = 1;
+int32_t block_slabs(int32_t Bk) {
+  int32_t split, nsplit;
+  plan_splits(Bk, split, nsplit);
+  return nsplit;
+}
+size_t slab_ws(int32_t Tc, int32_t Bk) {
+  const size_t ns = (size_t)block_slabs(Bk);
+  return round_up_sz((size_t)Tc * 4, 256) + round_up_sz((size_t)Tc * ns * 4, 256) +
+         round_up_sz((size_t)Tc * ns * CAPS * 8, 256);
+}
 size_t fused_ws(int32_t Tc, int32_t Bk, int32_t K) {
-  return refine_ws(Tc, cand_cap(K)) + round_up_sz((size_t)Tc * pitch(Bk) * 4, 256);
+  return refine_ws(Tc, cand_cap(K)) + round_up_sz((size_t)Tc * pitch(Bk) * 4, 256) + slab_ws(Tc, Bk);
 }
 size_t cand_ws(int32_t Tc, int32_t pooled_cols, int32_t n_blocks) {
   return refine_ws(Tc, cand_cap(n_blocks)) + round_up_sz((size_t)Tc * pitch(pooled_cols) * 4, 256) +
@@ -315,6 +330,10 @@ idx_status idx_logits_topk_fused(const idx_problem *p, int32_t K, int32_t block_
   RefineWs rw = carve_refine(cv, Tc, Kc);
   const int32_t sld = pitch(Bk);
   float *scratch = cv.take<float>((size_t)Tc * sld);
+  const int32_t nslab_max = block_slabs(Bk);
+  float *thr = cv.take<float>((size_t)Tc);
+  uint32_t *ccnt = cv.take<uint32_t>((size_t)Tc * nslab_max);
+  uint32_t *slab = cv.take<uint32_t>((size_t)Tc * nslab_max * CAPS * 2);
   if ((st = launched(idx::launch_key_bound((const uint8_t *)p->k, (const uint8_t *)p->k_scale, p->k_fmt, p->L,
                                            rw.kpart, rw.overflow, s))))
     return st;
@@ -323,11 +342,30 @@ idx_status idx_logits_topk_fused(const idx_problem *p, int32_t K, int32_t block_
     int32_t kb = 0;
     do {
       const int32_t nk = std::min(Bk, p->L - kb);
+      // blocks after the first also append candidates above each row's running threshold
+      bool slabs = false;
+      int32_t nslab = 0;
       if (nk > 0) {
         idx::LogitsArgs a = logits_args(p, r0, nr, kb, kb + nk, scratch, sld, nk);
-        if ((st = launched(idx::launch_logits(a, p->k_fmt, p->H, idx::STORE_BLOCK, s)))) return st;
+        slabs = kb >= SLAB_FROM * Bk && a.nsplit <= nslab_max && (int64_t)nr * a.nsplit * CAPS * 8 < INT32_MAX;
+        nslab = a.nsplit;
+        if (slabs) {
+          a.thr = thr;
+          a.cand = slab;
+          a.ccnt = ccnt;
+          a.caps = CAPS;
+        }
+        if ((st = launched(idx::launch_logits(a, p->k_fmt, p->H, slabs ? idx::STORE_CAND : idx::STORE_BLOCK, s))))
+          return st;
       }
       idx::TopkArgs b{};
+      if (slabs) {
+        b.cand = slab;
+        b.ccnt = ccnt;
+        b.nslab = nslab;
+        b.caps = CAPS;
+      }
+      b.thr_out = thr;
       b.vals = scratch;
       b.ld = sld;
       b.ncols = nk > 0 ? nk : 0;

@@ -5,7 +5,7 @@
 
 namespace idx {
 
-enum LogitsMode { STORE_DENSE = 0, STORE_BLOCK = 1, STORE_POOL8 = 2 };
+enum LogitsMode { STORE_DENSE = 0, STORE_BLOCK = 1, STORE_POOL8 = 2, STORE_CAND = 3 };
 
 // One launch of the scoring kernel: rows [row0, row0 + nrows) against absolute
 // keys [key_lo, key_hi), split into nsplit workgroup ranges of `split` keys.
@@ -25,6 +25,14 @@ struct LogitsArgs {
   float *out;     // row r of the launch is out + r * ld
   int64_t ld;
   int32_t wcols;  // columns available in an output row (dense W, block nkeys, pool ceil(nkeys/8))
+  // Candidate output (STORE_CAND = STORE_BLOCK plus this): launch row r's in-window values above
+  // thr[r] (NaN: none) also go, as (value bits, key id) word pairs in key order, to slab
+  // r * nsplit + split of caps pairs; ccnt[r * nsplit + split] receives the number of such
+  // values (which may exceed caps: the slab then holds the first caps of them).
+  const float *thr;
+  uint32_t *cand;
+  uint32_t *ccnt;
+  int32_t caps;
 };
 
 hipError_t launch_logits(const LogitsArgs &a, int k_fmt, int H, int mode, hipStream_t s);
@@ -55,6 +63,13 @@ struct TopkArgs {
   int32_t *out_idx;       // row r at out_idx + r * K
   float *out_val;         // row r at out_val + r * K
   int32_t first;          // 1: no running state yet (out_* contents are ignored)
+  // TOPK_BLOCK with the scoring launch's candidate slabs (nullable cand; layout as in
+  // LogitsArgs): a row whose list is full and whose nslab slabs all fit merges the slabs
+  // instead of reading vals
+  const uint32_t *cand;
+  const uint32_t *ccnt;
+  int32_t nslab, caps;
+  float *thr_out;         // nullable: per launch row, the full list's smallest value, else NaN
 };
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
 

@@ -52,6 +52,7 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 // ReLU as one integer max: a float with the sign bit set is a negative int32
@@ -72,6 +73,23 @@ __device__ __forceinline__ void lds_copy16(const void *g, uint32_t lds) {
 __device__ __forceinline__ void lds_copy4(const void *g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory");
 }
+// Inclusive prefix sum over the 16 lanes of a DPP row, and that row's total.
+__device__ __forceinline__ uint32_t row16_scan(uint32_t x, uint32_t &total) {
+  // row total by a butterfly (quad swaps, half-row and row mirrors), all on DPP: no LDS
+  // instruction, so no wait on the key reads in flight
+  uint32_t t = x;
+  t += (uint32_t)__builtin_amdgcn_mov_dpp((int)t, 0xB1, 0xF, 0xF, false);   // quad [1,0,3,2]
+  t += (uint32_t)__builtin_amdgcn_mov_dpp((int)t, 0x4E, 0xF, 0xF, false);   // quad [2,3,0,1]
+  t += (uint32_t)__builtin_amdgcn_mov_dpp((int)t, 0x141, 0xF, 0xF, false);  // row half mirror
+  t += (uint32_t)__builtin_amdgcn_mov_dpp((int)t, 0x140, 0xF, 0xF, false);  // row mirror
+  total = t;
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  return x;
+}
+
 // The value is in registers here (a use the compiler cannot move or drop).
 __device__ __forceinline__ void in_regs(v8i x) { asm volatile("" ::"v"(x)); }
 __device__ __forceinline__ void in_regs(float x) { asm volatile("" ::"v"(x)); }
@@ -91,7 +109,7 @@ __device__ __forceinline__ int swz8(int n) { return (n & 7) ^ ((n >> 3) & 1); }
 __device__ __forceinline__ int swz4(int n) { return ((n >> 1) ^ (n >> 3)) & 3; }
 
 template <int KF, int H, int MODE, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) void logits_kernel(LogitsArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MODE == STORE_CAND && H == 32 ? 2 : 3))) void logits_kernel(LogitsArgs a) {
   constexpr int QR = 128 / H;            // query rows per wave
   constexpr int HPT = 16 / QR;           // heads of one row in a 16-row A tile
   constexpr int NT = H / HPT;            // A tiles per wave (8)
@@ -100,7 +118,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) vo
   constexpr int TK = KF == 0 ? 128 : 256; // keys per LDS stage (16 KiB either way)
   constexpr int STAGE = TK * KB;
   constexpr int LPT = STAGE / 16 / (NW * 64);  // 16-byte chunks per thread per stage
-  constexpr int ST = TK / 64;                  // stores per stage and wave, at least
+  constexpr int ST = TK / 64;  // stores per stage and wave, at least (candidate stores come on top)
   static_assert(LPT * NW * 64 * 16 == STAGE, "stage must split evenly over the workgroup");
   static_assert(RPW <= 64 && TK <= NW * 64 && TK % 64 == 0, "layout limits");
 
@@ -134,7 +152,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) vo
   const int split_hi = min(split_lo + a.split, a.key_hi);
   const int s_lo = max(split_lo, wg_range[0]);
   const int s_hi = min(split_hi, wg_range[1]);
-  if (s_lo >= s_hi) return;  // uniform over the workgroup
+  if (s_lo >= s_hi) {  // uniform over the workgroup: nothing to score, no candidates
+    if (MODE == STORE_CAND && tid < r_end - r_begin)
+      a.ccnt[(r_begin - a.row0 + tid) * a.nsplit + split_i] = 0;
+    return;
+  }
   const int tile0 = s_lo & ~(TK - 1);
   const int ntiles = (s_hi - tile0 + TK - 1) / TK;
 
@@ -196,6 +218,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) vo
   }
   // keys this lane may store: inside its row's window and inside the workgroup range
   const int v_lo = max(kst, s_lo), v_hi = min(ket, s_hi);
+  // candidate slab of this lane's row (STORE_BLOCK with candidate output)
+  constexpr bool cand = MODE == STORE_CAND;
+  float thr_row = __builtin_nanf("");
+  int slab = 0;  // pair offset of the slab (slabs span < 2^31 bytes)
+  __amdgpu_buffer_rsrc_t crsrc;
+  if (cand) {
+    const int rr = min(t_out, r_end - 1) - a.row0;
+    thr_row = a.thr[rr];
+    slab = (rr * a.nsplit + split_i) * a.caps;
+    crsrc = __builtin_amdgcn_make_buffer_rsrc(a.cand, 0, a.nrows * a.nsplit * a.caps * 8, RSRC3);
+  }
+  uint32_t crow = 0;  // candidates of this lane's row so far (uniform over its 16 lanes)
   const bool writer = row_ok && (QR == 4 || (g & 1) == 0);
   // one buffer resource per wave over its QR output rows
   const int wrow = min(wr, a.row0 + a.nrows - 1) - a.row0;
@@ -271,7 +305,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) vo
 #pragma unroll
         for (int j = 0; j < 4; ++j) val[j] *= __int_as_float(sc[j]);
       }
-      if (MODE == STORE_DENSE || MODE == STORE_BLOCK) {
+      if (cand) {
+        // values above the row's running threshold also go to its slab, in key order
+        uint32_t pm = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          pm |= (uint32_t)(writer && s0 + j >= v_lo && s0 + j < v_hi && val[j] > thr_row) << j;
+        // wave-uniform tests: at high thresholds most batches have no candidate at all, and
+        // a store is issued only for a j that some lane of the wave needs (lanes without a
+        // candidate there, or past the slab, are dropped)
+        if (__builtin_amdgcn_ballot_w64(pm != 0u)) {
+          const uint32_t c = __builtin_popcount(pm);
+          uint32_t tot;
+          const uint32_t incl = row16_scan(c, tot);
+          uint32_t pos = crow + incl - c;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool bit = (pm >> j) & 1u;
+            if (__builtin_amdgcn_ballot_w64(bit)) {
+              const v2u e = {__float_as_uint(val[j]), (uint32_t)(s0 + j)};
+              __builtin_amdgcn_raw_buffer_store_b64(e, crsrc,
+                                                    bit && pos < (uint32_t)a.caps ? (slab + (int)pos) * 8 : OOB, 0, 0);
+            }
+            pos += bit;
+          }
+          crow += tot;
+        }
+      }
+      if (MODE != STORE_POOL8) {
         const int col = MODE == STORE_DENSE ? s0 - kst : s0 - a.key_lo;   // column of key s0
         if (writer && row_al && s0 >= v_lo && s0 + 4 <= lim) {
           const v4u d = {__float_as_uint(val[0]), __float_as_uint(val[1]), __float_as_uint(val[2]),
@@ -310,6 +371,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) vo
       }
     }
   }
+  if (cand && writer && n16 == 0) a.ccnt[(int64_t)(t_out - a.row0) * a.nsplit + split_i] = crow;
 }
 
 template <int KF, int H, int MODE>
@@ -328,6 +390,7 @@ hipError_t launch2(const LogitsArgs &a, int mode, hipStream_t s) {
   switch (mode) {
     case STORE_DENSE: return launch3<KF, H, STORE_DENSE>(a, s);
     case STORE_BLOCK: return launch3<KF, H, STORE_BLOCK>(a, s);
+    case STORE_CAND: return launch3<KF, H, STORE_CAND>(a, s);
     default: return launch3<KF, H, STORE_POOL8>(a, s);
   }
 }

@@ -39,15 +39,19 @@ constexpr int KMAX = 2560;          // longest running list
 constexpr int NB = 2048;            // histogram bins
 constexpr int CAPK = 4608;          // segment candidates held in LDS
 constexpr int CAP = 512;            // direct ranking threshold
+constexpr int CAPS_MAX = 512;       // largest candidate slab the merge path gathers
 constexpr int TOP_LOG2 = 26;        // level 0 resolves the 2^26 keys below the largest
 constexpr int TOP_SH = TOP_LOG2 - 11;
 
+constexpr int NI = KMAX + CAPK;     // items: the running list, then a segment's collected keys
+
 struct Smem {
-  int run_id[2][KMAX];
-  float run_val[2][KMAX];
-  uint32_t kkey[CAPK + 64];  // collected segment keys, column order (+ one spare slot per lane)
-  uint16_t kcol[CAPK + 64];  // their columns relative to the segment start
-  uint32_t hist[NB + 64]; // histogram bins (+ one spare slot per lane); the first CAP words
+  // Items in id order: the running list [0, run_n), then the candidates collected
+  // from a segment (or gathered from the scoring kernel's slabs), then one spare
+  // slot per lane for writes that are dropped.  A merge compacts them in place.
+  alignas(16) uint32_t ikey[NI + 64];
+  alignas(16) int32_t iid[NI + 64];
+  alignas(16) uint32_t hist[NB + 64]; // histogram bins (+ one spare slot per lane); the first CAP words
                           // double as the ranking list
   uint32_t red[3][NWV];
   uint32_t wsum[2][NWV];
@@ -137,6 +141,134 @@ __device__ __forceinline__ uint32_t bin_of(uint32_t k, uint32_t chi, int sh) {
   return min((chi - k) >> sh, (uint32_t)(NB - 1));
 }
 
+// The exact K-th key among the items ikey[0, N).  Entries in [clo, chi] number icnt;
+// `need` picks remain inside that interval.  Gives thk and need_eq, the number of
+// entries equal to thk that are taken.
+__device__ __forceinline__ void lds_select(Smem &sm, int N, uint32_t clo, uint32_t chi, int need, uint32_t icnt,
+                                           uint32_t &thk, int &need_eq, int tid, int lane, int wave) {
+  auto item_key = [&](int i) __attribute__((always_inline)) -> uint32_t { return sm.ikey[i]; };
+  for (;;) {
+    if (clo == chi) { thk = clo; need_eq = need; break; }
+    if (icnt <= (uint32_t)CAP) {
+      // rank the interval's entries directly
+      __syncthreads();
+      if (tid == 0) sm.bcast[0] = 0;
+      __syncthreads();
+      for (int i = tid; i < N; i += NTH) {
+        const uint32_t k = item_key(i);
+        if (k >= clo && k <= chi) {
+          const uint32_t slot = atomicAdd(&sm.bcast[0], 1u);
+          if (slot < (uint32_t)CAP) sm.hist[slot] = k;
+        }
+      }
+      __syncthreads();
+      const int n = (int)min(sm.bcast[0], (uint32_t)CAP);
+      // pad the list to whole 16-byte words with zero keys (below any key of the interval
+      // but key 0, whose count is corrected)
+      const int n4 = (n + 3) >> 2;
+      if (tid < 4 * n4 - n) sm.hist[n + tid] = 0u;
+      __syncthreads();
+      if (tid < n) {
+        const uint32_t mine = sm.hist[tid];
+        int gt = 0, ge = mine == 0u ? n - 4 * n4 : 0;
+        const uint4 *h4 = reinterpret_cast<const uint4 *>(sm.hist);
+#pragma unroll 4
+        for (int j = 0; j < n4; ++j) {
+          const uint4 o = h4[j];
+          gt += (o.x > mine) + (o.y > mine) + (o.z > mine) + (o.w > mine);
+          ge += (o.x >= mine) + (o.y >= mine) + (o.z >= mine) + (o.w >= mine);
+        }
+        if (gt < need && need <= ge) { sm.bcast[1] = mine; sm.bcast[2] = (uint32_t)(need - gt); }
+      }
+      __syncthreads();
+      thk = sm.bcast[1];
+      need_eq = (int)sm.bcast[2];
+      break;
+    }
+    const uint32_t span = chi - clo;
+    int sh = 0;
+    while ((span >> sh) >= (uint32_t)NB) ++sh;
+    __syncthreads();
+    for (int i = tid; i < NB; i += NTH) sm.hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < N; i += NTH) {
+      const uint32_t k = item_key(i);
+      if (k >= clo && k <= chi) atomicAdd(&sm.hist[bin_of(k, chi, sh)], 1u);
+    }
+    __syncthreads();
+    {
+      constexpr int BPT = NB / NTH;
+      uint32_t h[BPT], tot = 0;
+#pragma unroll
+      for (int i = 0; i < BPT; ++i) { h[i] = sm.hist[tid * BPT + i]; tot += h[i]; }
+      uint32_t before, d0, t0, t1;
+      block_scan2(sm, tot, 0u, before, d0, t0, t1, lane, wave);
+#pragma unroll
+      for (int i = 0; i < BPT; ++i) {
+        if (before < (uint32_t)need && (uint32_t)need <= before + h[i]) {
+          sm.bcast[0] = tid * BPT + i;
+          sm.bcast[1] = before;
+          sm.bcast[2] = h[i];
+        }
+        before += h[i];
+      }
+    }
+    __syncthreads();
+    const uint32_t bstar = sm.bcast[0];
+    need -= (int)sm.bcast[1];
+    icnt = sm.bcast[2];
+    const uint32_t nhi = chi - (bstar << sh);
+    clo = max(clo, nhi - min(nhi - clo, (1u << sh) - 1u));
+    chi = nhi;
+  }
+}
+
+// New running list: the taken items of ikey / iid [0, N) -- keys above thk, then
+// need_eq keys equal to thk in item order -- compacted in place, in item (= id)
+// order.  Items from run_n on carry ids relative to id0.  Thread tid reads items
+// 16 tid .. 16 tid + 15 into registers; one scan of (equal, above) counts places them.
+// Returns the new list length.
+__device__ __forceinline__ int merge_items(Smem &sm, int N, int run_n, int id0, uint32_t thk, int need_eq, int K,
+                                           int tid, int lane, int wave) {
+  constexpr int IPT = 16;
+  static_assert(IPT * NTH >= NI, "items per thread");
+  const int i0 = tid * IPT;
+  uint32_t kk[IPT];
+  int kid[IPT];
+  if (i0 < N) {  // i0 + IPT <= NI + 64
+    static_for<IPT / 4>([&](auto q) __attribute__((always_inline)) {
+      const uint4 k4 = *(const uint4 *)&sm.ikey[i0 + 4 * q];
+      const int4 d4 = *(const int4 *)&sm.iid[i0 + 4 * q];
+      kk[4 * q] = k4.x; kk[4 * q + 1] = k4.y; kk[4 * q + 2] = k4.z; kk[4 * q + 3] = k4.w;
+      kid[4 * q] = d4.x; kid[4 * q + 1] = d4.y; kid[4 * q + 2] = d4.z; kid[4 * q + 3] = d4.w;
+    });
+  } else {
+    static_for<IPT>([&](auto u) __attribute__((always_inline)) { kk[u] = 0u; kid[u] = -1; });
+  }
+  uint32_t m1 = 0, m2 = 0;  // items above thk / equal to it (taken by rank)
+  static_for<IPT>([&](auto u) __attribute__((always_inline)) {
+    const uint32_t k = i0 + u < N ? kk[u] : 0u;
+    m1 |= (uint32_t)(k != 0u && k > thk) << u;
+    m2 |= (uint32_t)(k != 0u && k == thk && need_eq > 0) << u;
+  });
+  // (the scan's barriers also order every read above before the writes below)
+  uint32_t eo, ao, etot, atot;
+  block_scan2(sm, __builtin_popcount(m2), __builtin_popcount(m1), eo, ao, etot, atot, lane, wave);
+  const uint32_t ne = (uint32_t)need_eq;
+  uint32_t e = eo, pos = ao + min(eo, ne);
+  static_for<IPT>([&](auto u) __attribute__((always_inline)) {
+    const bool tk = ((m1 >> u) & 1u) || (((m2 >> u) & 1u) && e < ne);
+    e += (m2 >> u) & 1u;
+    const int slot = tk && pos < (uint32_t)KMAX ? (int)pos : NI + lane;
+    sm.ikey[slot] = kk[u];
+    sm.iid[slot] = kid[u] + (i0 + u >= run_n ? id0 : 0);
+    pos += tk;
+  });
+  __syncthreads();
+  return min((int)(atot + min(etot, ne)), K);
+}
+
+template <bool SLABS>
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) void topk_kernel(TopkArgs a) {
   __shared__ Smem sm;
   const int r = blockIdx.x;
@@ -161,16 +293,25 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   if (!a.first && c_lo >= c_hi) return;  // nothing new for this row: running state stays as is
 
   // ---- running state
-  int cur = 0;
   int run_n = 0;
   if (!a.first) {
     uint32_t cnt = 0, d0 = 0, d1 = 0;
-    for (int p = tid; p < K; p += NTH) {
-      const int id = oidx[p];
-      sm.run_id[0][p] = id;
-      sm.run_val[0][p] = oval[p];
-      cnt += id >= 0;
-    }
+    constexpr int LPT = KMAX / NTH;  // entries per thread, all loads in flight at once
+    int idv[LPT];
+    float vv[LPT];
+    static_for<LPT>([&](auto u) __attribute__((always_inline)) {
+      const int p = tid + u * NTH;
+      idv[u] = p < K ? oidx[p] : -1;
+      vv[u] = p < K ? oval[p] : 0.f;
+    });
+    static_for<LPT>([&](auto u) __attribute__((always_inline)) {
+      const int p = tid + u * NTH;
+      if (p < K) {
+        sm.iid[p] = idv[u];
+        sm.ikey[p] = idv[u] >= 0 ? fkey(vv[u]) : 0u;
+        cnt += idv[u] >= 0;
+      }
+    });
     block_sum_minmax(sm, cnt, d0, d1, lane, wave);
     run_n = (int)cnt;
   }
@@ -183,10 +324,72 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const int seg = max(min(a.block, SEG) & ~3, 4);
   const int sbase = vec ? (c_lo & ~3) : c_lo;
 
-  for (int S = sbase; S < c_hi; S += seg) {
+  // ---- compact path: a full list whose block candidates above its smallest entry all
+  // fit the scoring kernel's slabs merges those instead of reading the block's columns
+  bool merged = false;
+  uint32_t list_min = 0;  // smallest key of the list after the last merge (once it is full)
+  if (SLABS && !a.first && run_n == K) {
+    uint32_t cs = 0, over = 0, d0 = 0xFFFFFFFFu;
+    if (tid < a.nslab) {
+      cs = a.ccnt[(int64_t)r * a.nslab + tid];
+      over = cs > (uint32_t)a.caps;
+    }
+    uint32_t ex, d1, tot_c, d2;
+    block_scan2(sm, cs, 0u, ex, d1, tot_c, d2, lane, wave);
+    uint32_t osum = over;
+    block_sum_minmax(sm, osum, d0, over, lane, wave);
+    if (osum == 0 && tot_c <= (uint32_t)CAPK && a.caps <= CAPS_MAX) {  // uniform
+      // the slabs hold their candidates in id order and cover consecutive key ranges,
+      // so appending them after the running list keeps the items in id order
+      if (tid < a.nslab) { sm.hist[tid] = ex; sm.hist[64 + tid] = cs; }
+      __syncthreads();
+      // wave w gathers slabs w, w + 8, ..., all of a slab's loads in flight at once
+      for (int sl = wave; sl < a.nslab; sl += NWV) {
+        const uint32_t base = run_n + sm.hist[sl], n = sm.hist[64 + sl];
+        const uint2 *src = (const uint2 *)a.cand + ((int64_t)r * a.nslab + sl) * a.caps;
+        uint2 ev[CAPS_MAX / 64];
+        static_for<CAPS_MAX / 64>([&](auto m) __attribute__((always_inline)) {
+          const uint32_t i = lane + 64 * m;
+          ev[m] = i < n ? src[i] : make_uint2(0u, 0u);
+        });
+        static_for<CAPS_MAX / 64>([&](auto m) __attribute__((always_inline)) {
+          const uint32_t i = lane + 64 * m;
+          if (i < n) {
+            const int id = (int)ev[m].y;
+            uint32_t k = fkey(__uint_as_float(ev[m].x));
+            if (mrow) {
+              const int64_t mj = (int64_t)id - ks;
+              if (!(mj >= 0 && mj < a.mask_w && mrow[mj])) k = 0;
+            }
+            sm.ikey[base + i] = k;
+            sm.iid[base + i] = id;
+          }
+        });
+      }
+      __syncthreads();
+      const int N = run_n + (int)tot_c;
+      // size and key range of the union
+      uint32_t total = 0, umin = 0xFFFFFFFFu, umax = 0;
+      for (int i = tid; i < N; i += NTH) {
+        const uint32_t k = sm.ikey[i];
+        total += k != 0u;
+        umin = min(umin, k != 0u ? k : 0xFFFFFFFFu);
+        umax = max(umax, k);
+      }
+      block_sum_minmax(sm, total, umin, umax, lane, wave);
+      uint32_t thk = 0;
+      int need_eq = 0;
+      if ((int)total > K) lds_select(sm, N, umin, umax, K, total, thk, need_eq, tid, lane, wave);
+      run_n = merge_items(sm, N, N, 0, thk, need_eq, K, tid, lane, wave);
+      list_min = (int)total > K ? thk : umin;
+      merged = true;
+    }
+  }
+
+  for (int S = sbase; S < c_hi && !merged; S += seg) {
     const int s0 = max(S, c_lo), s1 = min(S + seg, c_hi);  // valid columns of this segment
 
-    auto run_key = [&](int p) __attribute__((always_inline)) -> uint32_t { return fkey(sm.run_val[cur][p]); };
+    auto run_key = [&](int p) __attribute__((always_inline)) -> uint32_t { return sm.ikey[p]; };
     uint32_t floor_key = 0;
     if (run_n == K) {  // a full list: segment keys must beat its smallest entry
       uint32_t rlo = 0xFFFFFFFFu, rhi = 0, rn = 0;
@@ -290,8 +493,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         static_for<NCH>([&](auto c) __attribute__((always_inline)) {
           static_for<VPT>([&](auto j) __attribute__((always_inline)) {
             const uint32_t k = key[c][j];
-            const bool in = k >= clo && k <= chi;  // others count into this lane's spare slot
-            atomicAdd(&sm.hist[in ? bin_of(k, chi, sh) : (uint32_t)(NB + lane)], 1u);
+            if (k >= clo && k <= chi) atomicAdd(&sm.hist[bin_of(k, chi, sh)], 1u);
           });
           __builtin_amdgcn_sched_barrier(0);  // one chunk at a time: bounded live ranges
         });
@@ -398,9 +600,10 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       uint32_t pos = posb[c];
       static_for<VPT>([&](auto j) __attribute__((always_inline)) {
         const bool tk = (tb[c] >> j) & 1u;
-        const uint32_t slot = tk && pos < (uint32_t)CAPK ? pos : (uint32_t)(CAPK + lane);
-        sm.kkey[slot] = key[c][j];
-        sm.kcol[slot] = (uint16_t)(c * SPAN + tid * VPT + j);
+        if (tk && pos < (uint32_t)CAPK) {
+          sm.ikey[run_n + pos] = key[c][j];
+          sm.iid[run_n + pos] = c * SPAN + tid * VPT + j;   // made absolute by the merge
+        }
         pos += tk;
       });
       __builtin_amdgcn_sched_barrier(0);
@@ -411,150 +614,38 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 
     // ---- exact K-th key among the LDS-resident entries of [clo, chi]
     const int N = run_n + M;
-    auto item_key = [&](int i) __attribute__((always_inline)) -> uint32_t {
-      return i < run_n ? run_key(i) : sm.kkey[i - run_n];
-    };
     if (!decided) {
-      for (;;) {
-        if (clo == chi) { thk = clo; need_eq = need; break; }
-        if (icnt <= (uint32_t)CAP) {
-          // rank the interval's entries directly
-          __syncthreads();
-          if (tid == 0) sm.bcast[0] = 0;
-          __syncthreads();
-          for (int i = tid; i < N; i += NTH) {
-            const uint32_t k = item_key(i);
-            if (k >= clo && k <= chi) {
-              const uint32_t slot = atomicAdd(&sm.bcast[0], 1u);
-              if (slot < (uint32_t)CAP) sm.hist[slot] = k;
-            }
-          }
-          __syncthreads();
-          const int n = (int)min(sm.bcast[0], (uint32_t)CAP);
-          if (tid < n) {
-            const uint32_t mine = sm.hist[tid];
-            int gt = 0, ge = 0;
-            for (int j = 0; j < n; ++j) {
-              const uint32_t o = sm.hist[j];
-              gt += o > mine;
-              ge += o >= mine;
-            }
-            if (gt < need && need <= ge) { sm.bcast[1] = mine; sm.bcast[2] = (uint32_t)(need - gt); }
-          }
-          __syncthreads();
-          thk = sm.bcast[1];
-          need_eq = (int)sm.bcast[2];
-          break;
-        }
-        const uint32_t span = chi - clo;
-        int sh = 0;
-        while ((span >> sh) >= (uint32_t)NB) ++sh;
-        __syncthreads();
-        for (int i = tid; i < NB; i += NTH) sm.hist[i] = 0;
-        __syncthreads();
-        for (int i = tid; i < N; i += NTH) {
-          const uint32_t k = item_key(i);
-          if (k >= clo && k <= chi) atomicAdd(&sm.hist[bin_of(k, chi, sh)], 1u);
-        }
-        __syncthreads();
-        {
-          constexpr int BPT = NB / NTH;
-          uint32_t h[BPT], tot = 0;
-#pragma unroll
-          for (int i = 0; i < BPT; ++i) { h[i] = sm.hist[tid * BPT + i]; tot += h[i]; }
-          uint32_t before, d0, t0, t1;
-          block_scan2(sm, tot, 0u, before, d0, t0, t1, lane, wave);
-#pragma unroll
-          for (int i = 0; i < BPT; ++i) {
-            if (before < (uint32_t)need && (uint32_t)need <= before + h[i]) {
-              sm.bcast[0] = tid * BPT + i;
-              sm.bcast[1] = before;
-              sm.bcast[2] = h[i];
-            }
-            before += h[i];
-          }
-        }
-        __syncthreads();
-        const uint32_t bstar = sm.bcast[0];
-        need -= (int)sm.bcast[1];
-        icnt = sm.bcast[2];
-        const uint32_t nhi = chi - (bstar << sh);
-        clo = max(clo, nhi - min(nhi - clo, (1u << sh) - 1u));
-        chi = nhi;
-      }
+      lds_select(sm, N, clo, chi, need, icnt, thk, need_eq, tid, lane, wave);
     } else if ((int)total <= K) {
       thk = 0;       // take every entry
       need_eq = 0;
     }
 
     // ---- new running list: taken entries of (running ++ collected), id order
-    {
-      constexpr int IPT = (KMAX + CAPK + NTH - 1) / NTH;
-      const int i0 = tid * IPT;
-      auto taken_kind = [&](uint32_t k) __attribute__((always_inline)) -> int {
-        if (k == 0) return 0;
-        if (k > thk) return 1;
-        return k == thk && need_eq > 0 ? 2 : 0;  // 2: equal, taken by rank
-      };
-      uint32_t neq = 0;
-#pragma unroll 2
-      for (int u = 0; u < IPT; ++u) {
-        const int i = i0 + u;
-        if (i < N) neq += taken_kind(item_key(i)) == 2;
-      }
-      uint32_t eo, d0, d1, d2;
-      block_scan2(sm, neq, 0u, eo, d0, d1, d2, lane, wave);
-      uint32_t ntk = 0;
-      {
-        uint32_t e = eo;
-        for (int u = 0; u < IPT; ++u) {
-          const int i = i0 + u;
-          if (i < N) {
-            const int kind = taken_kind(item_key(i));
-            ntk += kind == 1 || (kind == 2 && e++ < (uint32_t)need_eq);
-          }
-        }
-      }
-      uint32_t po, pt, d3, d4;
-      block_scan2(sm, ntk, 0u, po, d3, pt, d4, lane, wave);
-      const int nxt = cur ^ 1;
-      {
-        uint32_t e = eo, pos = po;
-        for (int u = 0; u < IPT; ++u) {
-          const int i = i0 + u;
-          if (i < N) {
-            const uint32_t k = item_key(i);
-            const int kind = taken_kind(k);
-            if (kind == 1 || (kind == 2 && e++ < (uint32_t)need_eq)) {
-              if (pos < (uint32_t)KMAX) {
-                sm.run_id[nxt][pos] = i < run_n ? sm.run_id[cur][i] : off + S + (int)sm.kcol[i - run_n];
-                sm.run_val[nxt][pos] = kval(k);
-              }
-              ++pos;
-            }
-          }
-        }
-      }
-      run_n = min((int)pt, K);
-      cur = nxt;
-      __syncthreads();
-    }
+    run_n = merge_items(sm, N, run_n, off + S, thk, need_eq, K, tid, lane, wave);
+    list_min = (int)total > K ? thk : umin;
   }
 
-  // ---- write the running list
+  // ---- write the running list (and, for a following scoring launch, its threshold)
   __syncthreads();
   for (int p = tid; p < K; p += NTH) {
     const bool ok = p < run_n;
-    oidx[p] = ok ? sm.run_id[cur][p] : -1;
-    if (oval) oval[p] = ok ? sm.run_val[cur][p] : -__builtin_inff();
+    oidx[p] = ok ? sm.iid[p] : -1;
+    if (oval) oval[p] = ok ? kval(sm.ikey[p]) : -__builtin_inff();
   }
+  // a full list's smallest entry is the K-th key of the last merge (or, when that merge
+  // took its whole union, the union's smallest key)
+  if (a.thr_out && tid == 0) a.thr_out[r] = run_n == K ? kval(list_min) : __builtin_nanf("");
 }
 
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
   if (a.nrows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)a.nrows), dim3(NTH), 0, s, a);
+  if (a.cand)
+    hipLaunchKernelGGL(topk_kernel<true>, dim3((unsigned)a.nrows), dim3(NTH), 0, s, a);
+  else
+    hipLaunchKernelGGL(topk_kernel<false>, dim3((unsigned)a.nrows), dim3(NTH), 0, s, a);
   return hipGetLastError();
 }
 

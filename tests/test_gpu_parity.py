@@ -116,6 +116,29 @@ def test_fused_equals_dense_refined_bitwise(case, block_k, row_chunk):
     topk_ok(fi.cpu().numpy(), fv.cpu().numpy(), o, p.ks, K)
 
 
+def test_fused_slab_overflow_and_fit():
+    """Key blocks after the first merge their scoring-kernel candidate slabs when every
+    slab fits and read the whole block otherwise.  Scores are sums of non-negative terms
+    here, so scaling a block's keys up makes nearly all of them beat the running list:
+    the second block (x64) overflows its 512-entry slabs (1024-key splits) and falls back,
+    the third (x128, 512-key splits) fills its slabs exactly and merges them."""
+    T, L, H, K, Bk = 16, 20000, 32, 64, 8192
+    ks, ke = synth.causal_windows(T, L)
+    p = synth.make_problem(T, L, H, k_fmt=synth.K_FP8, seed=3, ks=ks, ke=ke)
+    p.k_scale[Bk:2 * Bk] *= 64.0
+    p.k_scale[2 * Bk:] *= 128.0
+    dq = oracle.Dequantised(p)
+    o = [oracle.row_logits(dq, t) for t in range(T)]
+    d = dev(p)
+    fi, fv = idx.idx_logits_topk_fused(d, K, block_k=Bk)
+    topk_ok(fi.cpu().numpy(), fv.cpu().numpy(), o, p.ks, K)
+    lg = idx.idx_mqa_logits(d, p.W)
+    ci, cv = idx.idx_topk(lg, d.ks, d.ke, idx.candidate_capacity(K))
+    di, dv = idx.idx_refine_topk(d, ci, cv, K)
+    assert torch.equal(di, fi)
+    assert torch.equal(dv.view(torch.int32), fv.view(torch.int32))
+
+
 def test_fused_masked_consumer(case):
     p, d, o = case
     K = 40
