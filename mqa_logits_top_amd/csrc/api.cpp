@@ -130,7 +130,7 @@ int32_t block_slabs(int32_t Bk) {
 }
 size_t slab_ws(int32_t Tc, int32_t Bk) {
   const size_t ns = (size_t)block_slabs(Bk);
-  return round_up_sz((size_t)Tc * 4, 256) + round_up_sz((size_t)Tc * ns * 4, 256) +
+  return round_up_sz((size_t)Tc * 4, 256) + round_up_sz((size_t)Tc * ns * idx::CAND_PARTS * 4, 256) +
          round_up_sz((size_t)Tc * ns * CAPS * 8, 256);
 }
 size_t fused_ws(int32_t Tc, int32_t Bk, int32_t K) {
@@ -332,7 +332,7 @@ idx_status idx_logits_topk_fused(const idx_problem *p, int32_t K, int32_t block_
   float *scratch = cv.take<float>((size_t)Tc * sld);
   const int32_t nslab_max = block_slabs(Bk);
   float *thr = cv.take<float>((size_t)Tc);
-  uint32_t *ccnt = cv.take<uint32_t>((size_t)Tc * nslab_max);
+  uint32_t *ccnt = cv.take<uint32_t>((size_t)Tc * nslab_max * idx::CAND_PARTS);
   uint32_t *slab = cv.take<uint32_t>((size_t)Tc * nslab_max * CAPS * 2);
   if ((st = launched(idx::launch_key_bound((const uint8_t *)p->k, (const uint8_t *)p->k_scale, p->k_fmt, p->L,
                                            rw.kpart, rw.overflow, s))))

@@ -7,8 +7,18 @@ namespace idx {
 
 enum LogitsMode { STORE_DENSE = 0, STORE_BLOCK = 1, STORE_POOL8 = 2, STORE_CAND = 3 };
 
+// Largest number of parts a scoring work item (row block x key split) is cut into.
+constexpr int CAND_PARTS = 4;
+// Candidate count word: the part's candidates (CAND_OVER if they exceeded its share of
+// the slab) in the low 16 bits, the pair offset of its share in the slab above them.
+constexpr uint32_t CAND_OVER = 0xFFFFu;
+
 // One launch of the scoring kernel: rows [row0, row0 + nrows) against absolute
-// keys [key_lo, key_hi), split into nsplit workgroup ranges of `split` keys.
+// keys [key_lo, key_hi), split into nsplit ranges of `split` keys.  A work item is
+// one row block x one key split; the launch layout (set by launch_logits) gives the
+// first nfull workgroups one whole item each, and cuts each later item into `parts`
+// consecutive tile ranges, one workgroup each, so that the last wave of workgroups
+// is as wide as the machine instead of a remainder.
 struct LogitsArgs {
   const uint8_t *q;
   const float *q_scale;
@@ -25,10 +35,12 @@ struct LogitsArgs {
   float *out;     // row r of the launch is out + r * ld
   int64_t ld;
   int32_t wcols;  // columns available in an output row (dense W, block nkeys, pool ceil(nkeys/8))
+  int32_t nfull, parts;  // launch layout (filled by launch_logits)
   // Candidate output (STORE_CAND = STORE_BLOCK plus this): launch row r's in-window values above
   // thr[r] (NaN: none) also go, as (value bits, key id) word pairs in key order, to slab
-  // r * nsplit + split of caps pairs; ccnt[r * nsplit + split] receives the number of such
-  // values (which may exceed caps: the slab then holds the first caps of them).
+  // r * nsplit + split of caps pairs, part p of an item to its p-th share; the count word
+  // ccnt[(r * nsplit + split) * CAND_PARTS + p] describes that share (parts that do not
+  // exist: count 0).
   const float *thr;
   uint32_t *cand;
   uint32_t *ccnt;

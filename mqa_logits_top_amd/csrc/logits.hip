@@ -44,6 +44,7 @@
 // XCD's L2 only ever holds 1/8 of the keys.
 #include "kernels.h"
 
+#include <algorithm>
 #include <climits>
 
 namespace idx {
@@ -129,8 +130,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MODE ==
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (keeps buffer resources scalar)
-  const int split_i = blockIdx.x % a.nsplit;
-  const int rb = blockIdx.x / a.nsplit;
+  // work item and part: the first nfull workgroups take item blockIdx.x whole, the rest
+  // take part `part` of `nparts` of a later item.  With splits and remainder in whole
+  // multiples of 8, a remainder workgroup stays on the XCD of its item's split
+  // (workgroup b runs on XCD b % 8, and so do the splits s with s % 8 == b % 8).
+  const int b = blockIdx.x;
+  int item = b, part = 0, nparts = 1;
+  if (b >= a.nfull) {
+    const int t = b - a.nfull;
+    nparts = a.parts;
+    if ((a.nsplit & 7) == 0 && (a.nfull & 7) == 0) {
+      const int i = t >> 3;
+      item = a.nfull + (t & 7) + 8 * (i / nparts);
+      part = i % nparts;
+    } else {
+      item = a.nfull + t / nparts;
+      part = t % nparts;
+    }
+  }
+  const int split_i = item % a.nsplit;
+  const int rb = item / a.nsplit;
   const int r_begin = a.row0 + rb * RPW;
   const int r_end = min(r_begin + RPW, a.row0 + a.nrows);
 
@@ -152,13 +171,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MODE ==
   const int split_hi = min(split_lo + a.split, a.key_hi);
   const int s_lo = max(split_lo, wg_range[0]);
   const int s_hi = min(split_hi, wg_range[1]);
-  if (s_lo >= s_hi) {  // uniform over the workgroup: nothing to score, no candidates
+  // this part's tiles of the item: [tile0, tile0 + ntiles * TK)
+  const int itile0 = s_lo & ~(TK - 1);
+  const int intiles = s_lo < s_hi ? (s_hi - itile0 + TK - 1) / TK : 0;
+  const int pt0 = part * intiles / nparts, pt1 = (part + 1) * intiles / nparts;
+  const int tile0 = itile0 + pt0 * TK;
+  const int ntiles = pt1 - pt0;
+  // candidate share of this part in each of its rows' slabs
+  const int share0 = part * a.caps / nparts, share = (part + 1) * a.caps / nparts - share0;
+  if (MODE == STORE_CAND && part == 0) {  // count words of the parts an item does not have
+    for (int i = tid; i < RPW * (CAND_PARTS - nparts); i += NW * 64) {
+      const int rr = r_begin + i / (CAND_PARTS - nparts);
+      if (rr < r_end)
+        a.ccnt[((rr - a.row0) * a.nsplit + split_i) * CAND_PARTS + nparts + i % (CAND_PARTS - nparts)] = 0;
+    }
+  }
+  if (ntiles <= 0) {  // uniform over the workgroup: nothing to score, no candidates
     if (MODE == STORE_CAND && tid < r_end - r_begin)
-      a.ccnt[(r_begin - a.row0 + tid) * a.nsplit + split_i] = 0;
+      a.ccnt[((r_begin - a.row0 + tid) * a.nsplit + split_i) * CAND_PARTS + part] = (uint32_t)share0 << 16;
     return;
   }
-  const int tile0 = s_lo & ~(TK - 1);
-  const int ntiles = (s_hi - tile0 + TK - 1) / TK;
 
   // ---- key stages: wave w's copy `it` of a stage fills its 1 KiB block it * NW + w;
   // lane l brings 16-byte slot (it * NW + w) * 64 + l.  LDS row p of a stage holds tile
@@ -226,7 +258,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MODE ==
   if (cand) {
     const int rr = min(t_out, r_end - 1) - a.row0;
     thr_row = a.thr[rr];
-    slab = (rr * a.nsplit + split_i) * a.caps;
+    slab = (rr * a.nsplit + split_i) * a.caps + share0;
     crsrc = __builtin_amdgcn_make_buffer_rsrc(a.cand, 0, a.nrows * a.nsplit * a.caps * 8, RSRC3);
   }
   uint32_t crow = 0;  // candidates of this lane's row so far (uniform over its 16 lanes)
@@ -325,7 +357,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MODE ==
             if (__builtin_amdgcn_ballot_w64(bit)) {
               const v2u e = {__float_as_uint(val[j]), (uint32_t)(s0 + j)};
               __builtin_amdgcn_raw_buffer_store_b64(e, crsrc,
-                                                    bit && pos < (uint32_t)a.caps ? (slab + (int)pos) * 8 : OOB, 0, 0);
+                                                    bit && pos < (uint32_t)share ? (slab + (int)pos) * 8 : OOB, 0, 0);
             }
             pos += bit;
           }
@@ -371,17 +403,46 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MODE ==
       }
     }
   }
-  if (cand && writer && n16 == 0) a.ccnt[(int64_t)(t_out - a.row0) * a.nsplit + split_i] = crow;
+  if (cand && writer && n16 == 0)
+    a.ccnt[((int64_t)(t_out - a.row0) * a.nsplit + split_i) * CAND_PARTS + part] =
+        ((uint32_t)share0 << 16) | (crow > (uint32_t)share ? CAND_OVER : crow);
+}
+
+// Workgroups of one kernel the current device runs at once (CUs x workgroups per CU),
+// queried once per device and kernel.
+template <class Kern>
+int resident_workgroups(Kern kern, int threads) {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0) != hipSuccess)
+      return 0;
+    cached[dev] = cus * per_cu;
+  }
+  return cached[dev];
 }
 
 template <int KF, int H, int MODE>
-hipError_t launch3(const LogitsArgs &a, hipStream_t s) {
+hipError_t launch3(const LogitsArgs &a0, hipStream_t s) {
   constexpr int NW = 4;   // 4 waves: up to 3 workgroups per CU, so a stage barrier never idles the CU
   constexpr int RPW = NW * (128 / H);
-  const int nrb = (a.nrows + RPW - 1) / RPW;
-  const int64_t grid = (int64_t)nrb * a.nsplit;
-  if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((logits_kernel<KF, H, MODE, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, s, a);
+  auto kern = logits_kernel<KF, H, MODE, NW>;
+  const int nrb = (a0.nrows + RPW - 1) / RPW;
+  const int64_t items = (int64_t)nrb * a0.nsplit;
+  if (items <= 0) return hipSuccess;
+  // Whole items fill as many complete waves of resident workgroups as they can; the
+  // remainder is cut into parts so that the last wave spans the machine as well.
+  LogitsArgs a = a0;
+  const int64_t slots = resident_workgroups(kern, NW * 64);
+  const int64_t full_waves = slots > 0 ? items / slots : items;
+  const int64_t rem = items - full_waves * slots;
+  a.parts = rem > 0 ? (int)std::min<int64_t>(CAND_PARTS, std::max<int64_t>(1, slots / rem)) : 1;
+  a.nfull = (int)(items - rem);
+  const int64_t grid = a.nfull + rem * a.parts;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -329,24 +329,30 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   bool merged = false;
   uint32_t list_min = 0;  // smallest key of the list after the last merge (once it is full)
   if (SLABS && !a.first && run_n == K) {
-    uint32_t cs = 0, over = 0, d0 = 0xFFFFFFFFu;
-    if (tid < a.nslab) {
-      cs = a.ccnt[(int64_t)r * a.nslab + tid];
-      over = cs > (uint32_t)a.caps;
+    // one count word per (slab, part): candidates in the low half, share offset above
+    const int ne = a.nslab * CAND_PARTS;
+    uint32_t cs = 0, over = 0, d0 = 0xFFFFFFFFu, cw = 0;
+    if (tid < ne) {
+      cw = a.ccnt[(int64_t)r * ne + tid];
+      cs = cw & 0xFFFFu;
+      over = cs == CAND_OVER;
+      if (over) cs = 0;
     }
     uint32_t ex, d1, tot_c, d2;
     block_scan2(sm, cs, 0u, ex, d1, tot_c, d2, lane, wave);
     uint32_t osum = over;
     block_sum_minmax(sm, osum, d0, over, lane, wave);
-    if (osum == 0 && tot_c <= (uint32_t)CAPK && a.caps <= CAPS_MAX) {  // uniform
-      // the slabs hold their candidates in id order and cover consecutive key ranges,
+    if (osum == 0 && tot_c <= (uint32_t)CAPK && a.caps <= CAPS_MAX && ne <= NTH) {  // uniform
+      // the shares hold their candidates in id order and cover consecutive key ranges,
       // so appending them after the running list keeps the items in id order
-      if (tid < a.nslab) { sm.hist[tid] = ex; sm.hist[64 + tid] = cs; }
+      if (tid < ne) { sm.hist[tid] = ex; sm.hist[NTH + tid] = cw & 0xFFFF0000u | cs; }
       __syncthreads();
-      // wave w gathers slabs w, w + 8, ..., all of a slab's loads in flight at once
-      for (int sl = wave; sl < a.nslab; sl += NWV) {
-        const uint32_t base = run_n + sm.hist[sl], n = sm.hist[64 + sl];
-        const uint2 *src = (const uint2 *)a.cand + ((int64_t)r * a.nslab + sl) * a.caps;
+      // wave w gathers shares w, w + 8, ..., all of a share's loads in flight at once
+      for (int e = wave; e < ne; e += NWV) {
+        const uint32_t base = run_n + sm.hist[e], n = sm.hist[NTH + e] & 0xFFFFu;
+        if (n == 0) continue;  // uniform over the wave
+        const uint2 *src = (const uint2 *)a.cand + ((int64_t)r * a.nslab + e / CAND_PARTS) * a.caps +
+                           (sm.hist[NTH + e] >> 16);
         uint2 ev[CAPS_MAX / 64];
         static_for<CAPS_MAX / 64>([&](auto m) __attribute__((always_inline)) {
           const uint32_t i = lane + 64 * m;
