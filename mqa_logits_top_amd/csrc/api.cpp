@@ -118,11 +118,16 @@ constexpr size_t HEAD = 256 + 1024;
 // instead of all sitting a power of two apart.
 int32_t pitch(int32_t cols) { return cols + 64; }
 size_t refine_ws(int32_t Tc, int32_t Kc) { return HEAD + 2 * round_up_sz((size_t)Tc * Kc * 4, 256); }
-// Candidate slabs of the fused path: for key blocks from SLAB_FROM on, the scoring
+// Candidate slabs of the fused path: for key blocks from slab_from() on, the scoring
 // kernel appends each row's values above its running list's smallest entry to one
 // slab of CAPS entries per key split; the top-K merges them instead of the block.
 constexpr int32_t CAPS = 512;
-constexpr int32_t SLAB_FROM = 1;
+// The candidate-writing scoring variant keeps 3 workgroups per CU except for fp8 keys
+// with H = 32, whose registers only fit 2: there it costs about a quarter of a block's
+// scoring time, more than the slab merge saves on the second block (whose running list
+// has seen one block only, so about K of its scores beat the threshold), and it starts
+// with the third block.
+int32_t slab_from(const idx_problem *p) { return p->k_fmt == IDX_K_FP8_E4M3 && p->H == 32 ? 2 : 1; }
 int32_t block_slabs(int32_t Bk) {
   int32_t split, nsplit;
   plan_splits(Bk, split, nsplit);
@@ -347,7 +352,7 @@ idx_status idx_logits_topk_fused(const idx_problem *p, int32_t K, int32_t block_
       int32_t nslab = 0;
       if (nk > 0) {
         idx::LogitsArgs a = logits_args(p, r0, nr, kb, kb + nk, scratch, sld, nk);
-        slabs = kb >= SLAB_FROM * Bk && a.nsplit <= nslab_max && (int64_t)nr * a.nsplit * CAPS * 8 < INT32_MAX;
+        slabs = kb >= slab_from(p) * Bk && a.nsplit <= nslab_max && (int64_t)nr * a.nsplit * CAPS * 8 < INT32_MAX;
         nslab = a.nsplit;
         if (slabs) {
           a.thr = thr;

@@ -122,7 +122,7 @@ def test_fused_slab_overflow_and_fit():
     here, so scaling a block's keys up makes nearly all of them beat the running list:
     the second block (x64) overflows its 512-entry slabs (1024-key splits) and falls back,
     the third (x128, 512-key splits) fills its slabs exactly and merges them."""
-    T, L, H, K, Bk = 16, 20000, 32, 64, 8192
+    T, L, H, K, Bk = 16, 20000, 64, 64, 8192   # H = 64: slabs from the second block on
     ks, ke = synth.causal_windows(T, L)
     p = synth.make_problem(T, L, H, k_fmt=synth.K_FP8, seed=3, ks=ks, ke=ke)
     p.k_scale[Bk:2 * Bk] *= 64.0
