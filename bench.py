@@ -61,15 +61,15 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload):
+def load_traffic(workload, keys_per_launch):
     """HBM bytes per scoring launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source."""
+    was taken on the current kernel source and launch size."""
     path = os.path.join(ROOT, "profiles", "logits_hbm_traffic.json")
     try:
         with open(path) as f:
             d = json.load(f)
         e = d.get(workload)
-        if e and e.get("kernel_source_hash") == kernel_source_hash():
+        if e and e.get("kernel_source_hash") == kernel_source_hash() and e.get("keys_per_launch") == keys_per_launch:
             return e["bytes_per_launch"]
     except (OSError, ValueError, KeyError):
         pass
@@ -86,11 +86,23 @@ def time_events(fn, n, stream):
     return [a.elapsed_time(b) for a, b in evs]
 
 
+def launch_keys(L, block_k):
+    """Keys per scoring launch of the fused path: key blocks go in pairs."""
+    return max(block_k, min(2 * block_k, (L + 255) // 256 * 256))
+
+
+def launch_scratch(T, nkeys):
+    """A [T, nkeys] view with the fused path's row pitch (64 floats past the row)."""
+    return torch.empty((T, nkeys + 64), dtype=torch.float32, device="cuda")[:, :nkeys]
+
+
 def scoring_launch_ms(p, d, block_k, reps, stream):
-    """Average duration of the scoring kernel as the fused path launches it (key-block layout):
-    reps x (one launch per key block), back to back on `stream` between one pair of events."""
-    scratch = torch.empty((p.T, block_k), dtype=torch.float32, device="cuda")
-    blocks = [(kb, min(block_k, p.L - kb)) for kb in range(0, p.L, block_k)]
+    """Average duration of the scoring kernel as the fused path launches it (key-block layout,
+    two key blocks per launch): reps x (one launch per key range), back to back on `stream`
+    between one pair of events."""
+    lk = launch_keys(p.L, block_k)
+    scratch = launch_scratch(p.T, lk)
+    blocks = [(kb, min(lk, p.L - kb)) for kb in range(0, p.L, lk)]
 
     def run():
         for _ in range(reps):
@@ -163,17 +175,17 @@ def traffic_probe(dev):
     COPY_BYTES that calibrates what those counters read for a known number of bytes."""
     p = synth.make_config("glm_chunk")
     d = idx.Inputs.from_host(p, device=dev)
-    Bk = p.meta["block_k"]
-    scratch = torch.empty((p.T, Bk), dtype=torch.float32, device=dev)
+    lk = launch_keys(p.L, p.meta["block_k"])
+    scratch = launch_scratch(p.T, lk)
     for rep in range(2):
-        for kb in range(0, p.L, Bk):
-            idx.idx_mqa_logits_block(d, 0, p.T, kb, min(Bk, p.L - kb), out=scratch)
+        for kb in range(0, p.L, lk):
+            idx.idx_mqa_logits_block(d, 0, p.T, kb, min(lk, p.L - kb), out=scratch)
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     for rep in range(2):
         dst.copy_(src)
     torch.cuda.synchronize()
-    log(f"[bench] traffic probe: {2 * ((p.L + Bk - 1) // Bk)} scoring launches, 2 copies of {COPY_BYTES} bytes")
+    log(f"[bench] traffic probe: {2 * ((p.L + lk - 1) // lk)} scoring launches, 2 copies of {COPY_BYTES} bytes")
 
 
 def traffic_summary(fetch_dir, write_dir):
@@ -202,7 +214,9 @@ def traffic_summary(fetch_dir, write_dir):
     nl = min(len(fetch["bytes_per_launch"]), len(write["bytes_per_launch"]))
     per_launch = [fetch["bytes_per_launch"][i] + write["bytes_per_launch"][i] for i in range(nl)]
     avg = float(np.mean(per_launch))
-    rec = {"kernel_source_hash": kernel_source_hash(), "bytes_per_launch": avg,
+    p = synth.make_config("glm_chunk")
+    rec = {"kernel_source_hash": kernel_source_hash(), "keys_per_launch": launch_keys(p.L, p.meta["block_k"]),
+           "bytes_per_launch": avg,
            "fetch_bytes_per_launch": float(np.mean(fetch["bytes_per_launch"])),
            "write_bytes_per_launch": float(np.mean(write["bytes_per_launch"])),
            "fetch_factor": fetch["factor"], "write_factor": write["factor"], "launches": nl}
@@ -298,10 +312,10 @@ def main():
     # roofline of the dominant kernel (scoring), timed per launch on the launch stream
     avg_ms, flops_per_launch, nblk = scoring_launch_ms(p, d, Bk, max(args.steps // 2, 3), stream)
     achieved = flops_per_launch / (avg_ms * 1e-3)
-    traffic = load_traffic(name)
+    traffic = load_traffic(name, launch_keys(p.L, Bk))
     roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": FP8_PEAK / 1e12, "unit": "TFLOP/s",
             "frac": achieved / FP8_PEAK, "traffic": traffic,
-            "kernel": "logits_kernel (fp8 keys, H=32, key-block store)", "avg_launch_ms": avg_ms,
+            "kernel": "logits_kernel (fp8 keys, H=32, key-block store, two 32768-key blocks per launch)", "avg_launch_ms": avg_ms,
             "launches_per_step": nblk, "flop_per_launch": flops_per_launch}
     log(f"[bench] scoring kernel {avg_ms:.4f} ms/launch -> {achieved / 1e12:.1f} TFLOP/s "
         f"({100 * achieved / FP8_PEAK:.1f}% of fp8 peak)")

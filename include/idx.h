@@ -148,8 +148,9 @@ idx_status idx_topk(const float *logits, int64_t ld, int32_t W, const int32_t *k
 /* Fused key-blocked indexer (P1 section 2.3): for each chunk of row_chunk rows
  * and each key block of block_k keys, score the block into workspace and merge
  * its top-(K + 512) into the running candidates of those rows; then settle the
- * boundary exactly (idx_refine_topk).  [T, L] logits are never materialised:
- * workspace is O(row_chunk * (block_k + K)), independent of L.  The result
+ * boundary exactly (idx_refine_topk).  Blocks are scored two per launch.  [T, L]
+ * logits are never materialised: workspace is O(row_chunk * (block_k + K)),
+ * independent of L.  The result
  * equals idx_mqa_logits + idx_topk (K + 512 columns) + idx_refine_topk
  * bitwise.  mask (nullable):
  * [T, ld_mask] bytes, column j <-> key ks[t] + j (the candidate mask of
