@@ -97,7 +97,8 @@ enum {
   IDX_OP_TOPK = 1,             /* idx_topk: no workspace                                */
   IDX_OP_LOGITS_TOPK_FUSED = 2,
   IDX_OP_BLOCK_CANDIDATES = 3, /* idx_block_candidates with logits == NULL (fused)      */
-  IDX_OP_BLOCK_CANDIDATES_DENSE = 4 /* idx_block_candidates from given logits           */
+  IDX_OP_BLOCK_CANDIDATES_DENSE = 4, /* idx_block_candidates from given logits          */
+  IDX_OP_GATHER_ROWS = 5       /* idx_gather_rows of K rows                             */
 };
 
 /* One indexer call's inputs (all device pointers). */
@@ -159,6 +160,18 @@ idx_status idx_logits_topk_fused(const idx_problem *p, int32_t K, int32_t block_
                                  const uint8_t *mask, int64_t ld_mask, int32_t *out_idx,
                                  float *out_val, void *ws, size_t ws_bytes, void *stream);
 
+/* The fused indexer with the index -> KV-slot transform in its final write (P3:
+ * the top-k kernel with the transform fused in; P2 Accuracy/equivalence:
+ * page_indices published next to raw_indices).  As idx_logits_topk_fused, plus
+ * slot_of_key: device int32 [L], the KV-cache slot of every key row (the caller's
+ * token -> slot table over the rows of k); out_slot: [T, K] int32,
+ * out_slot[t, j] = slot_of_key[out_idx[t, j]], -1 where out_idx[t, j] is -1.
+ * Both NULL: exactly idx_logits_topk_fused; one of them NULL: IDX_E_NULL. */
+idx_status idx_logits_topk_fused_paged(const idx_problem *p, int32_t K, int32_t block_k, int32_t row_chunk,
+                                       const uint8_t *mask, int64_t ld_mask, const int32_t *slot_of_key,
+                                       int32_t *out_idx, float *out_val, int32_t *out_slot, void *ws,
+                                       size_t ws_bytes, void *stream);
+
 /* Exact boundary of a top-K from K + R approximate candidates per row.
  * cand_idx / cand_val: device [T, ld_cand], the output of idx_topk with Kc
  * columns (ids ascending, -1 padded; values are the scores the ids were
@@ -204,6 +217,35 @@ idx_status idx_workspace_size(int32_t op, const idx_problem *p, int32_t K, int32
  * cu_q[B] get the empty window ks = ke = 0. */
 idx_status idx_ragged_windows(const int32_t *cu_q, const int32_t *cu_k, int32_t B, int32_t T,
                               int32_t *ks, int32_t *ke, void *stream);
+
+/* Per-row windows over compressed keys (P1 section 1: the ratio-1/2 source layers
+ * score a chunk against the compressed prefix; P1 section 1 also puts the row's
+ * own position into its window).  Request i owns query rows [cu_q[i], cu_q[i+1]),
+ * token rows [cu_k[i], cu_k[i+1]) (its new tokens are the last len_q of them) and
+ * key rows [cu_c[i], cu_c[i+1]), one key per `ratio` consecutive tokens.  New row j
+ * of request i is token prefix + j, prefix = len_k - len_q, and sees the keys of
+ * the complete groups up to it: ks = cu_c[i],
+ * ke = cu_c[i] + min(floor((prefix + j + 1) / ratio), cu_c[i+1] - cu_c[i]).
+ * ratio = 1 with cu_c = cu_k is idx_ragged_windows.  Rows at or past cu_q[B] get
+ * ks = ke = 0.  cu_q, cu_k, cu_c: device int32 [B + 1]; ratio >= 1. */
+idx_status idx_ragged_windows_ratio(const int32_t *cu_q, const int32_t *cu_k, const int32_t *cu_c, int32_t ratio,
+                                    int32_t B, int32_t T, int32_t *ks, int32_t *ke, void *stream);
+
+/* Row subset of a problem (P2 Modifications: publish only each request's tail
+ * rows, which the consumer would slice the masks down to anyway).  Copies row
+ * rows[r] of p (q, q_scale, w, ks, ke) for r < R into ws, and fills *out with a
+ * problem of R rows over p's keys whose row arrays point into ws.  Any entry point
+ * run on *out then scores only those rows; its output row r belongs to p's row
+ * rows[r].  rows[r] = -1 (or outside [0, p->T)) gives a padding row: zero q and the
+ * empty window.  rows: device int32 [R]; ws: idx_workspace_size(IDX_OP_GATHER_ROWS,
+ * p, K = R, ...) bytes, 256-byte aligned, and it must outlive the use of *out. */
+idx_status idx_gather_rows(const idx_problem *p, const int32_t *rows, int32_t R, idx_problem *out, void *ws,
+                           size_t ws_bytes, void *stream);
+
+/* The last n query rows of every request of a varlen batch (the rows a tail-only
+ * output keeps): rows[i * n + m] = cu_q[i+1] - n + m, or -1 where request i has
+ * fewer than n rows.  cu_q: device int32 [B + 1]; rows: device int32 [B * n]. */
+idx_status idx_tail_rows(const int32_t *cu_q, int32_t B, int32_t n, int32_t *rows, void *stream);
 
 /* Static description of a status code. */
 const char *idx_status_str(idx_status s);

@@ -28,12 +28,15 @@ IDX_OP_TOPK = 1
 IDX_OP_LOGITS_TOPK_FUSED = 2
 IDX_OP_BLOCK_CANDIDATES = 3
 IDX_OP_BLOCK_CANDIDATES_DENSE = 4
+IDX_OP_GATHER_ROWS = 5
 
 STATUS = {0: "IDX_OK", 1: "IDX_E_NULL", 2: "IDX_E_SHAPE", 3: "IDX_E_PARAM", 4: "IDX_E_FORMAT",
           5: "IDX_E_WORKSPACE", 6: "IDX_E_UNSUPPORTED", 7: "IDX_E_LAUNCH", 8: "IDX_E_ALIGN"}
 
-EXPORTS = ("idx_mqa_logits", "idx_mqa_logits_block", "idx_topk", "idx_logits_topk_fused", "idx_refine_topk",
-           "idx_block_candidates", "idx_workspace_size", "idx_ragged_windows", "idx_status_str")
+EXPORTS = ("idx_mqa_logits", "idx_mqa_logits_block", "idx_topk", "idx_logits_topk_fused",
+           "idx_logits_topk_fused_paged", "idx_refine_topk",
+           "idx_block_candidates", "idx_workspace_size", "idx_ragged_windows", "idx_ragged_windows_ratio",
+           "idx_gather_rows", "idx_tail_rows", "idx_status_str")
 
 
 class IdxError(RuntimeError):
@@ -66,10 +69,14 @@ def load_library():
     lib.idx_mqa_logits_block.argtypes = [P, i32, i32, i32, i32, VP, i64, VP]
     lib.idx_topk.argtypes = [VP, i64, i32, VP, VP, VP, i64, i32, i32, i32, VP, VP, VP, sz, VP]
     lib.idx_logits_topk_fused.argtypes = [P, i32, i32, i32, VP, i64, VP, VP, VP, sz, VP]
+    lib.idx_logits_topk_fused_paged.argtypes = [P, i32, i32, i32, VP, i64, VP, VP, VP, VP, VP, sz, VP]
     lib.idx_refine_topk.argtypes = [P, VP, VP, i64, i32, i32, i32, VP, VP, VP, sz, VP]
     lib.idx_block_candidates.argtypes = [P, VP, i64, i32, i32, i32, i32, VP, i64, i32, VP, VP, sz, VP]
     lib.idx_workspace_size.argtypes = [i32, P, i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
     lib.idx_ragged_windows.argtypes = [VP, VP, i32, i32, VP, VP, VP]
+    lib.idx_ragged_windows_ratio.argtypes = [VP, VP, VP, i32, i32, i32, VP, VP, VP]
+    lib.idx_gather_rows.argtypes = [P, VP, i32, P, VP, sz, VP]
+    lib.idx_tail_rows.argtypes = [VP, i32, i32, VP, VP]
     lib.idx_status_str.argtypes = [i32]
     lib.idx_status_str.restype = ctypes.c_char_p
     for name in EXPORTS:
@@ -214,6 +221,30 @@ def idx_logits_topk_fused(p: Inputs, K: int, block_k: int = 32768, row_chunk: in
     return out_idx, out_val
 
 
+def idx_logits_topk_fused_paged(p: Inputs, K: int, slot_of_key: torch.Tensor, block_k: int = 32768,
+                                row_chunk: int = 0, mask: Optional[torch.Tensor] = None,
+                                out_idx: Optional[torch.Tensor] = None, out_val: Optional[torch.Tensor] = None,
+                                out_slot: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                                with_values: bool = True, stream=None):
+    """idx_logits_topk_fused plus out_slot = slot_of_key[out_idx] (-1 pads), in the same final write."""
+    dev = p.q.device
+    if out_idx is None:
+        out_idx = torch.empty((p.T, K), dtype=torch.int32, device=dev)
+    if out_val is None and with_values:
+        out_val = torch.empty((p.T, K), dtype=torch.float32, device=dev)
+    if out_slot is None:
+        out_slot = torch.empty((p.T, K), dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = _workspace(idx_workspace_size(IDX_OP_LOGITS_TOPK_FUSED, p, K=K, block_k=block_k, row_chunk=row_chunk),
+                        dev)
+    s = p.struct()
+    _check("idx_logits_topk_fused_paged", load_library().idx_logits_topk_fused_paged(
+        ctypes.byref(s), K, block_k, row_chunk, _ptr(mask), mask.stride(0) if mask is not None else 0,
+        _ptr(slot_of_key), _ptr(out_idx), _ptr(out_val), _ptr(out_slot), _ptr(ws),
+        ws.numel() if ws is not None else 0, _stream(stream)))
+    return out_idx, out_val, out_slot
+
+
 RESERVE = 512   # extra candidates the exact boundary refinement keeps per row
 REFINE_WS = 1280
 
@@ -271,6 +302,49 @@ def idx_ragged_windows(cu_q: torch.Tensor, cu_k: torch.Tensor, T: int, stream=No
     _check("idx_ragged_windows", load_library().idx_ragged_windows(_ptr(cu_q), _ptr(cu_k), B, T, _ptr(ks), _ptr(ke),
                                                                    _stream(stream)))
     return ks, ke
+
+
+def idx_ragged_windows_ratio(cu_q: torch.Tensor, cu_k: torch.Tensor, cu_c: torch.Tensor, ratio: int, T: int,
+                             stream=None):
+    """Windows over keys compressed `ratio` tokens to one (cu_c: key rows per request)."""
+    B = int(cu_q.numel()) - 1
+    ks = torch.empty(T, dtype=torch.int32, device=cu_q.device)
+    ke = torch.empty(T, dtype=torch.int32, device=cu_q.device)
+    _check("idx_ragged_windows_ratio", load_library().idx_ragged_windows_ratio(
+        _ptr(cu_q), _ptr(cu_k), _ptr(cu_c), ratio, B, T, _ptr(ks), _ptr(ke), _stream(stream)))
+    return ks, ke
+
+
+def idx_gather_rows(p: Inputs, rows: torch.Tensor, ws: Optional[torch.Tensor] = None, stream=None) -> Inputs:
+    """The problem restricted to rows[r] (-1: padding row).  The returned Inputs' row tensors
+    are views of ws (the copies idx_gather_rows made); keys are shared with p."""
+    R = int(rows.numel())
+    if ws is None:
+        ws = _workspace(idx_workspace_size(IDX_OP_GATHER_ROWS, p, K=R), p.q.device)
+    s, out = p.struct(), idx_problem()
+    _check("idx_gather_rows", load_library().idx_gather_rows(ctypes.byref(s), _ptr(rows), R, ctypes.byref(out),
+                                                             _ptr(ws), ws.numel() if ws is not None else 0,
+                                                             _stream(stream)))
+    H, D = p.H, int(p.q.shape[2])
+
+    def view(ptr, nbytes, dtype, shape):   # the array the C call placed at ptr inside ws
+        if R == 0:
+            return torch.empty(shape, dtype=dtype, device=p.q.device)
+        o = ptr - ws.data_ptr()
+        return ws[o:o + nbytes].view(dtype).view(shape)
+
+    return Inputs(q=view(out.q, R * H * D, torch.uint8, (R, H, D)),
+                  q_scale=view(out.q_scale, R * H * 4, torch.float32, (R, H)), k=p.k, k_scale=p.k_scale,
+                  w=view(out.w, R * H * 4, torch.float32, (R, H)), ks=view(out.ks, R * 4, torch.int32, (R,)),
+                  ke=view(out.ke, R * 4, torch.int32, (R,)), k_fmt=p.k_fmt, scale=p.scale)
+
+
+def idx_tail_rows(cu_q: torch.Tensor, n: int, stream=None) -> torch.Tensor:
+    """The last n rows of every request ([B * n], -1 where a request is shorter)."""
+    B = int(cu_q.numel()) - 1
+    rows = torch.empty(B * n, dtype=torch.int32, device=cu_q.device)
+    _check("idx_tail_rows", load_library().idx_tail_rows(_ptr(cu_q), B, n, _ptr(rows), _stream(stream)))
+    return rows
 
 
 def idx_status_str(status: int) -> str:

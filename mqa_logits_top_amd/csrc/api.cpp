@@ -148,6 +148,11 @@ int32_t launch_keys(const idx_problem *p, int32_t Bk) {
   const int32_t all = round_up(p->L > 0 ? p->L : 1, KEY_ALIGN);
   return std::max(Bk, std::min(BLOCKS_PER_LAUNCH * Bk, all));
 }
+// Row gather: q [R, H, D] bytes, q_scale and w [R, H] floats, ks and ke [R].
+size_t gather_ws(int32_t R, int32_t H, int32_t D) {
+  return round_up_sz((size_t)R * H * D, 256) + 2 * round_up_sz((size_t)R * H * 4, 256) +
+         2 * round_up_sz((size_t)R * 4, 256);
+}
 size_t fused_ws(int32_t Tc, int32_t Bk, int32_t K) {
   return refine_ws(Tc, cand_cap(K)) + round_up_sz((size_t)Tc * pitch(Bk) * 4, 256) + slab_ws(Tc, Bk);
 }
@@ -229,6 +234,10 @@ idx_status idx_workspace_size(int32_t op, const idx_problem *p, int32_t K, int32
   switch (op) {
     case IDX_OP_MQA_LOGITS:
     case IDX_OP_TOPK: return IDX_OK;
+    case IDX_OP_GATHER_ROWS:
+      if (K < 0 || p->H <= 0 || p->D <= 0) return IDX_E_PARAM;
+      *bytes = gather_ws(K, p->H, p->D);
+      return IDX_OK;
     case IDX_OP_LOGITS_TOPK_FUSED: {
       if (K < 1 || K > MAX_K) return IDX_E_PARAM;
       const int32_t Bk = eff_block(p, block_k);
@@ -324,16 +333,27 @@ idx_status idx_topk(const float *logits, int64_t ld, int32_t W, const int32_t *k
 idx_status idx_logits_topk_fused(const idx_problem *p, int32_t K, int32_t block_k, int32_t row_chunk,
                                  const uint8_t *mask, int64_t ld_mask, int32_t *out_idx, float *out_val, void *ws,
                                  size_t ws_bytes, void *stream) {
+  return idx_logits_topk_fused_paged(p, K, block_k, row_chunk, mask, ld_mask, nullptr, out_idx, out_val, nullptr, ws,
+                                     ws_bytes, stream);
+}
+
+idx_status idx_logits_topk_fused_paged(const idx_problem *p, int32_t K, int32_t block_k, int32_t row_chunk,
+                                       const uint8_t *mask, int64_t ld_mask, const int32_t *slot_of_key,
+                                       int32_t *out_idx, float *out_val, int32_t *out_slot, void *ws,
+                                       size_t ws_bytes, void *stream) {
   idx_status st = check_problem(p, true);
   if (st) return st;
   if (!out_idx) return IDX_E_NULL;
+  if (!slot_of_key != !out_slot) return IDX_E_NULL;   // the transform needs both
   if (K < 1 || K > MAX_K) return IDX_E_PARAM;
   const int32_t Bk = eff_block(p, block_k);
   if ((st = check_block(Bk))) return st;
   if (row_chunk < 0) return IDX_E_PARAM;
   const int32_t Tc = eff_chunk(p, row_chunk);
   if (mask && ld_mask < 0) return IDX_E_SHAPE;
-  if (!aligned(out_idx, 4) || (out_val && !aligned(out_val, 4))) return IDX_E_ALIGN;
+  if (!aligned(out_idx, 4) || (out_val && !aligned(out_val, 4)) || (out_slot && !aligned(out_slot, 4)) ||
+      (slot_of_key && !aligned(slot_of_key, 4)))
+    return IDX_E_ALIGN;
   const int32_t LB = launch_keys(p, Bk);
   const size_t need = fused_ws(Tc, LB, K);
   if (p->T == 0) return IDX_OK;
@@ -405,6 +425,8 @@ idx_status idx_logits_topk_fused(const idx_problem *p, int32_t K, int32_t block_
     } while (kb < p->L);
     idx::RefineArgs r = refine_args(p, rw, r0, nr, Kc, K, 1, out_idx + (int64_t)r0 * K,
                                     out_val ? out_val + (int64_t)r0 * K : nullptr);
+    r.slot_of_key = slot_of_key;
+    r.out_slot = out_slot ? out_slot + (int64_t)r0 * K : nullptr;
     if ((st = launched(idx::launch_refine(r, s)))) return st;
   }
   return IDX_OK;
@@ -532,10 +554,49 @@ idx_status idx_block_candidates(const idx_problem *p, const float *logits, int64
 
 idx_status idx_ragged_windows(const int32_t *cu_q, const int32_t *cu_k, int32_t B, int32_t T, int32_t *ks,
                               int32_t *ke, void *stream) {
-  if (!cu_q || !cu_k || !ks || !ke) return IDX_E_NULL;
+  return idx_ragged_windows_ratio(cu_q, cu_k, cu_k, 1, B, T, ks, ke, stream);
+}
+
+idx_status idx_gather_rows(const idx_problem *p, const int32_t *rows, int32_t R, idx_problem *out, void *ws,
+                           size_t ws_bytes, void *stream) {
+  idx_status st = check_problem(p, true);
+  if (st) return st;
+  if (!out || (R > 0 && (!rows || !ws))) return IDX_E_NULL;
+  if (R < 0) return IDX_E_SHAPE;
+  if (R > 0 && ws_bytes < gather_ws(R, p->H, p->D)) return IDX_E_WORKSPACE;
+  if ((rows && !aligned(rows, 4)) || (ws && !aligned(ws, 256))) return IDX_E_ALIGN;
+  Carve cv{(uint8_t *)ws};
+  uint8_t *oq = cv.take<uint8_t>((size_t)R * p->H * p->D);
+  float *oqs = cv.take<float>((size_t)R * p->H);
+  float *ow = cv.take<float>((size_t)R * p->H);
+  int32_t *oks = cv.take<int32_t>((size_t)R);
+  int32_t *oke = cv.take<int32_t>((size_t)R);
+  *out = *p;
+  out->T = R;
+  out->q = oq;
+  out->q_scale = oqs;
+  out->w = ow;
+  out->ks = oks;
+  out->ke = oke;
+  return launched(idx::launch_gather_rows(rows, R, p->T, p->q, p->q_scale, p->w, p->ks, p->ke, p->H, p->D, oq, oqs, ow,
+                                          oks, oke, (hipStream_t)stream));
+}
+
+idx_status idx_tail_rows(const int32_t *cu_q, int32_t B, int32_t n, int32_t *rows, void *stream) {
+  if (!cu_q || !rows) return IDX_E_NULL;
+  if (B < 0 || n < 0) return IDX_E_SHAPE;
+  if (!aligned(cu_q, 4) || !aligned(rows, 4)) return IDX_E_ALIGN;
+  return launched(idx::launch_tail_rows(cu_q, B, n, rows, (hipStream_t)stream));
+}
+
+idx_status idx_ragged_windows_ratio(const int32_t *cu_q, const int32_t *cu_k, const int32_t *cu_c, int32_t ratio,
+                                    int32_t B, int32_t T, int32_t *ks, int32_t *ke, void *stream) {
+  if (!cu_q || !cu_k || !cu_c || !ks || !ke) return IDX_E_NULL;
   if (B < 0 || T < 0) return IDX_E_SHAPE;
-  if (!aligned(cu_q, 4) || !aligned(cu_k, 4) || !aligned(ks, 4) || !aligned(ke, 4)) return IDX_E_ALIGN;
-  return launched(idx::launch_ragged(cu_q, cu_k, B, T, ks, ke, (hipStream_t)stream));
+  if (ratio < 1) return IDX_E_PARAM;
+  if (!aligned(cu_q, 4) || !aligned(cu_k, 4) || !aligned(cu_c, 4) || !aligned(ks, 4) || !aligned(ke, 4))
+    return IDX_E_ALIGN;
+  return launched(idx::launch_ragged(cu_q, cu_k, cu_c, ratio, B, T, ks, ke, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -9,7 +9,12 @@
 //                 written in place into the caller's [rows, lc] buffer (P2
 //                 Modifications), from the kept block ids.
 //  - ragged:      per-row windows of a varlen batch, built once per batch on the
-//                 device (P3: one ragged plan per batch, no per-request syncs).
+//                 device (P3: one ragged plan per batch, no per-request syncs), over
+//                 plain or compressed keys (P1 section 1: the ratio-1/2 source layers).
+//  - tail rows:   the last n rows of every request, for outputs restricted to each
+//                 request's tail rows (P2 Modifications: tail-only candidate masks).
+//  - gather rows: a row subset of a problem (q, q_scale, w, ks, ke) copied into a
+//                 compact problem, so that any entry point serves just those rows.
 #include "kernels.h"
 
 namespace idx {
@@ -82,8 +87,8 @@ __global__ __launch_bounds__(256) void expand_mask_kernel(const int32_t *blocks,
   }
 }
 
-__global__ __launch_bounds__(256) void ragged_kernel(const int32_t *cu_q, const int32_t *cu_k, int32_t B, int32_t T,
-                                                     int32_t *ks, int32_t *ke) {
+__global__ __launch_bounds__(256) void ragged_kernel(const int32_t *cu_q, const int32_t *cu_k, const int32_t *cu_c,
+                                                     int32_t ratio, int32_t B, int32_t T, int32_t *ks, int32_t *ke) {
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= T) return;
   if (B <= 0 || t >= cu_q[B] || t < cu_q[0]) {
@@ -98,12 +103,66 @@ __global__ __launch_bounds__(256) void ragged_kernel(const int32_t *cu_q, const 
   }
   const int lq = cu_q[lo + 1] - cu_q[lo];
   const int lk = cu_k[lo + 1] - cu_k[lo];
+  const int lc = cu_c[lo + 1] - cu_c[lo];
   const int j = t - cu_q[lo];
-  ks[t] = cu_k[lo];
-  ke[t] = cu_k[lo] + (lk - lq) + j + 1;
+  // new row j is token (lk - lq) + j of its request and sees the keys of the complete
+  // groups of `ratio` tokens up to and including it (floor division)
+  const int seen = (lk - lq) + j + 1;
+  const int groups = seen >= 0 ? seen / ratio : -((-seen + ratio - 1) / ratio);
+  ks[t] = cu_c[lo];
+  ke[t] = cu_c[lo] + min(groups, lc);
+}
+
+// rows[i * n + m] = row cu_q[i+1] - n + m of request i, or -1 where the request is
+// shorter than n.
+__global__ __launch_bounds__(256) void tail_rows_kernel(const int32_t *cu_q, int32_t B, int32_t n, int32_t *rows) {
+  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (x >= (int64_t)B * n) return;
+  const int i = (int)(x / n), m = (int)(x % n);
+  const int t = cu_q[i + 1] - n + m;
+  rows[x] = t >= cu_q[i] ? t : -1;
+}
+
+// One workgroup per output row: its q bytes (H * D), q_scale and w (H floats each),
+// and its window.  Row -1 gets zeros and the empty window [0, 0).
+__global__ __launch_bounds__(256) void gather_rows_kernel(const int32_t *rows, int32_t T, const uint8_t *q,
+                                                          const float *q_scale, const float *w, const int32_t *ks,
+                                                          const int32_t *ke, int32_t H, int32_t D, uint8_t *oq,
+                                                          float *oqs, float *ow, int32_t *oks, int32_t *oke) {
+  const int r = blockIdx.x;
+  const int t = rows[r];
+  const bool ok = t >= 0 && t < T;
+  const int64_t nq = (int64_t)H * D / 16;   // 16-byte words of one q row
+  const uint4 *src = (const uint4 *)(q + (ok ? (int64_t)t * H * D : 0));
+  uint4 *dst = (uint4 *)(oq + (int64_t)r * H * D);
+  for (int64_t i = threadIdx.x; i < nq; i += 256) dst[i] = ok ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+  for (int h = threadIdx.x; h < H; h += 256) {
+    oqs[(int64_t)r * H + h] = ok ? q_scale[(int64_t)t * H + h] : 0.f;
+    ow[(int64_t)r * H + h] = ok ? w[(int64_t)t * H + h] : 0.f;
+  }
+  if (threadIdx.x == 0) {
+    oks[r] = ok ? ks[t] : 0;
+    oke[r] = ok ? ke[t] : 0;
+  }
 }
 
 }  // namespace
+
+hipError_t launch_tail_rows(const int32_t *cu_q, int32_t B, int32_t n, int32_t *rows, hipStream_t s) {
+  const int64_t total = (int64_t)B * n;
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(tail_rows_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, cu_q, B, n, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const int32_t *rows, int32_t R, int32_t T, const uint8_t *q, const float *q_scale,
+                              const float *w, const int32_t *ks, const int32_t *ke, int32_t H, int32_t D, uint8_t *oq,
+                              float *oqs, float *ow, int32_t *oks, int32_t *oke, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)R), dim3(256), 0, s, rows, T, q, q_scale, w, ks, ke, H, D, oq,
+                     oqs, ow, oks, oke);
+  return hipGetLastError();
+}
 
 hipError_t launch_fill_tail(float *logits, int64_t ld, int32_t W, const int32_t *ks, const int32_t *ke, int32_t row0,
                             int32_t nrows, hipStream_t s) {
@@ -134,10 +193,10 @@ hipError_t launch_expand_mask(const int32_t *blocks, int32_t n_blocks, const int
   return hipGetLastError();
 }
 
-hipError_t launch_ragged(const int32_t *cu_q, const int32_t *cu_k, int32_t B, int32_t T, int32_t *ks, int32_t *ke,
-                         hipStream_t s) {
+hipError_t launch_ragged(const int32_t *cu_q, const int32_t *cu_k, const int32_t *cu_c, int32_t ratio, int32_t B,
+                         int32_t T, int32_t *ks, int32_t *ke, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(ragged_kernel, dim3((T + 255) / 256), dim3(256), 0, s, cu_q, cu_k, B, T, ks, ke);
+  hipLaunchKernelGGL(ragged_kernel, dim3((T + 255) / 256), dim3(256), 0, s, cu_q, cu_k, cu_c, ratio, B, T, ks, ke);
   return hipGetLastError();
 }
 

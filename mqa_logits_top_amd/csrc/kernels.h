@@ -107,6 +107,10 @@ struct RefineArgs {
   uint32_t *overflow;       // rows whose band may extend below the list
   int32_t *out_idx;         // row r at out_idx + r * K
   float *out_val;
+  // Index -> KV-slot transform of the written list (pool 1 only; nullable pair):
+  // out_slot[r * K + j] = slot_of_key[out_idx[r * K + j]], -1 where the id is -1.
+  const int32_t *slot_of_key;
+  int32_t *out_slot;
 };
 int key_bound_parts(int L);
 hipError_t launch_key_bound(const uint8_t *k, const uint8_t *k_scale, int k_fmt, int L, float *part,
@@ -122,7 +126,11 @@ hipError_t launch_pool_dense(const float *logits, int64_t ld, int32_t W, const i
 hipError_t launch_expand_mask(const int32_t *blocks, int32_t n_blocks, const int32_t *ks, const int32_t *ke,
                               int32_t row0, int32_t nrows, int32_t pool, int32_t W, uint8_t *mask,
                               int64_t ld_mask, hipStream_t s);
-hipError_t launch_ragged(const int32_t *cu_q, const int32_t *cu_k, int32_t B, int32_t T, int32_t *ks,
-                         int32_t *ke, hipStream_t s);
+hipError_t launch_ragged(const int32_t *cu_q, const int32_t *cu_k, const int32_t *cu_c, int32_t ratio, int32_t B,
+                         int32_t T, int32_t *ks, int32_t *ke, hipStream_t s);
+hipError_t launch_tail_rows(const int32_t *cu_q, int32_t B, int32_t n, int32_t *rows, hipStream_t s);
+hipError_t launch_gather_rows(const int32_t *rows, int32_t R, int32_t T, const uint8_t *q, const float *q_scale,
+                              const float *w, const int32_t *ks, const int32_t *ke, int32_t H, int32_t D, uint8_t *oq,
+                              float *oqs, float *ow, int32_t *oks, int32_t *oke, hipStream_t s);
 
 }  // namespace idx

@@ -179,6 +179,7 @@ __global__ __launch_bounds__(NTH) void refine_kernel(RefineArgs a) {
   const float *cval = a.cand_val + (int64_t)r * a.ld_cand;
   int32_t *oidx = a.out_idx + (int64_t)r * K;
   float *oval = a.out_val ? a.out_val + (int64_t)r * K : nullptr;
+  int32_t *oslot = a.out_slot ? a.out_slot + (int64_t)r * K : nullptr;
 
   // ---- candidates (ids ascending, -1 padded): thread tid holds slots PER tid .. PER tid + PER - 1
   int32_t cid[PER];
@@ -471,6 +472,7 @@ __global__ __launch_bounds__(NTH) void refine_kernel(RefineArgs a) {
       if (pos < (uint32_t)K) {
         oidx[pos] = cid[e];
         if (oval) oval[pos] = cv[e];
+        if (oslot) oslot[pos] = a.slot_of_key[cid[e]];   // the index -> KV-slot transform
       }
       ++pos;
     }
@@ -478,6 +480,7 @@ __global__ __launch_bounds__(NTH) void refine_kernel(RefineArgs a) {
   for (int p = (int)min(total, (uint32_t)K) + tid; p < K; p += NTH) {
     oidx[p] = -1;
     if (oval) oval[p] = -__builtin_inff();
+    if (oslot) oslot[p] = -1;
   }
 }
 

@@ -203,3 +203,35 @@ def topk(dq: Dequantised, rows, K: int, masks=None):
         allowed = None if masks is None else masks[i][:len(v)]
         idx[i], val[i] = topk_row(v, int(dq.ks[t]), K, allowed)
     return idx, val, logits
+
+
+# ------------------------------------------------------------------ windows
+def ragged_windows(cu_q, cu_k, cu_c=None, ratio: int = 1):
+    """Per-row key windows [ks, ke) of a varlen batch, written out row by row.
+
+    P1 section 1: a chunk's rows score against their request's whole compressed
+    prefix (the ratio-1/2 source layers), and each new row sees keys up to its own
+    position; P1 section 2.1: a request can land on a cached prefix.  Request i owns
+    query rows [cu_q[i], cu_q[i+1]) and token rows [cu_k[i], cu_k[i+1]); its len_q new
+    tokens are the last of its len_k tokens, so new row j is token prefix + j with
+    prefix = len_k - len_q, and it has seen prefix + j + 1 tokens.  Keys are one per
+    `ratio` consecutive tokens, in rows [cu_c[i], cu_c[i+1]) (cu_c = cu_k when
+    ratio = 1), and the row sees the keys of its complete groups: floor(seen /
+    ratio), at most the request's key count.  Reading: the pages give the
+    compressed length but not how a partial group is treated; a key summarises a
+    whole group, so a row sees a key only once its group is complete.
+    """
+    cu_c = cu_k if cu_c is None else cu_c
+    T = int(cu_q[-1])
+    ks = np.zeros(T, np.int64)
+    ke = np.zeros(T, np.int64)
+    for i in range(len(cu_q) - 1):
+        len_q = int(cu_q[i + 1]) - int(cu_q[i])
+        len_k = int(cu_k[i + 1]) - int(cu_k[i])
+        len_c = int(cu_c[i + 1]) - int(cu_c[i])
+        for j in range(len_q):
+            seen = len_k - len_q + j + 1
+            t = int(cu_q[i]) + j
+            ks[t] = int(cu_c[i])
+            ke[t] = int(cu_c[i]) + min(seen // ratio, len_c)
+    return ks, ke

@@ -49,6 +49,41 @@ def _fused(lib, p, K=64, block_k=1024, row_chunk=0, ws=1 << 20, ws_bytes=1 << 30
                                      None)
 
 
+def test_paged_transform_needs_both_pointers(lib):
+    p = _problem()
+    f = 1 << 20
+    paged = lambda slot, out_slot: lib.idx_logits_topk_fused_paged(
+        ctypes.byref(p), 64, 1024, 0, None, 0, slot, f, None, out_slot, f, 1 << 30, None)
+    assert paged(f, None) == 1      # NULL: a table without an output
+    assert paged(None, f) == 1      # NULL: an output without a table
+    assert paged(f + 2, f) == 8     # ALIGN: int32 table
+
+
+def test_gather_and_tail_rows_checks(lib):
+    p = _problem()
+    f = 1 << 20
+    out = idx.idx_problem()
+    assert lib.idx_gather_rows(ctypes.byref(p), f, 4, None, f, 1 << 30, None) == 1       # NULL out
+    assert lib.idx_gather_rows(ctypes.byref(p), None, 4, ctypes.byref(out), f, 1 << 30, None) == 1
+    assert lib.idx_gather_rows(ctypes.byref(p), f, -1, ctypes.byref(out), f, 1 << 30, None) == 2
+    assert lib.idx_gather_rows(ctypes.byref(p), f, 4, ctypes.byref(out), f, 16, None) == 5  # WORKSPACE
+    assert lib.idx_gather_rows(ctypes.byref(p), f, 4, ctypes.byref(out), f + 16, 1 << 30, None) == 8
+    assert lib.idx_tail_rows(None, 2, 3, f, None) == 1
+    assert lib.idx_tail_rows(f, -1, 3, f, None) == 2
+    n = ctypes.c_size_t()
+    assert lib.idx_workspace_size(5, ctypes.byref(p), 10, 0, 0, 0, 0, 0, ctypes.byref(n)) == 0
+    assert n.value == _r(10 * 32 * 128) + 2 * _r(10 * 32 * 4) + 2 * _r(10 * 4)
+    # zero rows: nothing to copy, an empty problem over the same keys
+    assert lib.idx_gather_rows(ctypes.byref(p), None, 0, ctypes.byref(out), None, 0, None) == 0
+    assert out.T == 0 and out.L == p.L and out.k == p.k
+
+
+def test_ratio_windows_checks(lib):
+    f = 1 << 20
+    assert lib.idx_ragged_windows_ratio(f, f, None, 2, 2, 4, f, f, None) == 1
+    assert lib.idx_ragged_windows_ratio(f, f, f, 0, 2, 4, f, f, None) == 3     # PARAM: ratio < 1
+
+
 def test_problem_validation(lib):
     assert _fused(lib, _problem(D=64)) == 6            # UNSUPPORTED
     assert _fused(lib, _problem(H=48)) == 6

@@ -139,6 +139,56 @@ def test_fused_slab_overflow_and_fit():
     assert torch.equal(dv.view(torch.int32), fv.view(torch.int32))
 
 
+def test_fused_paged_transform(case):
+    """Index -> KV-slot transform in the final write: out_slot = slot_of_key[out_idx], -1 pads;
+    ids and values equal the untransformed call's."""
+    p, d, o = case
+    K = 64
+    rng = np.random.default_rng(11)
+    table = rng.permutation(4 * p.L)[:p.L].astype(np.int32)     # distinct slots, not the identity
+    fi, fv = idx.idx_logits_topk_fused(d, K, block_k=512)
+    pi, pv, ps = idx.idx_logits_topk_fused_paged(d, K, torch.from_numpy(table).cuda(), block_k=512)
+    assert torch.equal(fi, pi) and torch.equal(fv.view(torch.int32), pv.view(torch.int32))
+    ids = pi.cpu().numpy()
+    want = np.where(ids >= 0, table[np.maximum(ids, 0)], -1)
+    assert np.array_equal(ps.cpu().numpy(), want)
+    topk_ok(ids, pv.cpu().numpy(), o, p.ks, K)
+
+
+def test_gathered_rows_equal_full_rows(case):
+    """A row subset (with a padding row and a repeated row) scored on its own gives the
+    full problem's rows bitwise: the fused top-K, the candidate mask and block ids."""
+    p, d, o = case
+    K, W = 48, max(p.W, 1)
+    rows = np.array([p.T - 1, -1, 0, p.T // 2, p.T - 1], np.int32)
+    sub = idx.idx_gather_rows(d, torch.from_numpy(rows).cuda())
+    assert sub.T == len(rows)
+    fi, fv = idx.idx_logits_topk_fused(d, K, block_k=512)
+    si, sv = idx.idx_logits_topk_fused(sub, K, block_k=512)
+    for r, t in enumerate(rows):
+        if t < 0:
+            assert (si[r] == -1).all()
+        else:
+            assert torch.equal(si[r], fi[t]) and torch.equal(sv[r].view(torch.int32), fv[t].view(torch.int32))
+    if (p.ks % 8 == 0).all():
+        mf, _ = idx.idx_block_candidates(d, W, n_blocks=16, block_k=512)
+        ms, _ = idx.idx_block_candidates(sub, W, n_blocks=16, block_k=512)
+        for r, t in enumerate(rows):
+            assert (ms[r] == 0).all() if t < 0 else torch.equal(ms[r], mf[t])
+
+
+def test_tail_rows_kernel():
+    cu_q = np.array([0, 5, 5, 7, 20], np.int32)
+    n = 3
+    rows = idx.idx_tail_rows(torch.from_numpy(cu_q).cuda(), n).cpu().numpy()
+    want = []
+    for i in range(len(cu_q) - 1):
+        for m in range(n):
+            t = cu_q[i + 1] - n + m
+            want.append(t if t >= cu_q[i] else -1)
+    assert rows.tolist() == want
+
+
 def test_fused_masked_consumer(case):
     p, d, o = case
     K = 40
@@ -245,6 +295,24 @@ def test_ragged_windows_kernel():
     rks, rke = synth.ragged_windows(cu_q, cu_k)
     assert ks.cpu().numpy()[:30].tolist() == rks.tolist() and ke.cpu().numpy()[:30].tolist() == rke.tolist()
     assert (ks.cpu().numpy()[30:] == 0).all() and (ke.cpu().numpy()[30:] == 0).all()
+
+
+@pytest.mark.parametrize("ratio", [1, 2, 4])
+def test_ratio_windows_kernel(ratio):
+    """Windows over compressed keys, against the oracle's row-by-row definition; a request
+    whose token count is not a multiple of the ratio, an empty request, padding rows."""
+    lq = np.array([3, 7, 0, 20, 1], np.int64)
+    lk = np.array([11, 7, 5, 133, 64], np.int64)
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    cu_c = np.concatenate([[0], np.cumsum(lk // ratio)]).astype(np.int32)
+    T = int(cu_q[-1]) + 3
+    g = lambda a: torch.from_numpy(a).cuda()
+    ks, ke = idx.idx_ragged_windows_ratio(g(cu_q), g(cu_k), g(cu_c), ratio, T)
+    oks, oke = oracle.ragged_windows(cu_q, cu_k, cu_c, ratio=ratio)
+    n = int(cu_q[-1])
+    assert ks.cpu().numpy()[:n].tolist() == oks.tolist() and ke.cpu().numpy()[:n].tolist() == oke.tolist()
+    assert (ks.cpu().numpy()[n:] == 0).all() and (ke.cpu().numpy()[n:] == 0).all()
 
 
 def test_edge_shapes():

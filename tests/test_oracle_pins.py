@@ -328,3 +328,43 @@ def test_partial_last_block_pools_valid_keys_only():
     assert P.tolist() == [1.0, 5.0]
     mask, blocks = oracle.block_candidates_row(v, 8, 1, 16)
     assert blocks.tolist() == [1] and np.nonzero(mask)[0].tolist() == [8, 9]
+
+
+def test_ratio_windows_hand_example():
+    """Worked by hand: request 0 has 10 tokens (3 new), request 1 has 7 (2 new); ratio 2
+    gives 5 and 3 keys.  Rows see 8, 9, 10 and 6, 7 tokens: 4, 4, 5 and 3, 3 keys."""
+    ks, ke = oracle.ragged_windows([0, 3, 5], [0, 10, 17], [0, 5, 8], ratio=2)
+    assert ks.tolist() == [0, 0, 0, 5, 5]
+    assert ke.tolist() == [4, 4, 5, 8, 8]
+
+
+def test_ratio_windows_invariants():
+    """Ratio 1 is the plain causal tail; for any ratio the window grows by one key
+    exactly when a group completes, and the last row of a request whose length is a
+    multiple of the ratio sees all of its keys."""
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        B = int(rng.integers(1, 6))
+        lq = rng.integers(1, 40, B)
+        lk = lq + rng.integers(0, 300, B)
+        cu_q = np.concatenate([[0], np.cumsum(lq)])
+        cu_k = np.concatenate([[0], np.cumsum(lk)])
+        ks, ke = oracle.ragged_windows(cu_q, cu_k)
+        for i in range(B):
+            rows = slice(cu_q[i], cu_q[i + 1])
+            assert (ks[rows] == cu_k[i]).all()
+            assert ke[cu_q[i + 1] - 1] == cu_k[i + 1]          # the newest row sees every token
+            assert (np.diff(ke[rows]) == 1).all()
+        for r in (2, 4, 7):
+            lk_r = lk - lk % r                                 # whole groups only
+            lk_r = np.maximum(lk_r, lq)
+            cu_kr = np.concatenate([[0], np.cumsum(lk_r)])
+            cu_c = np.concatenate([[0], np.cumsum(lk_r // r)])
+            ks, ke = oracle.ragged_windows(cu_q, cu_kr, cu_c, ratio=r)
+            for i in range(B):
+                rows = np.arange(cu_q[i], cu_q[i + 1])
+                seen = lk_r[i] - lq[i] + np.arange(lq[i]) + 1
+                steps = np.diff(np.concatenate([[(seen[0] - 1) // r], ke[rows] - cu_c[i]]))
+                assert np.array_equal(steps, (seen % r == 0).astype(int))
+                if lk_r[i] % r == 0:
+                    assert ke[rows[-1]] == cu_c[i + 1]
