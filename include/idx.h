@@ -172,6 +172,19 @@ idx_status idx_logits_topk_fused_paged(const idx_problem *p, int32_t K, int32_t 
                                        int32_t *out_idx, float *out_val, int32_t *out_slot, void *ws,
                                        size_t ws_bytes, void *stream);
 
+/* The fused indexer as a block-aware consumer of the candidate source (P1 section
+ * 2.3: the consumers' masking applies per block; P2 Motivation: a byte mask over
+ * [rows, lc] is the memory problem).  As idx_logits_topk_fused with a mask, but the
+ * mask is given as block ids: row t may select key s only if block
+ * (s - ks[t]) / pool is among blocks[t * ld_blocks + i], i < n_blocks (the
+ * out_blocks layout of idx_block_candidates; ids -1 are ignored).  The result equals
+ * idx_logits_topk_fused with the byte mask those blocks expand to.  No [T, L] byte
+ * mask is read or written.  pool: a power of two, at least 8 for the default
+ * two-block launches of 32768 keys (IDX_E_UNSUPPORTED otherwise). */
+idx_status idx_logits_topk_fused_blocks(const idx_problem *p, int32_t K, int32_t block_k, int32_t row_chunk,
+                                        const int32_t *blocks, int64_t ld_blocks, int32_t n_blocks, int32_t pool,
+                                        int32_t *out_idx, float *out_val, void *ws, size_t ws_bytes, void *stream);
+
 /* Exact boundary of a top-K from K + R approximate candidates per row.
  * cand_idx / cand_val: device [T, ld_cand], the output of idx_topk with Kc
  * columns (ids ascending, -1 padded; values are the scores the ids were

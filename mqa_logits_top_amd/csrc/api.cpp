@@ -337,10 +337,15 @@ idx_status idx_logits_topk_fused(const idx_problem *p, int32_t K, int32_t block_
                                      ws_bytes, stream);
 }
 
-idx_status idx_logits_topk_fused_paged(const idx_problem *p, int32_t K, int32_t block_k, int32_t row_chunk,
-                                       const uint8_t *mask, int64_t ld_mask, const int32_t *slot_of_key,
-                                       int32_t *out_idx, float *out_val, int32_t *out_slot, void *ws,
-                                       size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+// The fused indexer with its optional consumers: a byte mask or a block list restricting
+// the selectable keys, and the index -> KV-slot transform of the final write.
+idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t row_chunk, const uint8_t *mask,
+                      int64_t ld_mask, const int32_t *blocks, int64_t ld_blocks, int32_t n_blocks, int32_t pool,
+                      const int32_t *slot_of_key, int32_t *out_idx, float *out_val, int32_t *out_slot, void *ws,
+                      size_t ws_bytes, void *stream) {
   idx_status st = check_problem(p, true);
   if (st) return st;
   if (!out_idx) return IDX_E_NULL;
@@ -355,6 +360,15 @@ idx_status idx_logits_topk_fused_paged(const idx_problem *p, int32_t K, int32_t 
       (slot_of_key && !aligned(slot_of_key, 4)))
     return IDX_E_ALIGN;
   const int32_t LB = launch_keys(p, Bk);
+  int32_t bsh = 0;
+  if (blocks) {
+    if (mask) return IDX_E_PARAM;                        // one consumer at a time
+    if (n_blocks < 0 || ld_blocks < n_blocks) return IDX_E_SHAPE;
+    if (pool < 1 || (pool & (pool - 1))) return IDX_E_UNSUPPORTED;
+    while ((1 << bsh) < pool) ++bsh;
+    if (((LB - 1) >> bsh) + 2 > idx::BMAP_BITS) return IDX_E_UNSUPPORTED;   // blocks of one launch
+    if (!aligned(blocks, 4)) return IDX_E_ALIGN;
+  }
   const size_t need = fused_ws(Tc, LB, K);
   if (p->T == 0) return IDX_OK;
   if (!ws) return IDX_E_NULL;
@@ -416,6 +430,10 @@ idx_status idx_logits_topk_fused_paged(const idx_problem *p, int32_t K, int32_t 
       b.mask = mask;
       b.ld_mask = ld_mask;
       b.mask_w = ld_mask;
+      b.blocks = blocks;
+      b.ld_blocks = ld_blocks;
+      b.n_blocks = n_blocks;
+      b.bpool_sh = bsh;
       b.K = Kc;
       b.out_idx = rw.cidx;
       b.out_val = rw.cval;
@@ -430,6 +448,25 @@ idx_status idx_logits_topk_fused_paged(const idx_problem *p, int32_t K, int32_t 
     if ((st = launched(idx::launch_refine(r, s)))) return st;
   }
   return IDX_OK;
+}
+}  // namespace
+
+extern "C" {
+
+idx_status idx_logits_topk_fused_paged(const idx_problem *p, int32_t K, int32_t block_k, int32_t row_chunk,
+                                       const uint8_t *mask, int64_t ld_mask, const int32_t *slot_of_key,
+                                       int32_t *out_idx, float *out_val, int32_t *out_slot, void *ws,
+                                       size_t ws_bytes, void *stream) {
+  return fused_impl(p, K, block_k, row_chunk, mask, ld_mask, nullptr, 0, 0, 1, slot_of_key, out_idx, out_val,
+                    out_slot, ws, ws_bytes, stream);
+}
+
+idx_status idx_logits_topk_fused_blocks(const idx_problem *p, int32_t K, int32_t block_k, int32_t row_chunk,
+                                        const int32_t *blocks, int64_t ld_blocks, int32_t n_blocks, int32_t pool,
+                                        int32_t *out_idx, float *out_val, void *ws, size_t ws_bytes, void *stream) {
+  if (!blocks) return IDX_E_NULL;
+  return fused_impl(p, K, block_k, row_chunk, nullptr, 0, blocks, ld_blocks, n_blocks, pool, nullptr, out_idx,
+                    out_val, nullptr, ws, ws_bytes, stream);
 }
 
 idx_status idx_refine_topk(const idx_problem *p, const int32_t *cand_idx, const float *cand_val, int64_t ld_cand,

@@ -71,6 +71,12 @@ struct TopkArgs {
   const uint8_t *mask;    // nullable (key modes only); byte (id - ks) of row t
   int64_t ld_mask;
   int64_t mask_w;         // mask columns per row; bytes at or past it count as 0
+  // Block-list consumer (nullable, TOPK_BLOCK only; exclusive with mask): row t may only
+  // select keys whose block (id - ks) >> bpool_sh is among blocks[t * ld_blocks + i],
+  // i < n_blocks (ids -1 ignored).  The launch's columns span at most BMAP_BITS blocks.
+  const int32_t *blocks;
+  int64_t ld_blocks;
+  int32_t n_blocks, bpool_sh;
   int32_t K;
   int32_t *out_idx;       // row r at out_idx + r * K
   float *out_val;         // row r at out_val + r * K
@@ -83,6 +89,7 @@ struct TopkArgs {
   int32_t nslab, caps;
   float *thr_out;         // nullable: per launch row, the full list's smallest value, else NaN
 };
+constexpr int BMAP_BITS = 9216;   // block bitmap of a top-K launch (65536 keys in 8-key blocks, and slack)
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
 
 // Exact boundary refinement of per-row candidate lists (see refine.hip).

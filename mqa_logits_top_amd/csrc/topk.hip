@@ -51,7 +51,8 @@ struct Smem {
   // slot per lane for writes that are dropped.  A merge compacts them in place.
   alignas(16) uint32_t ikey[NI + 64];
   alignas(16) int32_t iid[NI + 64];
-  alignas(16) uint32_t hist[NB + 64]; // histogram bins (+ one spare slot per lane); the first CAP words
+  alignas(16) uint32_t hist[NB + 64];
+  uint32_t bmap[BMAP_BITS / 32];  // the row's allowed blocks over the launch's columns (block consumer) // histogram bins (+ one spare slot per lane); the first CAP words
                           // double as the ranking list
   uint32_t red[3][NWV];
   uint32_t wsum[2][NWV];
@@ -268,7 +269,7 @@ __device__ __forceinline__ int merge_items(Smem &sm, int N, int run_n, int id0, 
   return min((int)(atot + min(etot, ne)), K);
 }
 
-template <bool SLABS>
+template <bool SLABS, bool BLOCKS>
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) void topk_kernel(TopkArgs a) {
   __shared__ Smem sm;
   const int r = blockIdx.x;
@@ -319,6 +320,25 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const float *vrow = a.vals + (int64_t)r * a.ld;
   const uint8_t *mrow = a.mask ? a.mask + (int64_t)t * a.ld_mask : nullptr;
   const int mshift = (a.mode == TOPK_DENSE || a.mode == TOPK_BLOCK) ? off - ks : 0;  // mask byte = c + mshift
+  // block consumer: bit b of bmap <=> row-relative block b_lo + b is allowed
+  int b_lo = 0;
+  if (BLOCKS) {
+    const int j0 = max(c_lo + mshift, 0);
+    b_lo = j0 >> a.bpool_sh;
+    const int nb = c_hi > c_lo ? ((c_hi - 1 + mshift) >> a.bpool_sh) - b_lo + 1 : 0;
+    for (int i = tid; i < BMAP_BITS / 32; i += NTH) sm.bmap[i] = 0;
+    __syncthreads();
+    const int32_t *brow = a.blocks + (int64_t)t * a.ld_blocks;
+    for (int i = tid; i < a.n_blocks; i += NTH) {
+      const int b = brow[i];
+      if (b >= 0 && b - b_lo >= 0 && b - b_lo < min(nb, BMAP_BITS)) atomicOr(&sm.bmap[(b - b_lo) >> 5], 1u << ((b - b_lo) & 31));
+    }
+    __syncthreads();
+  }
+  auto block_ok = [&](int64_t j) __attribute__((always_inline)) -> bool {  // row-relative position j
+    const int64_t b = (j >> a.bpool_sh) - b_lo;
+    return b >= 0 && b < BMAP_BITS && ((sm.bmap[b >> 5] >> (b & 31)) & 1u);
+  };
   // 16-byte loads when every row and every thread's first column are 16-byte aligned
   const bool vec = ((a.ld & 3) == 0) && (((uintptr_t)a.vals & 15) == 0);
   const int seg = max(min(a.block, SEG) & ~3, 4);
@@ -367,6 +387,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
               const int64_t mj = (int64_t)id - ks;
               if (!(mj >= 0 && mj < a.mask_w && mrow[mj])) k = 0;
             }
+            if (BLOCKS && !block_ok((int64_t)id - ks)) k = 0;
             sm.ikey[base + i] = k;
             sm.iid[base + i] = id;
           }
@@ -435,6 +456,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
             const int64_t mj = (int64_t)col + mshift;
             if (!(inside && mj < a.mask_w && mrow[mj])) k = 0;
           }
+          if (BLOCKS && !(inside && block_ok((int64_t)col + mshift))) k = 0;
           key[c][j] = k > floor_key ? k : 0u;
         });
       });
@@ -648,10 +670,16 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
   if (a.nrows <= 0) return hipSuccess;
-  if (a.cand)
-    hipLaunchKernelGGL(topk_kernel<true>, dim3((unsigned)a.nrows), dim3(NTH), 0, s, a);
-  else
-    hipLaunchKernelGGL(topk_kernel<false>, dim3((unsigned)a.nrows), dim3(NTH), 0, s, a);
+  if (a.blocks) {
+    if (a.cand)
+      hipLaunchKernelGGL((topk_kernel<true, true>), dim3((unsigned)a.nrows), dim3(NTH), 0, s, a);
+    else
+      hipLaunchKernelGGL((topk_kernel<false, true>), dim3((unsigned)a.nrows), dim3(NTH), 0, s, a);
+  } else if (a.cand) {
+    hipLaunchKernelGGL((topk_kernel<true, false>), dim3((unsigned)a.nrows), dim3(NTH), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((topk_kernel<false, false>), dim3((unsigned)a.nrows), dim3(NTH), 0, s, a);
+  }
   return hipGetLastError();
 }
 

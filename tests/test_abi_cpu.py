@@ -84,6 +84,18 @@ def test_ratio_windows_checks(lib):
     assert lib.idx_ragged_windows_ratio(f, f, f, 0, 2, 4, f, f, None) == 3     # PARAM: ratio < 1
 
 
+def test_block_consumer_checks(lib):
+    p = _problem()
+    f = 1 << 20
+    call = lambda blocks, ld, nb, pool, bk=1024: lib.idx_logits_topk_fused_blocks(
+        ctypes.byref(p), 64, bk, 0, blocks, ld, nb, pool, f, None, f, 1 << 30, None)
+    assert call(None, 16, 16, 8) == 1          # NULL
+    assert call(f, 8, 16, 8) == 2              # SHAPE: ld_blocks < n_blocks
+    assert call(f, 16, 16, 6) == 6             # UNSUPPORTED: pool not a power of two
+    assert call(f, 16, 16, 1, 32768) == 6      # UNSUPPORTED: 65536 keys per launch in 1-key blocks
+    assert call(f + 2, 16, 16, 8) == 8         # ALIGN
+
+
 def test_problem_validation(lib):
     assert _fused(lib, _problem(D=64)) == 6            # UNSUPPORTED
     assert _fused(lib, _problem(H=48)) == 6

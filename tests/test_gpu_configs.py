@@ -161,3 +161,6 @@ def test_ragged_candidates_and_masked_consumer():
     o2 = [oracle.row_logits(dq2, t) for t in rows]
     allowed = [mk[i][:len(o2[i])].astype(bool) for i in range(len(rows))]
     topk_ok(gi.cpu().numpy()[rows], gv.cpu().numpy()[rows], o2, p.ks[rows], K, allowed=allowed)
+    # the same consumer reading the block ids instead of the byte mask: identical output
+    bi, bv = idx.idx_logits_topk_fused_blocks(d2, K, blocks, pool=pool, block_k=c["block_k"], row_chunk=4096)
+    assert torch.equal(bi, gi) and torch.equal(bv.view(torch.int32), gv.view(torch.int32))

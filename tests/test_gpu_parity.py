@@ -177,6 +177,34 @@ def test_gathered_rows_equal_full_rows(case):
             assert (ms[r] == 0).all() if t < 0 else torch.equal(ms[r], mf[t])
 
 
+@pytest.mark.parametrize("pool", [8, 16])
+def test_fused_block_consumer(case, pool):
+    """Selection restricted to a block list equals selection under the byte mask the
+    blocks expand to (bitwise), and the oracle's masked top-K; lists with -1 entries,
+    repeats and blocks past the window."""
+    p, d, o = case
+    K = 40
+    rng = np.random.default_rng(pool)
+    nb = 24
+    blocks = np.full((p.T, nb), -1, np.int32)
+    W = max(p.W, 1)
+    mask = np.zeros((p.T, W), np.uint8)
+    for t in range(p.T):
+        win = int(p.ke[t] - p.ks[t])
+        nblk = max((win + pool - 1) // pool, 1)
+        pick = rng.integers(0, nblk + 3, nb - 4)          # some past the window, some repeated
+        blocks[t, :nb - 4] = pick
+        for b in pick:
+            lo = b * pool
+            mask[t, lo:min(lo + pool, win)] = 1
+    bt = torch.from_numpy(blocks).cuda()
+    bi, bv = idx.idx_logits_topk_fused_blocks(d, K, bt, pool=pool, block_k=512)
+    mi, mv = idx.idx_logits_topk_fused(d, K, block_k=512, mask=torch.from_numpy(mask).cuda())
+    assert torch.equal(bi, mi) and torch.equal(bv.view(torch.int32), mv.view(torch.int32))
+    allowed = [mask[t, :len(o[t])].astype(bool) for t in range(p.T)]
+    topk_ok(bi.cpu().numpy(), bv.cpu().numpy(), o, p.ks, K, allowed=allowed)
+
+
 def test_tail_rows_kernel():
     cu_q = np.array([0, 5, 5, 7, 20], np.int32)
     n = 3
