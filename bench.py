@@ -49,15 +49,21 @@ def block_pairs(p, kb, nk):
 
 
 def kernel_source_hash():
-    """Hash of the scoring kernel's code (comments and blank lines excluded), to tell whether
-    committed counter figures were taken on the kernel as it stands."""
+    """Hash of the scoring kernel's code (logits.hip and the LogitsArgs struct; comments and
+    blank lines excluded), to tell whether committed counter figures were taken on the kernel
+    as it stands."""
     h = hashlib.sha256()
-    for f in ("logits.hip", "kernels.h"):
-        with open(os.path.join(ROOT, "mqa_logits_top_amd", "csrc", f)) as fh:
-            for line in fh:
-                code = line.split("//", 1)[0].rstrip()
-                if code:
-                    h.update(code.encode() + b"\n")
+    csrc = os.path.join(ROOT, "mqa_logits_top_amd", "csrc")
+    with open(os.path.join(csrc, "logits.hip")) as fh:
+        text = fh.read()
+    with open(os.path.join(csrc, "kernels.h")) as fh:
+        hdr = fh.read()
+    a = hdr.index("struct LogitsArgs {")
+    text += hdr[a:hdr.index("};", a)]
+    for line in text.splitlines():
+        code = line.split("//", 1)[0].rstrip()
+        if code:
+            h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
@@ -115,6 +121,61 @@ def scoring_launch_ms(p, d, block_k, reps, stream):
     del scratch
     avg_ms = float(np.median(t)) / (reps * len(blocks))
     return avg_ms, flops / len(blocks), len(blocks)
+
+
+def dense_rowchunk_overlap(p, d, K, rows, stream):
+    """The dense row-chunked comparator (logits of `rows` rows, then top-(K + 512) and the exact
+    boundary) run serially on one stream and pipelined on two: chunk n + 1's logits on the main
+    stream while chunk n's selection runs on a side stream (both default priority), logits
+    double buffered and event-gated.  Returns (serial ms, pipelined ms); outputs must agree."""
+    W = p.W
+    Kc = idx.candidate_capacity(K)
+    side = torch.cuda.Stream()
+    bufs = [launch_scratch(rows, W) for _ in range(2)]
+    chunks = [(r0, min(rows, p.T - r0)) for r0 in range(0, p.T, rows)]
+    sub = lambda r0, n: idx.Inputs(q=d.q[r0:r0 + n], q_scale=d.q_scale[r0:r0 + n], k=d.k, k_scale=d.k_scale,
+                                   w=d.w[r0:r0 + n], ks=d.ks[r0:r0 + n], ke=d.ke[r0:r0 + n], k_fmt=d.k_fmt)
+    outs = {m: (torch.empty((p.T, K), dtype=torch.int32, device="cuda"),
+                torch.empty((p.T, K), dtype=torch.float32, device="cuda")) for m in ("serial", "piped")}
+    cand = [(torch.empty((rows, Kc), dtype=torch.int32, device="cuda"),
+             torch.empty((rows, Kc), dtype=torch.float32, device="cuda")) for _ in range(2)]
+    rws = [torch.empty(idx.REFINE_WS, dtype=torch.uint8, device="cuda") for _ in range(2)]
+
+    def select(i, r0, n, sp, st):
+        lg = bufs[i % 2][:n]
+        ci, cv = cand[i % 2]
+        idx.idx_topk(lg, sp.ks, sp.ke, Kc, W=W, out_idx=ci[:n], out_val=cv[:n], stream=st)
+        oi, ov = outs["piped" if st is side else "serial"]
+        idx.idx_refine_topk(sp, ci[:n], cv[:n], K, out_idx=oi[r0:r0 + n], out_val=ov[r0:r0 + n], ws=rws[i % 2],
+                            stream=st)
+
+    def serial():
+        for i, (r0, n) in enumerate(chunks):
+            sp = sub(r0, n)
+            idx.idx_mqa_logits(sp, W, out=bufs[i % 2][:n], stream=stream)
+            select(i, r0, n, sp, stream)
+
+    def piped():
+        done = [None, None]                   # selection of the chunk that last used each buffer
+        for i, (r0, n) in enumerate(chunks):
+            sp = sub(r0, n)
+            if done[i % 2] is not None:
+                stream.wait_event(done[i % 2])
+            idx.idx_mqa_logits(sp, W, out=bufs[i % 2][:n], stream=stream)
+            ready = torch.cuda.Event()
+            ready.record(stream)
+            side.wait_event(ready)
+            select(i, r0, n, sp, side)
+            done[i % 2] = torch.cuda.Event()
+            done[i % 2].record(side)
+        stream.wait_event(done[(len(chunks) - 1) % 2])
+
+    serial(); piped()
+    torch.cuda.synchronize()
+    ts = float(np.median(time_events(serial, 3, stream)))
+    tp = float(np.median(time_events(piped, 3, stream)))
+    assert torch.equal(outs["serial"][0], outs["piped"][0])
+    return ts, tp
 
 
 def cpu_baseline(p, K, budget_s):
@@ -369,6 +430,57 @@ def main():
                                    0, 0, 0, ctypes.byref(n_))
             flat[str(L)] = int(n_.value)
         extra["long_ctx_peak_transient_bytes_by_L"] = flat
+        # two-stream overlap of the dense row-chunked comparator (glm_chunk shapes, 512-row chunks)
+        ts, tp = dense_rowchunk_overlap(p, d, K, 512, stream)
+        extra["dense_rowchunk_overlap"] = {"rows_per_chunk": 512, "serial_ms": ts, "two_stream_ms": tp,
+                                           "gain": ts / tp - 1.0}
+        log(f"[bench] dense row-chunked comparator: serial {ts:.3f} ms, two streams {tp:.3f} ms")
+        # index -> KV-slot transform in the final write (glm_chunk)
+        table = torch.randperm(2 * p.L, device=dev)[:p.L].to(torch.int32)
+        wsg = torch.empty(idx.idx_workspace_size(idx.IDX_OP_LOGITS_TOPK_FUSED, d, K=K, block_k=Bk), dtype=torch.uint8,
+                          device=dev)
+        tf = time_events(lambda: idx.idx_logits_topk_fused(d, K, block_k=Bk, out_idx=out_idx, out_val=out_val,
+                                                           ws=wsg, stream=stream), 5, stream)
+        tpg = time_events(lambda: idx.idx_logits_topk_fused_paged(d, K, table, block_k=Bk, out_idx=out_idx,
+                                                                  out_val=out_val, ws=wsg, stream=stream), 5, stream)
+        del wsg
+        extra["paged_transform"] = {"fused_ms": float(np.median(tf)), "fused_paged_ms": float(np.median(tpg))}
+        # candidate source and its consumers on the ragged batch: every row vs each request's tail rows,
+        # byte-mask consumer vs block-list consumer
+        p5 = synth.make_config("ragged_cand")
+        c5 = p5.meta
+        d5 = idx.Inputs.from_host(p5, device=dev)
+        W5, nb5, pool5, K5, bk5 = p5.W, c5["n_blocks"], c5["pool"], c5["K"], c5["block_k"]
+        blocks5 = torch.empty((p5.T, nb5), dtype=torch.int32, device=dev)
+        ws5 = torch.empty(idx.idx_workspace_size(idx.IDX_OP_BLOCK_CANDIDATES, d5, block_k=bk5, row_chunk=4096,
+                                                 pool=pool5, n_blocks=nb5), dtype=torch.uint8, device=dev)
+        mask5 = torch.empty((p5.T, W5), dtype=torch.uint8, device=dev)
+        cand_all = time_events(lambda: idx.idx_block_candidates(d5, W5, pool=pool5, n_blocks=nb5, block_k=bk5,
+                                                                row_chunk=4096, mask=mask5, out_blocks=blocks5,
+                                                                ws=ws5, stream=stream), 3, stream)
+        tail = idx.idx_tail_rows(torch.tensor(c5["cu_q"], dtype=torch.int32, device=dev), 512)
+        d5t = idx.idx_gather_rows(d5, tail)
+        mask5t = torch.empty((d5t.T, W5), dtype=torch.uint8, device=dev)
+        cand_tail = time_events(lambda: idx.idx_block_candidates(d5t, W5, pool=pool5, n_blocks=nb5, block_k=bk5,
+                                                                 row_chunk=4096, mask=mask5t, ws=ws5, stream=stream),
+                                3, stream)
+        p5c = synth.consumer_layer(p5)
+        d5c = idx.Inputs.from_host(p5c, device=dev)
+        wsc = torch.empty(idx.idx_workspace_size(idx.IDX_OP_LOGITS_TOPK_FUSED, d5c, K=K5, block_k=bk5, row_chunk=4096),
+                          dtype=torch.uint8, device=dev)
+        cons_mask = time_events(lambda: idx.idx_logits_topk_fused(d5c, K5, block_k=bk5, row_chunk=4096, mask=mask5,
+                                                                  ws=wsc, stream=stream), 3, stream)
+        cons_blocks = time_events(lambda: idx.idx_logits_topk_fused_blocks(d5c, K5, blocks5, pool=pool5, block_k=bk5,
+                                                                           row_chunk=4096, ws=wsc, stream=stream),
+                                  3, stream)
+        extra["ragged_candidates"] = {
+            "all_rows": {"rows": p5.T, "ms": float(np.median(cand_all)), "mask_bytes": int(mask5.numel())},
+            "tail_rows_512": {"rows": int(d5t.T), "ms": float(np.median(cand_tail)), "mask_bytes": int(mask5t.numel())},
+            "consumer_byte_mask_ms": float(np.median(cons_mask)),
+            "consumer_block_ids_ms": float(np.median(cons_blocks)), "block_ids_bytes": int(blocks5.numel() * 4)}
+        log(f"[bench] ragged candidates: all rows {np.median(cand_all):.2f} ms, tail rows {np.median(cand_tail):.2f} ms;"
+            f" consumer: byte mask {np.median(cons_mask):.2f} ms, block ids {np.median(cons_blocks):.2f} ms")
+        del d5, d5t, d5c, mask5, mask5t, ws5, wsc
         out["extra"] = extra
 
     if not args.no_cpu:
