@@ -272,7 +272,9 @@ __device__ __forceinline__ int merge_items(Smem &sm, int N, int run_n, int id0, 
 template <bool SLABS, bool BLOCKS>
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) void topk_kernel(TopkArgs a) {
   __shared__ Smem sm;
-  const int r = blockIdx.x;
+  // newest rows first: the scoring launch before this one wrote them last, so they are the
+  // ones still held in the memory-side cache
+  const int r = a.nrows - 1 - (int)blockIdx.x;
   const int t = a.row0 + r;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
