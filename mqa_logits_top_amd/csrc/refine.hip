@@ -242,6 +242,7 @@ __global__ __launch_bounds__(NTH) void refine_kernel(RefineArgs a) {
         if (tid < m) {
           const uint32_t me = rl[tid];
           int gt = 0, ge = 0;
+#pragma unroll 8
           for (int j = 0; j < m; ++j) {
             const uint32_t o = rl[j];
             gt += o > me;
@@ -425,6 +426,7 @@ __global__ __launch_bounds__(NTH) void refine_kernel(RefineArgs a) {
       const uint32_t kj = sm.bexact[j];
       const int idj = sm.bid[j];
       int rank = 0;
+#pragma unroll 8
       for (int m = 0; m < nb; ++m) {
         const uint32_t km = sm.bexact[m];
         rank += km > kj || (km == kj && sm.bid[m] < idj);
