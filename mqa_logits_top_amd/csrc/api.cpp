@@ -135,7 +135,8 @@ int32_t block_slabs(int32_t Bk) {
 }
 size_t slab_ws(int32_t Tc, int32_t Bk) {
   const size_t ns = (size_t)block_slabs(Bk);
-  return round_up_sz((size_t)Tc * 4, 256) + round_up_sz((size_t)Tc * ns * idx::CAND_PARTS * 4, 256) +
+  return round_up_sz((size_t)Tc * 4, 256) + round_up_sz((size_t)(Tc / 8 + 1) * 4, 256) +
+         round_up_sz((size_t)Tc * ns * idx::CAND_PARTS * 4, 256) +
          round_up_sz((size_t)Tc * ns * CAPS * 8, 256);
 }
 // Keys per scoring and top-K launch of the fused path: key blocks go in pairs (the
@@ -382,6 +383,7 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
   float *scratch = cv.take<float>((size_t)Tc * sld);
   const int32_t nslab_max = block_slabs(LB);
   float *thr = cv.take<float>((size_t)Tc);
+  uint32_t *ovf = cv.take<uint32_t>((size_t)Tc / 8 + 1);   // per scoring row block (>= 8 rows)
   uint32_t *ccnt = cv.take<uint32_t>((size_t)Tc * nslab_max * idx::CAND_PARTS);
   uint32_t *slab = cv.take<uint32_t>((size_t)Tc * nslab_max * CAPS * 2);
   if ((st = launched(idx::launch_key_bound((const uint8_t *)p->k, (const uint8_t *)p->k_scale, p->k_fmt, p->L,
@@ -392,21 +394,38 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
     int32_t kb = 0;
     do {
       const int32_t nk = std::min(LB, p->L - kb);
-      // launches after the first also append candidates above each row's running threshold
+      // launches after the first write only the scores above each row's running threshold,
+      // to candidate slabs; the row blocks where a slab overflowed are then scored again into
+      // the scratch, which the top-K reads for those rows
       bool slabs = false;
       int32_t nslab = 0;
       if (nk > 0) {
         idx::LogitsArgs a = logits_args(p, r0, nr, kb, kb + nk, scratch, sld, nk);
         slabs = kb >= slab_from(p) * LB && a.nsplit <= nslab_max && (int64_t)nr * a.nsplit * CAPS * 8 < INT32_MAX;
         nslab = a.nsplit;
-        if (slabs) {
+        if (slabs && !mask && !blocks) {
+          idx::LogitsArgs c = a;
+          c.thr = thr;
+          c.cand = slab;
+          c.ccnt = ccnt;
+          c.caps = CAPS;
+          if ((st = launched(idx::launch_logits(c, p->k_fmt, p->H, idx::STORE_SLAB, s)))) return st;
+          const int32_t rpw = idx::logits_rows_per_workgroup(p->H);
+          if ((st = launched(idx::launch_slab_check(ccnt, a.nsplit * idx::CAND_PARTS, thr, nr, rpw, ovf, s))))
+            return st;
+          a.only_flagged = ovf;
+          if ((st = launched(idx::launch_logits(a, p->k_fmt, p->H, idx::STORE_BLOCK, s)))) return st;
+        } else if (slabs) {
+          // a consumer mask the scoring kernel does not see would fill the slabs with keys the
+          // top-K then drops: score the block and the slabs in one pass instead
           a.thr = thr;
           a.cand = slab;
           a.ccnt = ccnt;
           a.caps = CAPS;
-        }
-        if ((st = launched(idx::launch_logits(a, p->k_fmt, p->H, slabs ? idx::STORE_CAND : idx::STORE_BLOCK, s))))
+          if ((st = launched(idx::launch_logits(a, p->k_fmt, p->H, idx::STORE_CAND, s)))) return st;
+        } else if ((st = launched(idx::launch_logits(a, p->k_fmt, p->H, idx::STORE_BLOCK, s)))) {
           return st;
+        }
       }
       idx::TopkArgs b{};
       if (slabs) {

@@ -5,7 +5,8 @@
 
 namespace idx {
 
-enum LogitsMode { STORE_DENSE = 0, STORE_BLOCK = 1, STORE_POOL8 = 2, STORE_CAND = 3 };
+// STORE_SLAB: the candidate output of STORE_CAND alone, no block scores.
+enum LogitsMode { STORE_DENSE = 0, STORE_BLOCK = 1, STORE_POOL8 = 2, STORE_CAND = 3, STORE_SLAB = 4 };
 
 // Largest number of parts a scoring work item (row block x key split) is cut into.
 constexpr int CAND_PARTS = 4;
@@ -44,10 +45,19 @@ struct LogitsArgs {
   const float *thr;
   uint32_t *cand;
   uint32_t *ccnt;
+  // STORE_BLOCK: score only the row blocks (RPW rows of the launch) whose word here is
+  // nonzero (nullable: all)
+  const uint32_t *only_flagged;
   int32_t caps;
 };
 
 hipError_t launch_logits(const LogitsArgs &a, int k_fmt, int H, int mode, hipStream_t s);
+int logits_rows_per_workgroup(int H);   // RPW of the scoring launches
+// Row blocks of a candidate-slab launch whose rows the top-K cannot serve from the slabs
+// alone (a share overflowed, the shares together exceed the merge capacity, or the row's
+// list is not full yet: thr NaN): flags[b] = 1 for them, 0 for the others.
+hipError_t launch_slab_check(const uint32_t *ccnt, int32_t nshares, const float *thr, int32_t nrows, int32_t rpw,
+                             uint32_t *flags, hipStream_t s);
 
 // Top-K over row-major fp32 values (one workgroup per row, running top-K kept
 // across passes).  Row r of the launch is problem row t = row0 + r.  Column c

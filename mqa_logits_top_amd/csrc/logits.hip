@@ -110,7 +110,7 @@ __device__ __forceinline__ int swz8(int n) { return (n & 7) ^ ((n >> 3) & 1); }
 __device__ __forceinline__ int swz4(int n) { return ((n >> 1) ^ (n >> 3)) & 3; }
 
 template <int KF, int H, int MODE, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MODE == STORE_CAND && H == 32 ? 2 : 3))) void logits_kernel(LogitsArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((MODE == STORE_CAND || MODE == STORE_SLAB) && H == 32 ? 2 : 3))) void logits_kernel(LogitsArgs a) {
   constexpr int QR = 128 / H;            // query rows per wave
   constexpr int HPT = 16 / QR;           // heads of one row in a 16-row A tile
   constexpr int NT = H / HPT;            // A tiles per wave (8)
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MODE ==
   constexpr int TK = KF == 0 ? 128 : 256; // keys per LDS stage (16 KiB either way)
   constexpr int STAGE = TK * KB;
   constexpr int LPT = STAGE / 16 / (NW * 64);  // 16-byte chunks per thread per stage
-  constexpr int ST = TK / 64;  // stores per stage and wave, at least (candidate stores come on top)
+  constexpr int ST = MODE == STORE_SLAB ? 0 : TK / 64;  // stores per stage and wave, at least (candidate stores on top)
   static_assert(LPT * NW * 64 * 16 == STAGE, "stage must split evenly over the workgroup");
   static_assert(RPW <= 64 && TK <= NW * 64 && TK % 64 == 0, "layout limits");
 
@@ -150,6 +150,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MODE ==
   }
   const int split_i = item % a.nsplit;
   const int rb = item / a.nsplit;
+  if (MODE == STORE_BLOCK && a.only_flagged && a.only_flagged[rb] == 0) return;   // uniform
   const int r_begin = a.row0 + rb * RPW;
   const int r_end = min(r_begin + RPW, a.row0 + a.nrows);
 
@@ -179,7 +180,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MODE ==
   const int ntiles = pt1 - pt0;
   // candidate share of this part in each of its rows' slabs
   const int share0 = part * a.caps / nparts, share = (part + 1) * a.caps / nparts - share0;
-  if (MODE == STORE_CAND && part == 0) {  // count words of the parts an item does not have
+  constexpr bool cand = MODE == STORE_CAND || MODE == STORE_SLAB;
+  if (cand && part == 0) {  // count words of the parts an item does not have
     for (int i = tid; i < RPW * (CAND_PARTS - nparts); i += NW * 64) {
       const int rr = r_begin + i / (CAND_PARTS - nparts);
       if (rr < r_end)
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MODE ==
     }
   }
   if (ntiles <= 0) {  // uniform over the workgroup: nothing to score, no candidates
-    if (MODE == STORE_CAND && tid < r_end - r_begin)
+    if (cand && tid < r_end - r_begin)
       a.ccnt[((r_begin - a.row0 + tid) * a.nsplit + split_i) * CAND_PARTS + part] = (uint32_t)share0 << 16;
     return;
   }
@@ -251,7 +253,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MODE ==
   // keys this lane may store: inside its row's window and inside the workgroup range
   const int v_lo = max(kst, s_lo), v_hi = min(ket, s_hi);
   // candidate slab of this lane's row (STORE_BLOCK with candidate output)
-  constexpr bool cand = MODE == STORE_CAND;
   float thr_row = __builtin_nanf("");
   int slab = 0;  // pair offset of the slab (slabs span < 2^31 bytes)
   __amdgpu_buffer_rsrc_t crsrc;
@@ -364,7 +365,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MODE ==
           crow += tot;
         }
       }
-      if (MODE != STORE_POOL8) {
+      if (MODE != STORE_POOL8 && MODE != STORE_SLAB) {
         const int col = MODE == STORE_DENSE ? s0 - kst : s0 - a.key_lo;   // column of key s0
         if (writer && row_al && s0 >= v_lo && s0 + 4 <= lim) {
           const v4u d = {__float_as_uint(val[0]), __float_as_uint(val[1]), __float_as_uint(val[2]),
@@ -425,9 +426,11 @@ int resident_workgroups(Kern kern, int threads) {
   return cached[dev];
 }
 
+constexpr int NW_LAUNCH = 4;   // 4 waves: up to 3 workgroups per CU, so a stage barrier never idles the CU
+
 template <int KF, int H, int MODE>
 hipError_t launch3(const LogitsArgs &a0, hipStream_t s) {
-  constexpr int NW = 4;   // 4 waves: up to 3 workgroups per CU, so a stage barrier never idles the CU
+  constexpr int NW = NW_LAUNCH;
   constexpr int RPW = NW * (128 / H);
   auto kern = logits_kernel<KF, H, MODE, NW>;
   const int nrb = (a0.nrows + RPW - 1) / RPW;
@@ -452,11 +455,14 @@ hipError_t launch2(const LogitsArgs &a, int mode, hipStream_t s) {
     case STORE_DENSE: return launch3<KF, H, STORE_DENSE>(a, s);
     case STORE_BLOCK: return launch3<KF, H, STORE_BLOCK>(a, s);
     case STORE_CAND: return launch3<KF, H, STORE_CAND>(a, s);
+    case STORE_SLAB: return launch3<KF, H, STORE_SLAB>(a, s);
     default: return launch3<KF, H, STORE_POOL8>(a, s);
   }
 }
 
 }  // namespace
+
+int logits_rows_per_workgroup(int H) { return NW_LAUNCH * (128 / H); }
 
 hipError_t launch_logits(const LogitsArgs &a, int k_fmt, int H, int mode, hipStream_t s) {
   if (k_fmt == 0) return H == 32 ? launch2<0, 32>(a, mode, s) : launch2<0, 64>(a, mode, s);

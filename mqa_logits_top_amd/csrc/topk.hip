@@ -668,7 +668,36 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   if (a.thr_out && tid == 0) a.thr_out[r] = run_n == K ? kval(list_min) : __builtin_nanf("");
 }
 
+// One wave per row block: does any of its rows need the block's scores?  The conditions
+// are those under which topk_kernel<true, *> leaves the slab merge for the column pass.
+// Lanes take the row's count words (nshares <= NTH); the wave sums them.
+__global__ __launch_bounds__(64) void slab_check_kernel(const uint32_t *ccnt, int32_t nshares, const float *thr,
+                                                        int32_t nrows, int32_t rpw, uint32_t *flags) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  bool need = nshares > NTH;
+  for (int r = b * rpw; r < min((b + 1) * rpw, nrows); ++r) {
+    uint32_t tot = 0, over = 0;
+    for (int e = lane; e < nshares; e += 64) {
+      const uint32_t c = ccnt[(int64_t)r * nshares + e] & 0xFFFFu;
+      over |= c == CAND_OVER;
+      tot += c == CAND_OVER ? 0u : c;
+    }
+    tot = wave_sum(tot);
+    over = wave_max(over);
+    need |= over != 0u || tot > (uint32_t)CAPK || !(thr[r] == thr[r]);   // NaN: the row's list is not full
+  }
+  if (lane == 0) flags[b] = need ? 1u : 0u;
+}
+
 }  // namespace
+
+hipError_t launch_slab_check(const uint32_t *ccnt, int32_t nshares, const float *thr, int32_t nrows, int32_t rpw,
+                             uint32_t *flags, hipStream_t s) {
+  const int nb = (nrows + rpw - 1) / rpw;
+  if (nb <= 0) return hipSuccess;
+  hipLaunchKernelGGL(slab_check_kernel, dim3(nb), dim3(64), 0, s, ccnt, nshares, thr, nrows, rpw, flags);
+  return hipGetLastError();
+}
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
   if (a.nrows <= 0) return hipSuccess;

@@ -153,8 +153,8 @@ def test_workspace_sizes(lib):
     n = ctypes.c_size_t()
     assert lib.idx_workspace_size(2, ctypes.byref(p), 2048, 32768, 0, 0, 0, 0, ctypes.byref(n)) == 0
     # key blocks are scored in pairs: 65536 keys per launch, split 16 ways
-    # thresholds, count words (16 splits x 4 parts), (value, id) pairs (16 slabs of 512)
-    slab = lambda Tc: _r(Tc * 4) + _r(Tc * 16 * 4 * 4) + _r(Tc * 16 * 512 * 8)
+    # thresholds, overflow flags, count words (16 splits x 4 parts), (value, id) pairs (16 slabs of 512)
+    slab = lambda Tc: _r(Tc * 4) + _r((Tc // 8 + 1) * 4) + _r(Tc * 16 * 4 * 4) + _r(Tc * 16 * 512 * 8)
     assert n.value == head + 2 * _r(2048 * kc(2048) * 4) + 2048 * (65536 + 64) * 4 + slab(2048)
     # the row chunk bounds the workspace; the number of keys does not enter
     p2 = _problem(T=16384, L=487936)
