@@ -139,15 +139,17 @@ def test_fused_slab_overflow_and_fit():
     assert torch.equal(dv.view(torch.int32), fv.view(torch.int32))
 
 
-def test_fused_paged_transform(case):
+@pytest.mark.parametrize("row_chunk", [0, 16])
+def test_fused_paged_transform(case, row_chunk):
     """Index -> KV-slot transform in the final write: out_slot = slot_of_key[out_idx], -1 pads;
-    ids and values equal the untransformed call's."""
+    ids and values equal the untransformed call's (also across row chunks)."""
     p, d, o = case
     K = 64
     rng = np.random.default_rng(11)
     table = rng.permutation(4 * p.L)[:p.L].astype(np.int32)     # distinct slots, not the identity
     fi, fv = idx.idx_logits_topk_fused(d, K, block_k=512)
-    pi, pv, ps = idx.idx_logits_topk_fused_paged(d, K, torch.from_numpy(table).cuda(), block_k=512)
+    pi, pv, ps = idx.idx_logits_topk_fused_paged(d, K, torch.from_numpy(table).cuda(), block_k=512,
+                                                 row_chunk=row_chunk)
     assert torch.equal(fi, pi) and torch.equal(fv.view(torch.int32), pv.view(torch.int32))
     ids = pi.cpu().numpy()
     want = np.where(ids >= 0, table[np.maximum(ids, 0)], -1)
@@ -198,7 +200,7 @@ def test_fused_block_consumer(case, pool):
             lo = b * pool
             mask[t, lo:min(lo + pool, win)] = 1
     bt = torch.from_numpy(blocks).cuda()
-    bi, bv = idx.idx_logits_topk_fused_blocks(d, K, bt, pool=pool, block_k=512)
+    bi, bv = idx.idx_logits_topk_fused_blocks(d, K, bt, pool=pool, block_k=512, row_chunk=8 if pool == 16 else 0)
     mi, mv = idx.idx_logits_topk_fused(d, K, block_k=512, mask=torch.from_numpy(mask).cuda())
     assert torch.equal(bi, mi) and torch.equal(bv.view(torch.int32), mv.view(torch.int32))
     allowed = [mask[t, :len(o[t])].astype(bool) for t in range(p.T)]
