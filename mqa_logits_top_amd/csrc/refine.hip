@@ -91,11 +91,6 @@ __device__ __forceinline__ double quads_sum_f64(double x) {
   return __longlong_as_double((long long)(((uint64_t)h32[0] << 32) | l32[0])) +
          __longlong_as_double((long long)(((uint64_t)h32[1] << 32) | l32[1]));
 }
-template <class T, class Op>
-__device__ __forceinline__ T wave_all(T x, Op op) {
-  for (int o = 32; o > 0; o >>= 1) x = op(x, __shfl_xor(x, o));
-  return x;
-}
 
 static_assert(KB * 4 * KPAD * 2 >= NB + 64 + RCAP && KB * 4 * KPAD * 2 >= KC_MAX, "key buffer overlays");
 
@@ -118,7 +113,7 @@ struct Smem {
 
 // Block-wide sum / min / max helpers (all threads call).
 __device__ __forceinline__ uint32_t block_sum(Smem &sm, uint32_t x, int lane, int wave) {
-  x = wave_all(x, [](uint32_t a, uint32_t b) { return a + b; });
+  x = wave_sum(x);
   __syncthreads();
   if (lane == 0) sm.red[0][wave] = x;
   __syncthreads();
@@ -128,10 +123,9 @@ __device__ __forceinline__ uint32_t block_sum(Smem &sm, uint32_t x, int lane, in
   return s;
 }
 __device__ __forceinline__ void block_sum3(Smem &sm, uint32_t &a, uint32_t &b, uint32_t &c, int lane, int wave) {
-  auto add = [](uint32_t x, uint32_t y) { return x + y; };
-  a = wave_all(a, add);
-  b = wave_all(b, add);
-  c = wave_all(c, add);
+  a = wave_sum(a);
+  b = wave_sum(b);
+  c = wave_sum(c);
   __syncthreads();
   if (lane == 0) { sm.red[0][wave] = a; sm.red[1][wave] = b; sm.red[2][wave] = c; }
   __syncthreads();
@@ -141,8 +135,8 @@ __device__ __forceinline__ void block_sum3(Smem &sm, uint32_t &a, uint32_t &b, u
 }
 
 __device__ __forceinline__ void block_minmax(Smem &sm, uint32_t &lo, uint32_t &hi, int lane, int wave) {
-  lo = wave_all(lo, [](uint32_t x, uint32_t y) { return min(x, y); });
-  hi = wave_all(hi, [](uint32_t x, uint32_t y) { return max(x, y); });
+  lo = wave_min(lo);
+  hi = wave_max(hi);
   __syncthreads();
   if (lane == 0) { sm.red[1][wave] = lo; sm.red[2][wave] = hi; }
   __syncthreads();
@@ -153,11 +147,7 @@ __device__ __forceinline__ void block_minmax(Smem &sm, uint32_t &lo, uint32_t &h
 }
 // Exclusive prefix sum in thread order.
 __device__ __forceinline__ uint32_t block_excl_scan(Smem &sm, uint32_t x, int lane, int wave) {
-  uint32_t incl = x;
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
+  const uint32_t incl = wave_incl_scan(x);
   __syncthreads();
   if (lane == 63) sm.red[0][wave] = incl;
   __syncthreads();
@@ -298,10 +288,10 @@ __global__ __launch_bounds__(NTH) void refine_kernel(RefineArgs a) {
     mq = fmaxf(mq, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mq), 0xB1, 0xF, 0xF, false)));
     mq = fmaxf(mq, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mq), 0x4E, 0xF, 0xF, false)));
     float part = (cc == 0 && wave < hw) ? fabsf(wh * qsh * a.scale) * mq : 0.f;
-    part = wave_all(part, [](float x, float y) { return x + y; });
+    part = wave_reduce_f32(part, [](float x, float y) { return x + y; });
     float kmax = 0.f;
     for (int i = lane; i < a.npart; i += 64) kmax = fmaxf(kmax, a.kmax_part[i]);
-    kmax = wave_all(kmax, [](float x, float y) { return fmaxf(x, y); });
+    kmax = wave_reduce_f32(kmax, [](float x, float y) { return fmaxf(x, y); });
     if (lane == 0) sm.fred[wave] = part;
     if (tid == 0) sm.misc[2] = 0;
     __syncthreads();
@@ -454,11 +444,7 @@ __global__ __launch_bounds__(NTH) void refine_kernel(RefineArgs a) {
   uint32_t kept = 0;
 #pragma unroll
   for (int e = 0; e < PER; ++e) kept += cid[e] >= 0;
-  uint32_t incl = kept;
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
+  const uint32_t incl = wave_incl_scan(kept);
   __syncthreads();
   if (lane == 63) sm.red[0][wave] = incl;
   __syncthreads();
