@@ -29,6 +29,12 @@
 //
 // For pooled candidates (block ids), a block's exact value is the max of the
 // exact scores of its in-window keys.
+//
+// The band re-score is a small dense contraction (heads x 128 dims x 16 keys
+// per batch) and runs on the fp64 MFMA (16x16x4): A = q of 16 heads, B = 16
+// band keys, both decoded from their fp8 / e2m1 codes in registers.  Chunk c of
+// a lane's dims is 32 c + 8 (lane / 16) + i (i < 8), so each MFMA sums dims of
+// one 32-element MX block and per-block sums stay separate before their scale.
 #include <cfloat>
 
 #include "common.h"
@@ -41,11 +47,13 @@ constexpr int NTH = 256;
 constexpr int NWV = NTH / 64;
 constexpr int PER = 10;                 // candidates per thread, contiguous
 constexpr int KC_MAX = NTH * PER;       // 2560
-constexpr int KB = 16;                  // band keys scored per batch
-constexpr int KPAD = 34;                // doubles per 32-element key chunk in LDS (chunks on distinct banks)
+constexpr int KB = 16;                  // band keys scored per batch (the MFMA's 16 columns)
 constexpr int NB = 2048;                // selection histogram bins
 constexpr int RCAP = 256;               // direct ranking threshold
 constexpr float GAMMA = 2.0f;
+
+typedef double d4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
 
 // OCP E4M3 ("FN") code -> float, exact.
 __device__ __forceinline__ float e4m3(uint32_t c) {
@@ -62,24 +70,18 @@ __device__ __forceinline__ float e2m1(uint32_t c) {
   return (c & 8u) ? -v : v;
 }
 
-// Wave reductions on DPP / permlane moves (32-bit lanes; doubles move as two halves).
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double x) {
-  const uint64_t u = (uint64_t)__double_as_longlong(x);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xF, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
-  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+// Four E4M3 codes (bytes of w, low first) -> exact doubles.
+__device__ __forceinline__ void fp8x4_f64(uint32_t w, double *o) {
+  const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  o[0] = (double)lo[0];
+  o[1] = (double)lo[1];
+  o[2] = (double)hi[0];
+  o[3] = (double)hi[1];
 }
-// sum over the 4 lanes of a quad
-__device__ __forceinline__ double quad_sum_f64(double x) {
-  x += dpp_f64<0xB1>(x);  // quad [1,0,3,2]
-  x += dpp_f64<0x4E>(x);  // quad [2,3,0,1]
-  return x;
-}
-// sum over the 16 lanes 4 i (i < 16) of a wave: quads already hold their sums
-__device__ __forceinline__ double quads_sum_f64(double x) {
-  x += dpp_f64<0x141>(x);  // row half mirror: pairs the two quads of each half row
-  x += dpp_f64<0x140>(x);  // row mirror: pairs the half rows
+
+// Sum over the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48) by permlane swaps; the
+// result is the same value in every lane (doubles move as two 32-bit halves).
+__device__ __forceinline__ double rows_sum_f64(double x) {
   const uint64_t u = (uint64_t)__double_as_longlong(x);
   const auto l16 = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
   const auto h16 = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
@@ -92,20 +94,19 @@ __device__ __forceinline__ double quads_sum_f64(double x) {
          __longlong_as_double((long long)(((uint64_t)h32[1] << 32) | l32[1]));
 }
 
-static_assert(KB * 4 * KPAD * 2 >= NB + 64 + RCAP && KB * 4 * KPAD * 2 >= KC_MAX, "key buffer overlays");
+constexpr int OVL = KC_MAX;             // words of the overlay buffer
+static_assert(OVL >= NB + 64 + RCAP && OVL * 4 >= 2 * 64 * 4 * 8, "overlay buffer uses");
+
 
 struct Smem {
   uint8_t state[KC_MAX];       // per candidate slot: 0 out, 1 certain, 2 band, 3 band and taken
   int16_t band[KC_MAX];        // band entry -> candidate slot
   uint32_t bexact[KC_MAX];     // band entry -> key of its exact score (pooled: max over its keys)
   int32_t bid[KC_MAX];         // band entry -> candidate id
-  double kd[KB][4][KPAD];      // decoded key rows of a batch by 32-element chunk (element values, no
-                               // MX block scale); also the selection's histogram, and at the end the
-                               // taken band entries' exact scores by slot
-  double ksc[KB][4];           // per key: k_scale (fp8, all four) or the four MX block scales
-  int32_t bk_key[KB];          // batch slot -> key row (-1: none)
-  int32_t bk_ent[KB];          // batch slot -> band entry
-  double part[KB][NWV];        // per key and wave: head-sum partials
+  // overlay: the selection's histogram and ranking list; during the band scores the second
+  // chunk group's dot partials (32 heads); at the end the taken band entries' exact scores by slot
+  __attribute__((aligned(16))) uint32_t ovl[OVL];
+  double part[2][KB][NWV];     // per batch parity, key and head tile: head-sum partials
   uint32_t red[3][NWV];
   float fred[NWV];
   uint32_t misc[8];
@@ -158,13 +159,14 @@ __device__ __forceinline__ uint32_t block_excl_scan(Smem &sm, uint32_t x, int la
   return before;
 }
 
+template <int H>
 __global__ __launch_bounds__(NTH) void refine_kernel(RefineArgs a) {
   __shared__ Smem sm;
   const int r = blockIdx.x;
   const int t = a.row0 + r;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int Kc = a.Kc, K = a.K, H = a.H;
+  const int Kc = a.Kc, K = a.K;
   const int32_t *cidx = a.cand_idx + (int64_t)r * a.ld_cand;
   const float *cval = a.cand_val + (int64_t)r * a.ld_cand;
   int32_t *oidx = a.out_idx + (int64_t)r * K;
@@ -182,27 +184,45 @@ __global__ __launch_bounds__(NTH) void refine_kernel(RefineArgs a) {
     cv[e] = i < Kc ? cval[i] : 0.f;
     mine += cid[e] >= 0;
   }
-  // ---- this lane's q slice: head h = 16 (wave % hw) + lane / 4, dims 32 (lane % 4) .. + 31
-  const int hw = H / 16;                        // waves covering all heads (2 or 4)
-  const int hq = 16 * (wave % hw) + (lane >> 2);
+  // ---- error-bound inputs: lane (head hq = 16 (wave % HW) + lane / 4, dims 32 (lane % 4) .. + 31)
+  constexpr int HW = H / 16;                    // head tiles of 16 (2 or 4)
+  constexpr int NCH = 4 * HW / NWV;             // 32-dim chunks per wave in the band scores (2 or 4)
+  const int hq = 16 * (wave % HW) + (lane >> 2);
   const int cc = lane & 3;
-  double qd[32];
+  uint32_t qmax = 0;                            // largest |E4M3| code of the slice (monotone in the low 7 bits)
   {
     const uint8_t *qp = a.q + ((int64_t)t * H + hq) * 128 + 32 * cc;
     const uint4 u0 = *(const uint4 *)qp, u1 = *(const uint4 *)(qp + 16);
     const uint32_t w8[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
-    for (int i = 0; i < 32; ++i) qd[i] = (double)e4m3((w8[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+    for (int i = 0; i < 32; ++i) qmax = max(qmax, (w8[i >> 2] >> (8 * (i & 3))) & 0x7Fu);
   }
   const float wh = a.w[(int64_t)t * H + hq];
   const float qsh = a.q_scale[(int64_t)t * H + hq];
+  // ---- band-score operands: wave = (head tile, chunk group); lane holds head 16 tile + lane % 16
+  // (A rows) and key slot lane % 16 (B columns); dims 32 c + 8 g + i of its chunks c, g = lane / 16
+  const int tile = wave % HW, cgrp = wave / HW, g = lane >> 4;
+  uint2 qraw[NCH];                              // E4M3 codes, decoded per batch (keeps registers for occupancy)
+  {
+    const uint8_t *qp = a.q + ((int64_t)t * H + 16 * tile + (lane & 15)) * 128 + 8 * g;
+#pragma unroll
+    for (int cl = 0; cl < NCH; ++cl) qraw[cl] = *(const uint2 *)(qp + 32 * (cgrp * NCH + cl));
+  }
+  // epilogue rows: lane holds D rows 4 r + g (r < 4) of its tile
+  float qs4[4], w4[4];
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) {
+    const int64_t hh = (int64_t)t * H + 16 * tile + 4 * r4 + g;
+    qs4[r4] = a.q_scale[hh];
+    w4[r4] = a.w[hh];
+  }
   const int n = (int)block_sum(sm, mine, lane, wave);
 
   if (n > K) {
     // ---- theta: key of the K-th largest candidate.  Histograms over the candidates'
     // key range [clo, chi] (bins anchored at chi) narrow it to one bin until at most
     // RCAP candidates remain, which are ranked directly.
-    uint32_t *hist = (uint32_t *)&sm.kd[0][0][0];   // NB bins + one spare slot per lane
+    uint32_t *hist = sm.ovl;                         // NB bins + one spare slot per lane
     uint32_t *rl = hist + NB + 64;                   // ranking list
     uint32_t ck[PER];
     uint32_t clo = 0xFFFFFFFFu, chi = 0;
@@ -282,12 +302,10 @@ __global__ __launch_bounds__(NTH) void refine_kernel(RefineArgs a) {
     const float theta = kval(thk);
 
     // ---- per-row error bound D = GAMMA 2^-13 Kmax sum_h |w'_h| Mq_h (Mq_h: largest |q| of head h)
-    float mq = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) mq = fmaxf(mq, (float)fabs(qd[i]));
+    float mq = e4m3(qmax);
     mq = fmaxf(mq, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mq), 0xB1, 0xF, 0xF, false)));
     mq = fmaxf(mq, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mq), 0x4E, 0xF, 0xF, false)));
-    float part = (cc == 0 && wave < hw) ? fabsf(wh * qsh * a.scale) * mq : 0.f;
+    float part = (cc == 0 && wave < HW) ? fabsf(wh * qsh * a.scale) * mq : 0.f;
     part = wave_reduce_f32(part, [](float x, float y) { return x + y; });
     float kmax = 0.f;
     for (int i = lane; i < a.npart; i += 64) kmax = fmaxf(kmax, a.kmax_part[i]);
@@ -328,12 +346,10 @@ __global__ __launch_bounds__(NTH) void refine_kernel(RefineArgs a) {
     const int need_b = K - (int)nin;
     if (tid == 0 && n == Kc && below == 0 && a.overflow) atomicAdd(a.overflow, 1u);
 
-    // ---- exact scores of the band, KB keys per batch (raw bytes of batch b + 1 fetched early)
+    // ---- exact scores of the band, KB keys per batch (raw codes of batch b + 1 fetched early)
     const int kpe = a.pool == 1 ? 1 : a.pool;   // keys per band entry
     const int nkeys = nb * kpe;
     const int ks = max(a.ks[t], 0), ke = min(a.ke[t], a.L);
-    // batch element of this thread: key slot j = tid / 16, 16-thread groups read 8 (fp8) / 4 (fp4) bytes each
-    const int jb = tid >> 4, part16 = tid & 15;
     auto key_of = [&](int e) __attribute__((always_inline)) -> int {  // batch element e -> key row or -1
       if (e >= nkeys) return -1;
       const int be = e / kpe;
@@ -342,75 +358,110 @@ __global__ __launch_bounds__(NTH) void refine_kernel(RefineArgs a) {
       if (s < 0 || s >= a.L || (a.pool > 1 && s >= ke)) s = -1;
       return s;
     };
-    uint2 raw = {0u, 0u};
-    uint32_t rsc = 0;
-    int rkey = -1;
+    // lane's B column: key slot j = lane % 16; codes of its dims 32 c + 8 g + i
+    const int jk = lane & 15;
+    uint2 nraw[NCH];
+    uint32_t nsc = 0;
+    int nkey = -1;
     auto fetch = [&](int base) __attribute__((always_inline)) {
-      rkey = key_of(base + jb);
-      raw = (uint2){0u, 0u};
-      rsc = 0;
-      if (rkey >= 0) {
-        if (a.k_fmt == 0) raw = *(const uint2 *)(a.k + (int64_t)rkey * 128 + 8 * part16);
-        else raw.x = *(const uint32_t *)(a.k + (int64_t)rkey * 64 + 4 * part16);
-        if (part16 == 0) rsc = *(const uint32_t *)(a.k_scale + (int64_t)rkey * 4);
+      nkey = key_of(base + jk);
+      nsc = 0;
+#pragma unroll
+      for (int cl = 0; cl < NCH; ++cl) nraw[cl] = (uint2){0u, 0u};
+      if (nkey >= 0) {
+        const int c0 = cgrp * NCH;
+        if (a.k_fmt == 0) {
+          const uint8_t *kp = a.k + (int64_t)nkey * 128 + 8 * g;
+#pragma unroll
+          for (int cl = 0; cl < NCH; ++cl) nraw[cl] = *(const uint2 *)(kp + 32 * (c0 + cl));
+        } else {
+          const uint8_t *kp = a.k + (int64_t)nkey * 64 + 4 * g;
+#pragma unroll
+          for (int cl = 0; cl < NCH; ++cl) nraw[cl].x = *(const uint32_t *)(kp + 16 * (c0 + cl));
+        }
+        nsc = *(const uint32_t *)(a.k_scale + (int64_t)nkey * 4);
       }
     };
+    double *pd = (double *)sm.ovl;               // second chunk group's dots: [tile][lane][4]
     __syncthreads();  // band lists complete
     if (nkeys > 0) fetch(0);
-    for (int base = 0; base < nkeys; base += KB) {
-      // decode the batch: thread (jb, part16) owns 8 elements of key slot jb
-      if (tid < KB * 16) {
-        if (part16 == 0) {
-          sm.bk_key[jb] = rkey;
-          sm.bk_ent[jb] = (base + jb) / kpe;
-          const float f = __uint_as_float(rsc);
+    int par = 0;
+    for (int base = 0; base < nkeys; base += KB, par ^= 1) {
+      uint2 raw[NCH];
 #pragma unroll
-          for (int blk = 0; blk < 4; ++blk)
-            sm.ksc[jb][blk] = rkey < 0 ? 0.0 : a.k_fmt == 0 ? (double)f : (double)e8m0((rsc >> (8 * blk)) & 0xFFu);
+      for (int cl = 0; cl < NCH; ++cl) raw[cl] = nraw[cl];
+      const uint32_t rsc = nsc;
+      const int rkey = nkey;
+#pragma unroll
+      for (int cl = 0; cl < NCH; ++cl) {   // opaque per batch: the decode below is not hoisted out of the loop
+        asm volatile("" : "+v"(qraw[cl].x));
+        asm volatile("" : "+v"(qraw[cl].y));
+      }
+      if (base + KB < nkeys) fetch(base + KB);
+      // D[4 r + g][jk] = dot(head 16 tile + 4 r + g, key slot jk) over this wave's chunks.
+      // Per-chunk sums of fp8 x fp8 / fp8 x e2m1 products are exact in fp64 in any order.
+      d4 dot = {0.0, 0.0, 0.0, 0.0};
+      if (a.k_fmt == 0) {
+#pragma unroll
+        for (int cl = 0; cl < NCH; ++cl) {
+          double qa[8], kb[8];
+          fp8x4_f64(qraw[cl].x, qa);
+          fp8x4_f64(qraw[cl].y, qa + 4);
+          fp8x4_f64(raw[cl].x, kb);
+          fp8x4_f64(raw[cl].y, kb + 4);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) dot = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[i], kb[i], dot, 0, 0, 0);
         }
-        if (a.k_fmt == 0) {
+      } else {
+        // MX: each 32-dim block sum times its power-of-two scale; blocks summed as (b0 + b1) + (b2 + b3)
+        d4 pair[NCH / 2];
+#pragma unroll
+        for (int cl = 0; cl < NCH; ++cl) {
+          double qa[8];
+          fp8x4_f64(qraw[cl].x, qa);
+          fp8x4_f64(qraw[cl].y, qa + 4);
+          d4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
           for (int i = 0; i < 8; ++i)
-            sm.kd[jb][part16 >> 2][8 * (part16 & 3) + i] = (double)e4m3(((i < 4 ? raw.x : raw.y) >> (8 * (i & 3))) & 0xFFu);
-        } else {
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[i], (double)e2m1((raw[cl].x >> (4 * i)) & 0xFu), acc, 0, 0, 0);
+          const double bs = (double)e8m0((rsc >> (8 * (cgrp * NCH + cl))) & 0xFFu);
+          acc *= bs;
+          if (cl & 1) pair[cl >> 1] += acc;
+          else pair[cl >> 1] = acc;
+        }
+        dot = pair[0];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) sm.kd[jb][part16 >> 2][8 * (part16 & 3) + i] = (double)e2m1((raw.x >> (4 * i)) & 0xFu);
-        }
+        for (int pi = 1; pi < NCH / 2; ++pi) dot += pair[pi];
       }
-      __syncthreads();
-      if (base + KB < nkeys) fetch(base + KB);
-      // dots: waves of one head group share a key; lane (head, chunk) sums its 32 dims
-      const int kpw = NWV / hw;                       // keys in flight per step (1 for H = 64, 2 for H = 32)
-      for (int j0 = 0; j0 < KB; j0 += kpw) {
-        const int j = j0 + wave / hw;
-        double acc = 0.0;
+      if constexpr (NCH < 4) {
+        // 32 heads: the second chunk group hands its dots to the first
+        if (cgrp == 1) *(d4 *)&pd[(tile * 64 + lane) * 4] = dot;
+        __syncthreads();
+        if (cgrp == 0) dot += *(const d4 *)&pd[(tile * 64 + lane) * 4];
+      }
+      if (cgrp == 0) {
+        // scales, ReLU, weights; sum over the tile's 16 heads (4 rows here, then the 4 lane rows)
+        const double ksc = a.k_fmt == 0 ? (double)__uint_as_float(rsc) : 1.0;
+        double hs = 0.0;
 #pragma unroll
-        for (int i = 0; i < 32; i += 2) {
-          const double2 kk = *(const double2 *)&sm.kd[j][cc][i];
-          acc = fma(qd[i], kk.x, acc);
-          acc = fma(qd[i + 1], kk.y, acc);
+        for (int r4 = 0; r4 < 4; ++r4) {
+          double d = dot[r4];
+          if (a.k_fmt == 0) d *= ksc;
+          const double dh = d * (double)qs4[r4] * (double)a.scale;
+          hs += (double)w4[r4] * (dh > 0.0 ? dh : 0.0);
         }
-        // chunk sums are exact; MX block scales are powers of two, the fp8 k_scale
-        // multiplies the whole dot once
-        if (a.k_fmt != 0) acc *= sm.ksc[j][cc];
-        double dot = quad_sum_f64(acc);                // head hq, all 128 dims, in all 4 lanes
-        if (a.k_fmt == 0) dot *= sm.ksc[j][0];
-        const double dh = dot * (double)qsh * (double)a.scale;
-        const double term = (double)wh * (dh > 0.0 ? dh : 0.0);
-        const double ws = quads_sum_f64(term);         // 16 heads of this wave
-        if (lane == 0) sm.part[j][wave % hw] = ws;
+        hs = rows_sum_f64(hs);
+        if (g == 0) sm.part[par][jk][tile] = hs;
       }
       __syncthreads();
-      if (tid < KB) {
-        const int s = sm.bk_key[tid];
-        if (s >= 0) {
-          double sc = 0.0;
-          for (int w = 0; w < hw; ++w) sc += sm.part[tid][w];
-          atomicMax(&sm.bexact[sm.bk_ent[tid]], fkey((float)sc));
-        }
+      if (tid < KB && rkey >= 0) {   // wave 0, lane = key slot
+        double sc = 0.0;
+#pragma unroll
+        for (int w = 0; w < HW; ++w) sc += sm.part[par][tid][w];
+        atomicMax(&sm.bexact[(base + tid) / kpe], fkey((float)sc));
       }
-      __syncthreads();
     }
+    __syncthreads();
     // ---- order the band by (exact desc, id asc) and take need_b of it
     for (int j = tid; j < nb; j += NTH) {
       const uint32_t kj = sm.bexact[j];
@@ -425,7 +476,7 @@ __global__ __launch_bounds__(NTH) void refine_kernel(RefineArgs a) {
     }
     __syncthreads();
     // taken band entries carry their exact score: per-slot values in the (now free) key buffer
-    float *sval = (float *)&sm.kd[0][0][0];
+    float *sval = (float *)sm.ovl;
     for (int j = tid; j < nb; j += NTH) {
       const int i = sm.band[j];
       if (sm.state[i] == 3) sval[i] = kval(sm.bexact[j]);
@@ -527,7 +578,9 @@ hipError_t launch_key_bound(const uint8_t *k, const uint8_t *k_scale, int k_fmt,
 
 hipError_t launch_refine(const RefineArgs &a, hipStream_t s) {
   if (a.nrows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(refine_kernel, dim3((unsigned)a.nrows), dim3(NTH), 0, s, a);
+  if (a.H == 32) hipLaunchKernelGGL(refine_kernel<32>, dim3((unsigned)a.nrows), dim3(NTH), 0, s, a);
+  else if (a.H == 64) hipLaunchKernelGGL(refine_kernel<64>, dim3((unsigned)a.nrows), dim3(NTH), 0, s, a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
