@@ -208,7 +208,8 @@ def cpu_baseline(p, K, budget_s):
         with threadpool_limits(limits=1):
             t2 = time.perf_counter()
             sp = 0
-            for t in order[rows:rows + 4]:
+            sel = order[rows:rows + 4] if rows + 4 <= len(order) else order[:4]   # whole sample done: reuse rows
+            for t in sel:
                 v = oracle.row_logits(dq, int(t))
                 oracle.topk_row(v, int(p.ks[t]), K)
                 sp += len(v)
