@@ -126,6 +126,17 @@ def row_logits(dq: Dequantised, t: int) -> np.ndarray:
     return dq.w[t] @ np.maximum(dots, 0.0)              # sum over heads
 
 
+def row_magnitude(dq: Dequantised, t: int) -> np.ndarray:
+    """M[t, s] = sum_h |w[t, h]| * max(0, scale * <qd[t, h, :], kd[s, :]>) for s in [ks_t, ke_t):
+    the size of I[t, s]'s head terms.  It equals I[t, s] when every weight of the row is
+    >= 0 (all the pages' workloads draw w from U(0, 1)); with weights of both signs the
+    terms can cancel, and a floating-point head sum is accurate relative to M, not to I.
+    The parity checks take their relative tolerance against max(|I|, M)."""
+    ks, ke = int(dq.ks[t]), int(dq.ke[t])
+    dots = dq.scale * (dq.qd[t] @ dq.kd[ks:ke].T)       # [H, ke - ks]
+    return np.abs(dq.w[t]) @ np.maximum(dots, 0.0)
+
+
 def dense_logits(dq: Dequantised, rows, W: int) -> np.ndarray:
     """Row-relative dense logits [len(rows), W]: column j holds key ks_t + j; -inf outside the
     window (P1 section 1: output [T, max_seqlen_k] fp32)."""

@@ -8,7 +8,7 @@ import torch
 import mqa_logits_top_amd as idx
 import oracle
 import synth
-from checks import logits_ok, topk_ok
+from checks import Windows, logits_ok, topk_ok
 
 pytestmark = pytest.mark.gpu
 
@@ -30,23 +30,28 @@ def _rows_windows(T, L, kind, seed=0):
 
 
 CASES = [
-    # (T, L, H, k_fmt, windows)
-    (37, 1500, 32, synth.K_FP8, "causal"),
-    (37, 1500, 64, synth.K_FP8, "causal"),
-    (29, 1333, 64, synth.K_MXFP4, "causal"),
-    (21, 1100, 32, synth.K_MXFP4, "random"),
-    (45, 2000, 64, synth.K_FP8, "random"),
+    # (T, L, H, k_fmt, windows, lower end of the head weights' U(w_lo, 1) range)
+    (37, 1500, 32, synth.K_FP8, "causal", 0.0),
+    (37, 1500, 64, synth.K_FP8, "causal", 0.0),
+    (29, 1333, 64, synth.K_MXFP4, "causal", 0.0),
+    (21, 1100, 32, synth.K_MXFP4, "random", 0.0),
+    (45, 2000, 64, synth.K_FP8, "random", 0.0),
+    # head weights of either sign (the weights may have any sign): logits of either sign,
+    # heads that subtract, keys whose score is exactly 0
+    (33, 1700, 32, synth.K_FP8, "causal", -0.5),
+    (27, 1400, 64, synth.K_MXFP4, "random", -1.0),
 ]
 
 
-@pytest.fixture(scope="module", params=CASES, ids=lambda c: f"T{c[0]}-L{c[1]}-H{c[2]}-f{c[3]}-{c[4]}")
+@pytest.fixture(scope="module", params=CASES, ids=lambda c: f"T{c[0]}-L{c[1]}-H{c[2]}-f{c[3]}-{c[4]}-w{c[5]}")
 def case(request):
-    T, L, H, fmt, win = request.param
+    T, L, H, fmt, win, w_lo = request.param
     ks, ke = _rows_windows(T, L, win, seed=T)
     p = synth.make_problem(T, L, H, k_fmt=fmt, seed=T + H, ks=ks, ke=ke,
-                           dup_rows=(L // 20 if fmt == synth.K_MXFP4 else 0))
+                           dup_rows=(L // 20 if fmt == synth.K_MXFP4 else 0), w_lo=w_lo)
     dq = oracle.Dequantised(p)
-    o = [oracle.row_logits(dq, t) for t in range(T)]
+    o = Windows([oracle.row_logits(dq, t) for t in range(T)],
+                [oracle.row_magnitude(dq, t) for t in range(T)])
     return p, dev(p), o
 
 
@@ -55,9 +60,11 @@ def test_dense_logits(case):
     W = max(p.W, 1)
     g = idx.idx_mqa_logits(d, W).cpu().numpy()
     ref = np.full((p.T, W), -np.inf)
+    mag = np.zeros((p.T, W))
     for t, v in enumerate(o):
         ref[t, :len(v)] = v
-    logits_ok(g, ref)
+        mag[t, :len(v)] = o.mag[t]
+    logits_ok(g, ref, mag=mag)
 
 
 def test_logits_block_rectangle(case):
@@ -70,7 +77,7 @@ def test_logits_block_rectangle(case):
         inw = np.zeros(nkeys, bool)
         if hi > lo:
             inw[lo - key0:hi - key0] = True
-            logits_ok(g[r, inw], o[t][lo - p.ks[t]:hi - p.ks[t]])
+            logits_ok(g[r, inw], o[t][lo - p.ks[t]:hi - p.ks[t]], mag=o.mag[t][lo - p.ks[t]:hi - p.ks[t]])
         assert np.isnan(g[r, ~inw]).all(), "wrote outside the window"
 
 

@@ -368,3 +368,48 @@ def test_ratio_windows_invariants():
                 assert np.array_equal(steps, (seen % r == 0).astype(int))
                 if lk_r[i] % r == 0:
                     assert ke[rows[-1]] == cu_c[i + 1]
+
+
+# ----------------------------------------------------------------- head-term size
+def test_magnitude_closed_form_and_sign_pins():
+    """oracle.row_magnitude = sum_h |w_h| ReLU(dot_h).  Pinned against: a hand-worked
+    one-hot case with a negative weight; |w| == w for non-negative weights (equal to the
+    logits bitwise); negating every weight negates the logits and keeps the sizes; the
+    sizes bound the logits (triangle inequality); splitting the weights by sign gives the
+    logits as (positive part) - (negative part) and the sizes as their sum."""
+    T, L, H, D = 1, 4, 2, 128
+    q = np.zeros((T, H, D), np.uint8)
+    q[0, :, 5] = [0x38, 0x40]                      # head 0: 1, head 1: 2
+    k = np.zeros((L, D), np.uint8)
+    k[:, 5] = [0x38, 0xB8, 0x40, 0x00]             # 1, -1, 2, 0
+    w = np.array([[0.5, -0.25]], np.float32)
+    p = synth.Problem(q=q, q_scale=np.ones((T, H), np.float32), k=k, k_scale=np.ones(L, np.float32), k_fmt=0,
+                      w=w, ks=np.array([0], np.int32), ke=np.array([L], np.int32))
+    dq = oracle.Dequantised(p)
+    # dots: head 0 -> [1, -1, 2, 0], head 1 -> [2, -2, 4, 0]
+    assert oracle.row_logits(dq, 0).tolist() == [0.5 - 0.5, 0.0, 1.0 - 1.0, 0.0]
+    assert oracle.row_magnitude(dq, 0).tolist() == [0.5 + 0.5, 0.0, 1.0 + 1.0, 0.0]
+
+    p = _small(T=3, L=300, H=8)
+    dq = oracle.Dequantised(p)
+    for t in range(p.T):
+        assert np.array_equal(oracle.row_magnitude(dq, t), oracle.row_logits(dq, t))   # w >= 0 here
+    pn = synth.Problem(**{**p.__dict__})
+    pn.w = -p.w
+    dqn = oracle.Dequantised(pn)
+    pm = synth.Problem(**{**p.__dict__})
+    sign = np.where(np.random.default_rng(2).random(p.w.shape) < 0.5, -1.0, 1.0).astype(np.float32)
+    pm.w = p.w * sign
+    dqm = oracle.Dequantised(pm)
+    pp, pq = synth.Problem(**{**p.__dict__}), synth.Problem(**{**p.__dict__})
+    pp.w = np.where(sign > 0, p.w, 0).astype(np.float32)
+    pq.w = np.where(sign < 0, p.w, 0).astype(np.float32)
+    dqp, dqq = oracle.Dequantised(pp), oracle.Dequantised(pq)
+    for t in range(p.T):
+        assert np.array_equal(oracle.row_logits(dqn, t), -oracle.row_logits(dq, t))
+        assert np.array_equal(oracle.row_magnitude(dqn, t), oracle.row_magnitude(dq, t))
+        m, v = oracle.row_magnitude(dqm, t), oracle.row_logits(dqm, t)
+        assert (m >= np.abs(v) - 1e-12 * m).all()
+        a, b = oracle.row_logits(dqp, t), oracle.row_logits(dqq, t)
+        np.testing.assert_allclose(v, a - b, rtol=1e-12, atol=1e-12 * m.max())
+        np.testing.assert_allclose(m, a + b, rtol=1e-12, atol=0)
