@@ -391,8 +391,10 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       floor_key = rlo;
     }
 
-    // ---- the segment's keys, in registers: key[c][j] is column S + 8192 c + 16 tid + j
+    // ---- the segment's keys, in registers: key[c][j] is column S + 8192 c + 16 tid + j;
+    // their count and range are taken as each chunk converts, while later chunks still load
     uint32_t key[NCH][VPT];
+    uint32_t seg_n = 0, seg_lo = 0xFFFFFFFFu, seg_hi = 0;
     {
       float raw[NCH][VPT];
       static_for<NCH>([&](auto c) __attribute__((always_inline)) {
@@ -423,29 +425,27 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
             if (!(inside && mj < a.mask_w && mrow[mj])) k = 0;
           }
           if (BLOCKS && !(inside && block_ok((int64_t)col + mshift))) k = 0;
-          key[c][j] = k > floor_key ? k : 0u;
+          k = k > floor_key ? k : 0u;
+          key[c][j] = k;
+          seg_n += k != 0u;
+          seg_lo = min(seg_lo, k != 0u ? k : 0xFFFFFFFFu);
+          seg_hi = max(seg_hi, k);
         });
       });
     }
 
-    // ---- sweep 1: size and key range of the union
+    // ---- size and key range of the union: the segment's part from the load, the running list's here
     uint32_t total = 0, umin = 0xFFFFFFFFu, umax = 0;
     {
-      uint32_t n = 0;
+      uint32_t n = seg_n;
+      umin = seg_lo;
+      umax = seg_hi;
       for (int p = tid; p < run_n; p += NTH) {
         const uint32_t k = run_key(p);
         ++n;
         umin = min(umin, k);
         umax = max(umax, k);
       }
-      static_for<NCH>([&](auto c) __attribute__((always_inline)) {
-        static_for<VPT>([&](auto j) __attribute__((always_inline)) {
-          const uint32_t k = key[c][j];
-          n += k != 0u;
-          umin = min(umin, k != 0u ? k : 0xFFFFFFFFu);
-          umax = max(umax, k);
-        });
-      });
       total = n;
       block_sum_minmax(sm, total, umin, umax, lane, wave);
     }
