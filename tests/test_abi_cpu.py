@@ -182,3 +182,13 @@ def test_refine_validation(lib):
     assert lib.idx_refine_topk(ctypes.byref(p), f, f, 600, 600, 64, 4, f, None, f, 4096, None) == 6   # pool
     assert lib.idx_refine_topk(ctypes.byref(p), f, f, 500, 600, 64, 1, f, None, f, 4096, None) == 2   # ld < Kc
     assert lib.idx_refine_topk(ctypes.byref(p), f, f, 600, 600, 64, 1, f, None, f, 100, None) == 5    # ws
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built HIP library every entry point raises; there is no fallback path."""
+    monkeypatch.setattr(idx, "_lib", None)
+    monkeypatch.setattr(idx, "LIB_PATH", str(tmp_path / "libidx.so"))
+    with pytest.raises(ImportError, match="not built"):
+        idx.load_library()
+    with pytest.raises(ImportError, match="not built"):
+        idx.idx_status_str(0)
