@@ -369,3 +369,39 @@ def test_edge_shapes():
         for t, v in enumerate(o):
             ref[t, :len(v)] = v
         logits_ok(g, ref)
+
+
+@pytest.mark.parametrize("fmt,H", [(synth.K_FP8, 32), (synth.K_MXFP4, 64)])
+def test_scale_and_spread_scales(fmt, H):
+    """The extra positive scalar `scale` (not a power of two), per-(row, head) q scales over
+    six binades and key scales over ten (fp8: k_scale; MXFP4: E8M0 codes shifted per key):
+    dense logits and the fused top-K against the oracle, the exact boundary's overflow
+    count at zero, fused == dense + refine bitwise."""
+    T, L, K = 24, 2300, 96
+    ks, ke = synth.causal_windows(T, L)
+    p = synth.make_problem(T, L, H, k_fmt=fmt, seed=41, ks=ks, ke=ke, scale=0.37)
+    rng = np.random.default_rng(41)
+    p.q_scale = (p.q_scale * np.exp2(rng.integers(-3, 4, p.q_scale.shape))).astype(np.float32)
+    if fmt == synth.K_FP8:
+        p.k_scale = (p.k_scale * np.exp2(rng.integers(-5, 6, p.k_scale.shape))).astype(np.float32)
+    else:
+        shift = rng.integers(-5, 6, (p.L, 1))
+        p.k_scale = np.clip(p.k_scale.astype(np.int64) + shift, 1, 254).astype(np.uint8)
+    dq = oracle.Dequantised(p)
+    o = Windows([oracle.row_logits(dq, t) for t in range(T)], [oracle.row_magnitude(dq, t) for t in range(T)])
+    d = dev(p)
+    W = max(p.W, 1)
+    g = idx.idx_mqa_logits(d, W).cpu().numpy()
+    ref = np.full((T, W), -np.inf)
+    for t, v in enumerate(o):
+        ref[t, :len(v)] = v
+    logits_ok(g, ref)
+    ws = torch.empty(idx.idx_workspace_size(idx.IDX_OP_LOGITS_TOPK_FUSED, d, K=K, block_k=512), dtype=torch.uint8,
+                     device="cuda")
+    fi, fv = idx.idx_logits_topk_fused(d, K, block_k=512, ws=ws)
+    assert idx.overflow_count(ws) == 0
+    topk_ok(fi.cpu().numpy(), fv.cpu().numpy(), o, p.ks, K)
+    lg = idx.idx_mqa_logits(d, W)
+    ci, cv = idx.idx_topk(lg, d.ks, d.ke, idx.candidate_capacity(K))
+    di, dv = idx.idx_refine_topk(d, ci, cv, K)
+    assert torch.equal(di, fi) and torch.equal(dv.view(torch.int32), fv.view(torch.int32))
