@@ -101,8 +101,8 @@ static_assert(OVL >= NB + 64 + RCAP && OVL * 4 >= 2 * 64 * 4 * 8, "overlay buffe
 struct Smem {
   uint8_t state[KC_MAX];       // per candidate slot: 0 out, 1 certain, 2 band, 3 band and taken
   int16_t band[KC_MAX];        // band entry -> candidate slot
-  uint32_t bexact[KC_MAX];     // band entry -> key of its exact score (pooled: max over its keys)
-  int32_t bid[KC_MAX];         // band entry -> candidate id
+  alignas(16) uint32_t bexact[KC_MAX];  // band entry -> key of its exact score (pooled: max over its keys)
+  alignas(16) int32_t bid[KC_MAX];      // band entry -> candidate id
   // overlay: the selection's histogram and ranking list; during the band scores the second
   // chunk group's dot partials (32 heads); at the end the taken band entries' exact scores by slot
   __attribute__((aligned(16))) uint32_t ovl[OVL];
@@ -462,15 +462,24 @@ __global__ __launch_bounds__(NTH) void refine_kernel(RefineArgs a) {
       }
     }
     __syncthreads();
-    // ---- order the band by (exact desc, id asc) and take need_b of it
+    // ---- order the band by (exact desc, id asc) and take need_b of it.  Entries are read
+    // four at a time and compared without branches, so the loads of many entries are in
+    // flight together (a short-circuit comparison became a branch per entry, each waiting
+    // for its own LDS read: ~270 cycles per entry).
     for (int j = tid; j < nb; j += NTH) {
       const uint32_t kj = sm.bexact[j];
       const int idj = sm.bid[j];
       int rank = 0;
-#pragma unroll 8
-      for (int m = 0; m < nb; ++m) {
-        const uint32_t km = sm.bexact[m];
-        rank += km > kj || (km == kj && sm.bid[m] < idj);
+      const int nb4 = (nb + 3) >> 2;   // 4 nb4 <= KC_MAX: reads stay inside the arrays
+#pragma unroll 4
+      for (int m4 = 0; m4 < nb4; ++m4) {
+        const uint4 k4 = *(const uint4 *)&sm.bexact[4 * m4];
+        const int4 i4 = *(const int4 *)&sm.bid[4 * m4];
+        const uint32_t km[4] = {k4.x, k4.y, k4.z, k4.w};
+        const int im[4] = {i4.x, i4.y, i4.z, i4.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          rank += (int)(4 * m4 + u < nb) & ((int)(km[u] > kj) | ((int)(km[u] == kj) & (int)(im[u] < idj)));
       }
       if (rank < need_b) sm.state[sm.band[j]] = 3;
     }
