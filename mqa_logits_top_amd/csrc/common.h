@@ -21,9 +21,8 @@ __device__ __forceinline__ void static_for(F &&f) {
 // Order-preserving map fp32 -> uint32 (larger key <=> larger value; -0 ranks as +0).
 // Key 0 is never produced by a real number below NaN patterns and serves as "empty".
 __device__ __forceinline__ uint32_t fkey(float v) {
-  uint32_t u = __float_as_uint(v);
-  if (u == 0x80000000u) u = 0;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(v + 0.0f);   // -0 + 0 = +0 (round to nearest): one key for both zeros
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 __device__ __forceinline__ float kval(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);

@@ -414,24 +414,34 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
           });
         }
       });
+      uint32_t seg_lm1 = 0xFFFFFFFFu;   // smallest nonzero key minus 1 (a zero key wraps to the top)
+      auto keep = [&](uint32_t &slot, uint32_t k) __attribute__((always_inline)) {
+        k = k > floor_key ? k : 0u;
+        slot = k;
+        seg_n += k != 0u;
+        seg_lm1 = min(seg_lm1, k - 1u);
+        seg_hi = max(seg_hi, k);
+      };
       static_for<NCH>([&](auto c) __attribute__((always_inline)) {
         const int cb = S + c * SPAN + tid * VPT;
-        static_for<VPT>([&](auto j) __attribute__((always_inline)) {
-          const int col = cb + j;
-          const bool inside = col >= s0 && col < s1;
-          uint32_t k = inside ? fkey(raw[c][j]) : 0u;
-          if (mrow) {
-            const int64_t mj = (int64_t)col + mshift;
-            if (!(inside && mj < a.mask_w && mrow[mj])) k = 0;
-          }
-          if (BLOCKS && !(inside && block_ok((int64_t)col + mshift))) k = 0;
-          k = k > floor_key ? k : 0u;
-          key[c][j] = k;
-          seg_n += k != 0u;
-          seg_lo = min(seg_lo, k != 0u ? k : 0xFFFFFFFFu);
-          seg_hi = max(seg_hi, k);
-        });
+        if (cb >= s0 && cb + VPT <= s1 && !mrow && !BLOCKS) {
+          // the whole chunk lies in the window and no consumer filter applies: no per-column tests
+          static_for<VPT>([&](auto j) __attribute__((always_inline)) { keep(key[c][j], fkey(raw[c][j])); });
+        } else {
+          static_for<VPT>([&](auto j) __attribute__((always_inline)) {
+            const int col = cb + j;
+            const bool inside = col >= s0 && col < s1;
+            uint32_t k = inside ? fkey(raw[c][j]) : 0u;
+            if (mrow) {
+              const int64_t mj = (int64_t)col + mshift;
+              if (!(inside && mj < a.mask_w && mrow[mj])) k = 0;
+            }
+            if (BLOCKS && !(inside && block_ok((int64_t)col + mshift))) k = 0;
+            keep(key[c][j], k);
+          });
+        }
       });
+      seg_lo = seg_lm1 == 0xFFFFFFFFu ? 0xFFFFFFFFu : seg_lm1 + 1u;
     }
 
     // ---- size and key range of the union: the segment's part from the load, the running list's here
