@@ -405,3 +405,41 @@ def test_scale_and_spread_scales(fmt, H):
     ci, cv = idx.idx_topk(lg, d.ks, d.ke, idx.candidate_capacity(K))
     di, dv = idx.idx_refine_topk(d, ci, cv, K)
     assert torch.equal(di, fi) and torch.equal(dv.view(torch.int32), fv.view(torch.int32))
+
+
+def _long_rows(W):
+    """Rows of 20000 columns (more than four times the selection's 4608-entry LDS candidate
+    list, so the register histogram narrows over several levels), with values that differ
+    by column position within each thread's 16 columns, all-equal rows, heavy ties, signed
+    zeros and tiny negatives."""
+    rng = np.random.default_rng(17)
+    col = np.arange(W)
+    sampled = (col % 16) < 4
+    rows = [
+        rng.normal(size=W),                                          # i.i.d.
+        np.where(sampled, 1000.0 + rng.normal(size=W), rng.normal(size=W)),   # large in 4 of every 16 columns
+        np.where(sampled, rng.normal(size=W), 1000.0 + rng.normal(size=W)),   # large in 12 of every 16 columns
+        np.full(W, 2.5),                                             # all equal
+        np.round(rng.normal(size=W), 1),                             # heavy ties
+        np.where(rng.random(W) < 0.5, 0.0, -0.0),                    # signed zeros
+        -np.abs(rng.normal(size=W)) * 1e-30,                         # tiny negatives
+    ]
+    return np.stack(rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("K,block_k", [(2000, 32768), (2560, 32768), (512, 16384), (100, 32768)])
+def test_topk_selection_exact_long_rows(K, block_k):
+    W = 20000
+    vals = _long_rows(W)
+    T = vals.shape[0]
+    ks = np.zeros(T, np.int32)
+    ke = np.full(T, W, np.int32)
+    ke[4] = W - 7                       # a ragged window end inside a sampled group
+    g = torch.from_numpy(np.ascontiguousarray(vals)).cuda()
+    gi, gv = idx.idx_topk(g, torch.from_numpy(ks).cuda(), torch.from_numpy(ke).cuda(), K, block_k=block_k)
+    gi, gv = gi.cpu().numpy(), gv.cpu().numpy()
+    for t in range(T):
+        win = vals[t, :ke[t] - ks[t]].astype(np.float64)
+        oi, ov = oracle.topk_row(win, int(ks[t]), K)
+        assert np.array_equal(gi[t], oi), f"row {t}"
+        assert np.array_equal(gv[t], ov.astype(np.float32)) or np.array_equal(np.abs(gv[t]), np.abs(ov)), f"row {t}"
