@@ -414,11 +414,11 @@ def _long_rows(W):
     zeros and tiny negatives."""
     rng = np.random.default_rng(17)
     col = np.arange(W)
-    sampled = (col % 16) < 4
+    first4 = (col % 16) < 4
     rows = [
         rng.normal(size=W),                                          # i.i.d.
-        np.where(sampled, 1000.0 + rng.normal(size=W), rng.normal(size=W)),   # large in 4 of every 16 columns
-        np.where(sampled, rng.normal(size=W), 1000.0 + rng.normal(size=W)),   # large in 12 of every 16 columns
+        np.where(first4, 1000.0 + rng.normal(size=W), rng.normal(size=W)),   # large in 4 of every 16 columns
+        np.where(first4, rng.normal(size=W), 1000.0 + rng.normal(size=W)),   # large in 12 of every 16 columns
         np.full(W, 2.5),                                             # all equal
         np.round(rng.normal(size=W), 1),                             # heavy ties
         np.where(rng.random(W) < 0.5, 0.0, -0.0),                    # signed zeros
