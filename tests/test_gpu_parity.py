@@ -434,7 +434,7 @@ def test_topk_selection_exact_long_rows(K, block_k):
     T = vals.shape[0]
     ks = np.zeros(T, np.int32)
     ke = np.full(T, W, np.int32)
-    ke[4] = W - 7                       # a ragged window end inside a sampled group
+    ke[4] = W - 7                       # a ragged window end inside a 16-column group
     g = torch.from_numpy(np.ascontiguousarray(vals)).cuda()
     gi, gv = idx.idx_topk(g, torch.from_numpy(ks).cuda(), torch.from_numpy(ke).cuda(), K, block_k=block_k)
     gi, gv = gi.cpu().numpy(), gv.cpu().numpy()
