@@ -301,6 +301,72 @@ def traffic_summary(fetch_dir, write_dir):
           f"(kernel source hash {rec['kernel_source_hash']}).")
 
 
+def fused_line(p, d, K, block_k, row_chunk, reps, stream):
+    """One workload's fused call, timed with HIP events on `stream` after a warm-up call."""
+    ws = torch.empty(idx.idx_workspace_size(idx.IDX_OP_LOGITS_TOPK_FUSED, d, K=K, block_k=block_k, row_chunk=row_chunk),
+                     dtype=torch.uint8, device="cuda")
+    oi = torch.empty((p.T, K), dtype=torch.int32, device="cuda")
+    ov = torch.empty((p.T, K), dtype=torch.float32, device="cuda")
+    run = lambda: idx.idx_logits_topk_fused(d, K, block_k=block_k, row_chunk=row_chunk, out_idx=oi, out_val=ov,
+                                            ws=ws, stream=stream)
+    run()
+    ms = float(np.median(time_events(run, reps, stream)))
+    flops = 2 * p.H * p.D * p.pairs
+    assert idx.overflow_count(ws) == 0
+    line = {"T": p.T, "L": p.L, "H": p.H, "K": K, "block_k": block_k, "row_chunk": row_chunk, "pairs": int(p.pairs),
+            "ms": ms, "pairs_per_s": p.pairs / (ms * 1e-3), "tflops": flops / (ms * 1e-3) / 1e12,
+            "fp8_peak_frac": flops / (ms * 1e-3) / FP8_PEAK, "peak_transient_bytes": int(ws.numel())}
+    return line, oi, ov
+
+
+def workload_lines(dev, stream):
+    """The fused indexer on the tiny, long-context and ragged workloads (glm_chunk is the headline line,
+    dsv4_mxfp4 is timed above), and on the long-context workload the row-chunked dense comparator under a
+    2 GiB fp32 logits budget: logits of as many rows as fit, their top-(K + 512), then the exact boundary."""
+    out = {}
+    for name, row_chunk, reps in (("tiny", 0, 10), ("long_ctx", 4096, 3), ("ragged_cand", 4096, 3)):
+        p = synth.make_config(name)
+        d = idx.Inputs.from_host(p, device=dev)
+        K, Bk = p.meta["K"], p.meta["block_k"]
+        line, oi, ov = fused_line(p, d, K, Bk, row_chunk, reps, stream)
+        out[name] = line
+        log(f"[bench] {name}: fused {line['ms']:.3f} ms -> {line['pairs_per_s']:.3e} pairs/s, "
+            f"{line['tflops']:.0f} TFLOP/s ({100 * line['fp8_peak_frac']:.1f}% of fp8 peak), "
+            f"workspace {line['peak_transient_bytes'] / 2**20:.0f} MiB")
+        if name == "long_ctx":
+            W = p.W
+            chunk = (2 << 30) // (4 * W)
+            buf = torch.empty((chunk, W), dtype=torch.float32, device=dev)
+            Kc = idx.candidate_capacity(K)
+            ci = torch.empty((p.T, Kc), dtype=torch.int32, device=dev)
+            cv = torch.empty((p.T, Kc), dtype=torch.float32, device=dev)
+            rws = torch.empty(idx.REFINE_WS, dtype=torch.uint8, device=dev)
+            di = torch.empty((p.T, K), dtype=torch.int32, device=dev)
+            dv = torch.empty((p.T, K), dtype=torch.float32, device=dev)
+
+            def dense():
+                for r0 in range(0, p.T, chunk):
+                    nr = min(chunk, p.T - r0)
+                    sub = idx.Inputs(q=d.q[r0:r0 + nr], q_scale=d.q_scale[r0:r0 + nr], k=d.k, k_scale=d.k_scale,
+                                     w=d.w[r0:r0 + nr], ks=d.ks[r0:r0 + nr], ke=d.ke[r0:r0 + nr], k_fmt=d.k_fmt)
+                    lg = idx.idx_mqa_logits(sub, W, out=buf[:nr], stream=stream)
+                    idx.idx_topk(lg, sub.ks, sub.ke, Kc, out_idx=ci[r0:r0 + nr], out_val=cv[r0:r0 + nr],
+                                 stream=stream)
+                idx.idx_refine_topk(d, ci, cv, K, out_idx=di, out_val=dv, ws=rws, stream=stream)
+
+            ms = float(np.median(time_events(dense, 1, stream)))
+            assert torch.equal(di, oi) and torch.equal(dv.view(torch.int32), ov.view(torch.int32))
+            out[name]["dense_rowchunked"] = {"rows_per_chunk": int(chunk), "chunks": -(-p.T // chunk), "ms": ms,
+                                             "pairs_per_s": p.pairs / (ms * 1e-3),
+                                             "peak_transient_bytes": int(buf.numel() * 4 + 8 * p.T * Kc)}
+            log(f"[bench] long_ctx: row-chunked dense comparator ({chunk} rows x {W} fp32 per chunk) {ms:.1f} ms, "
+                f"equal to the fused result")
+            del buf, ci, cv, rws, di, dv
+        del d, oi, ov
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -482,6 +548,7 @@ def main():
         log(f"[bench] ragged candidates: all rows {np.median(cand_all):.2f} ms, tail rows {np.median(cand_tail):.2f} ms;"
             f" consumer: byte mask {np.median(cons_mask):.2f} ms, block ids {np.median(cons_blocks):.2f} ms")
         del d5, d5t, d5c, mask5, mask5t, ws5, wsc
+        extra["workloads"] = workload_lines(dev, stream)
         out["extra"] = extra
 
     if not args.no_cpu:

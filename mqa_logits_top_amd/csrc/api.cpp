@@ -154,12 +154,31 @@ size_t gather_ws(int32_t R, int32_t H, int32_t D) {
   return round_up_sz((size_t)R * H * D, 256) + 2 * round_up_sz((size_t)R * H * 4, 256) +
          2 * round_up_sz((size_t)R * 4, 256);
 }
+// Window flags of the scoring launches (idx::WindowFlags), a fixed region.
+constexpr size_t FLAGS_WS = (size_t)idx::MAX_WINDOW_FLAGS * 4;
 size_t fused_ws(int32_t Tc, int32_t Bk, int32_t K) {
-  return refine_ws(Tc, cand_cap(K)) + round_up_sz((size_t)Tc * pitch(Bk) * 4, 256) + slab_ws(Tc, Bk);
+  return refine_ws(Tc, cand_cap(K)) + round_up_sz((size_t)Tc * pitch(Bk) * 4, 256) + slab_ws(Tc, Bk) + FLAGS_WS;
 }
-size_t cand_ws(int32_t Tc, int32_t pooled_cols, int32_t n_blocks) {
+size_t cand_ws(int32_t Tc, int32_t pooled_cols, int32_t n_blocks, bool fused) {
   return refine_ws(Tc, cand_cap(n_blocks)) + round_up_sz((size_t)Tc * pitch(pooled_cols) * 4, 256) +
-         round_up_sz((size_t)Tc * n_blocks * 4, 256);
+         round_up_sz((size_t)Tc * n_blocks * 4, 256) + (fused ? FLAGS_WS : 0);
+}
+// The flags of a call whose row chunks of Tc rows meet key launches of LB keys (nullptr in
+// `flags` when there would be more than the region holds: the launches then stay by key split).
+idx::WindowFlags window_flags(const idx_problem *p, int32_t Tc, int32_t LB, uint32_t *region) {
+  idx::WindowFlags f{};
+  f.ks = p->ks;
+  f.ke = p->ke;
+  f.T = p->T;
+  f.Tc = Tc;
+  f.LB = LB;
+  f.nlaunch = p->L > 0 ? (p->L + LB - 1) / LB : 0;
+  const int64_t n = (int64_t)((p->T + Tc - 1) / Tc) * f.nlaunch;
+  f.flags = n > 0 && n <= idx::MAX_WINDOW_FLAGS ? region : nullptr;
+  return f;
+}
+const uint32_t *launch_flag(const idx::WindowFlags &f, int32_t r0, int32_t kb) {
+  return f.flags ? f.flags + (int64_t)(r0 / f.Tc) * f.nlaunch + kb / f.LB : nullptr;
 }
 
 struct RefineWs {
@@ -251,14 +270,14 @@ idx_status idx_workspace_size(int32_t op, const idx_problem *p, int32_t K, int32
       if (n_blocks < 1 || n_blocks > MAX_K) return IDX_E_PARAM;
       const int32_t Bk = eff_block(p, block_k);
       if (check_block(Bk) != IDX_OK) return IDX_E_PARAM;
-      *bytes = cand_ws(Tc, Bk / pool, n_blocks);
+      *bytes = cand_ws(Tc, Bk / pool, n_blocks, true);
       return IDX_OK;
     }
     case IDX_OP_BLOCK_CANDIDATES_DENSE: {
       if (pool != 8) return IDX_E_UNSUPPORTED;
       if (n_blocks < 1 || n_blocks > MAX_K) return IDX_E_PARAM;
       if (W < 0 || W > MAX_W) return IDX_E_SHAPE;
-      *bytes = cand_ws(Tc, (W + pool - 1) / pool, n_blocks);
+      *bytes = cand_ws(Tc, (W + pool - 1) / pool, n_blocks, false);
       return IDX_OK;
     }
     default: return IDX_E_PARAM;
@@ -386,8 +405,9 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
   uint32_t *ovf = cv.take<uint32_t>((size_t)Tc / 8 + 1);   // per scoring row block (>= 8 rows)
   uint32_t *ccnt = cv.take<uint32_t>((size_t)Tc * nslab_max * idx::CAND_PARTS);
   uint32_t *slab = cv.take<uint32_t>((size_t)Tc * nslab_max * CAPS * 2);
+  const idx::WindowFlags wf = window_flags(p, Tc, LB, cv.take<uint32_t>(idx::MAX_WINDOW_FLAGS));
   if ((st = launched(idx::launch_key_bound((const uint8_t *)p->k, (const uint8_t *)p->k_scale, p->k_fmt, p->L,
-                                           rw.kpart, rw.overflow, s))))
+                                           rw.kpart, rw.overflow, &wf, s))))
     return st;
   for (int32_t r0 = 0; r0 < p->T; r0 += Tc) {
     const int32_t nr = std::min(Tc, p->T - r0);
@@ -401,6 +421,7 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
       int32_t nslab = 0;
       if (nk > 0) {
         idx::LogitsArgs a = logits_args(p, r0, nr, kb, kb + nk, scratch, sld, nk);
+        a.by_row = launch_flag(wf, r0, kb);
         slabs = kb >= slab_from(p) * LB && a.nsplit <= nslab_max && (int64_t)nr * a.nsplit * CAPS * 8 < INT32_MAX;
         nslab = a.nsplit;
         if (slabs && !mask && !blocks) {
@@ -511,7 +532,7 @@ idx_status idx_refine_topk(const idx_problem *p, const int32_t *cand_idx, const 
   rw.cidx = const_cast<int32_t *>(cand_idx);
   rw.cval = const_cast<float *>(cand_val);
   if ((st = launched(idx::launch_key_bound((const uint8_t *)p->k, (const uint8_t *)p->k_scale, p->k_fmt, p->L,
-                                           rw.kpart, rw.overflow, s))))
+                                           rw.kpart, rw.overflow, nullptr, s))))
     return st;
   idx::RefineArgs r = refine_args(p, rw, 0, p->T, Kc, K, pool, out_idx, out_val);
   r.ld_cand = ld_cand;
@@ -535,7 +556,7 @@ idx_status idx_block_candidates(const idx_problem *p, const float *logits, int64
   const int32_t Bk = eff_block(p, block_k);
   if (!logits && (st = check_block(Bk))) return st;
   const int32_t pooled_cols = logits ? (W + pool - 1) / pool : Bk / pool;
-  const size_t need = cand_ws(Tc, pooled_cols, n_blocks);
+  const size_t need = cand_ws(Tc, pooled_cols, n_blocks, !logits);
   if (p->T == 0) return IDX_OK;
   if (!ws) return IDX_E_NULL;
   if (ws_bytes < need) return IDX_E_WORKSPACE;
@@ -547,9 +568,11 @@ idx_status idx_block_candidates(const idx_problem *p, const float *logits, int64
   const int32_t pld = pitch(pooled_cols);
   float *pooled = cv.take<float>((size_t)Tc * pld);
   int32_t *kept = cv.take<int32_t>((size_t)Tc * n_blocks);
+  idx::WindowFlags wf{};
   if (!logits) {
+    wf = window_flags(p, Tc, Bk, cv.take<uint32_t>(idx::MAX_WINDOW_FLAGS));
     if ((st = launched(idx::launch_key_bound((const uint8_t *)p->k, (const uint8_t *)p->k_scale, p->k_fmt, p->L,
-                                             rw.kpart, rw.overflow, s))))
+                                             rw.kpart, rw.overflow, &wf, s))))
       return st;
   }
   for (int32_t r0 = 0; r0 < p->T; r0 += Tc) {
@@ -586,6 +609,7 @@ idx_status idx_block_candidates(const idx_problem *p, const float *logits, int64
         const int32_t nk = std::min(Bk, p->L - kb);
         if (nk > 0) {
           idx::LogitsArgs a = logits_args(p, r0, nr, kb, kb + nk, pooled, pld, (nk + pool - 1) / pool);
+          a.by_row = launch_flag(wf, r0, kb);
           if ((st = launched(idx::launch_logits(a, p->k_fmt, p->H, idx::STORE_POOL8, s)))) return st;
         }
         b.vals = pooled;

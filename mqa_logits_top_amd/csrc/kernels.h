@@ -49,6 +49,12 @@ struct LogitsArgs {
   // nonzero (nullable: all)
   const uint32_t *only_flagged;
   int32_t caps;
+  // Workgroup -> XCD layout (nullable: by key split).  By key split, each split's workgroups
+  // share an XCD, so its keys stay in one L2 (rows whose windows span the keys).  By row block
+  // (nonzero word here), each row block's workgroups share an XCD; a launch whose rows each see
+  // only a small part of the keys (a ragged batch of short requests) then spreads its active
+  // workgroups over every XCD instead of the few that own the splits those windows touch.
+  const uint32_t *by_row;
 };
 
 hipError_t launch_logits(const LogitsArgs &a, int k_fmt, int H, int mode, hipStream_t s);
@@ -130,8 +136,18 @@ struct RefineArgs {
   int32_t *out_slot;
 };
 int key_bound_parts(int L);
+// Window coverage of the scoring launches of a row-chunked, key-blocked call: for row chunk c
+// (rows [c Tc, c Tc + Tc)) and key launch l (keys [l LB, l LB + LB)), flags[c * nlaunch + l] = 1
+// when the rows' windows cover less than half of that rectangle (the launch then lays its
+// workgroups out by row block), else 0.
+struct WindowFlags {
+  const int32_t *ks, *ke;
+  int32_t T, Tc, LB, nlaunch;
+  uint32_t *flags;
+};
+constexpr int32_t MAX_WINDOW_FLAGS = 16384;
 hipError_t launch_key_bound(const uint8_t *k, const uint8_t *k_scale, int k_fmt, int L, float *part,
-                            uint32_t *overflow, hipStream_t s);
+                            uint32_t *overflow, const WindowFlags *wf, hipStream_t s);
 hipError_t launch_refine(const RefineArgs &a, hipStream_t s);
 
 // Dense-logits helpers

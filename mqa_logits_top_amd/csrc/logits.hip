@@ -38,10 +38,15 @@
 // on the bits, and MFMA results land in VGPRs (built with VGPR-form MFMA), so
 // the epilogue costs 2 VALU ops per (t, h, s).
 //
-// Grid: (row blocks of RPW = 16 rows) x (nsplit key splits).  Workgroup b
-// takes split b % nsplit, row block b / nsplit; when nsplit is a multiple of
-// 8 every split's workgroups land on one XCD (round-robin dispatch), so each
-// XCD's L2 only ever holds 1/8 of the keys.
+// Grid: (row blocks of RPW rows) x (nsplit key splits), in one of two layouts
+// (workgroup b runs on XCD b % 8, round-robin dispatch).  By key split (the
+// default): workgroup b takes split b % nsplit, row block b / nsplit; with nsplit
+// a multiple of 8 every split's workgroups land on one XCD, so each XCD's L2 only
+// ever holds 1/8 of the keys.  By row block, when the rows' windows cover less than
+// half of the launch's keys (a per-launch flag computed on the device from the
+// windows): row blocks == b (mod 8) run on XCD b % 8 with all their splits, so a
+// ragged batch of short requests, whose active items all sit in a few splits,
+// still spreads over every XCD.
 #include "kernels.h"
 
 #include <algorithm>
@@ -148,8 +153,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((MODE =
       part = t % nparts;
     }
   }
-  const int split_i = item % a.nsplit;
-  const int rb = item / a.nsplit;
+  // Items are (row block, key split) pairs.  By key split: item = rb * nsplit + split, so
+  // workgroup b (XCD b % 8) takes splits == b (mod 8).  By row block: items run row block
+  // fastest within groups of 8, item = (group * nsplit + split) * 8 + rb % 8, so workgroup b
+  // takes row blocks == b (mod 8).  Row blocks are padded to whole groups of 8.
+  int split_i, rb;
+  if (a.by_row && *a.by_row != 0u) {   // uniform
+    const int grp = item / (8 * a.nsplit), rem8 = item % (8 * a.nsplit);
+    split_i = rem8 >> 3;
+    rb = grp * 8 + (rem8 & 7);
+  } else {
+    split_i = item % a.nsplit;
+    rb = item / a.nsplit;
+  }
+  if (rb * RPW >= a.nrows) return;   // padding (uniform)
   if (MODE == STORE_BLOCK && a.only_flagged && a.only_flagged[rb] == 0) return;   // uniform
   const int r_begin = a.row0 + rb * RPW;
   const int r_end = min(r_begin + RPW, a.row0 + a.nrows);
@@ -434,7 +451,7 @@ hipError_t launch3(const LogitsArgs &a0, hipStream_t s) {
   constexpr int RPW = NW * (128 / H);
   auto kern = logits_kernel<KF, H, MODE, NW>;
   const int nrb = (a0.nrows + RPW - 1) / RPW;
-  const int64_t items = (int64_t)nrb * a0.nsplit;
+  const int64_t items = (int64_t)((nrb + 7) / 8) * 8 * a0.nsplit;   // row blocks padded to whole groups of 8
   if (items <= 0) return hipSuccess;
   // Whole items fill as many complete waves of resident workgroups as they can; the
   // remainder is cut into parts so that the last wave spans the machine as well.

@@ -532,13 +532,39 @@ __global__ __launch_bounds__(NTH) void refine_kernel(RefineArgs a) {
   }
 }
 
-// Largest |k| over all key rows: per-workgroup partial maxima.
+// Window coverage of one (row chunk, key launch) rectangle: flag 1 when the rows' windows
+// cover less than half of it (see WindowFlags).
+__device__ void window_flag(const WindowFlags wf, int L, int f) {
+  __shared__ double wred[4];
+  const int c = f / wf.nlaunch, l = f % wf.nlaunch;
+  const int r0 = c * wf.Tc, r1 = min(wf.T, r0 + wf.Tc);
+  const int klo = l * wf.LB, khi = min(L, klo + wf.LB);
+  double sum = 0.0;
+  for (int r = r0 + (int)threadIdx.x; r < r1; r += 256) {
+    const int lo = max(max(wf.ks[r], 0), klo), hi = min(min(wf.ke[r], L), khi);
+    sum += (double)max(hi - lo, 0);
+  }
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+  if ((threadIdx.x & 63) == 0) wred[threadIdx.x >> 6] = sum;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double tot = (wred[0] + wred[1]) + (wred[2] + wred[3]);
+    wf.flags[f] = 2.0 * tot < (double)(r1 - r0) * (double)(khi - klo) ? 1u : 0u;
+  }
+}
+
+// Largest |k| over all key rows: per-workgroup partial maxima (workgroups [0, np)); the
+// workgroups after them compute the window flags, one each.
 __global__ __launch_bounds__(256) void key_bound_kernel(const uint8_t *k, const uint8_t *k_scale, int k_fmt, int L,
-                                                        float *part, uint32_t *overflow) {
+                                                        float *part, uint32_t *overflow, int np, WindowFlags wf) {
   __shared__ float red[4];
+  if ((int)blockIdx.x >= np) {   // uniform
+    window_flag(wf, L, (int)blockIdx.x - np);
+    return;
+  }
   if (blockIdx.x == 0 && threadIdx.x == 0 && overflow) *overflow = 0;  // runs before the refinement in stream order
   float m = 0.f;
-  for (int s = blockIdx.x * 256 + threadIdx.x; s < L; s += gridDim.x * 256) {
+  for (int s = blockIdx.x * 256 + threadIdx.x; s < L; s += np * 256) {
     if (k_fmt == 0) {
       const uint4 *row = (const uint4 *)(k + (int64_t)s * 128);
       uint32_t bm = 0;
@@ -579,9 +605,16 @@ __global__ __launch_bounds__(256) void key_bound_kernel(const uint8_t *k, const 
 int key_bound_parts(int L) { return L <= 0 ? 1 : min(256, (L + 255) / 256); }
 
 hipError_t launch_key_bound(const uint8_t *k, const uint8_t *k_scale, int k_fmt, int L, float *part,
-                            uint32_t *overflow, hipStream_t s) {
+                            uint32_t *overflow, const WindowFlags *wf, hipStream_t s) {
   const int np = key_bound_parts(L);
-  hipLaunchKernelGGL(key_bound_kernel, dim3(np), dim3(256), 0, s, k, k_scale, k_fmt, L, part, overflow);
+  WindowFlags w{};
+  int nf = 0;
+  if (wf && wf->flags && wf->Tc > 0 && wf->LB > 0 && wf->nlaunch > 0) {
+    nf = ((wf->T + wf->Tc - 1) / wf->Tc) * wf->nlaunch;
+    if (nf > MAX_WINDOW_FLAGS) nf = 0;   // callers pass no flags to their launches then
+    else w = *wf;
+  }
+  hipLaunchKernelGGL(key_bound_kernel, dim3(np + nf), dim3(256), 0, s, k, k_scale, k_fmt, L, part, overflow, np, w);
   return hipGetLastError();
 }
 

@@ -155,17 +155,18 @@ def test_workspace_sizes(lib):
     # key blocks are scored in pairs: 65536 keys per launch, split 16 ways
     # thresholds, overflow flags, count words (16 splits x 4 parts), (value, id) pairs (16 slabs of 512)
     slab = lambda Tc: _r(Tc * 4) + _r((Tc // 8 + 1) * 4) + _r(Tc * 16 * 4 * 4) + _r(Tc * 16 * 512 * 8)
-    assert n.value == head + 2 * _r(2048 * kc(2048) * 4) + 2048 * (65536 + 64) * 4 + slab(2048)
+    flags = 16384 * 4   # window flags of the scoring launches, a fixed region
+    assert n.value == head + 2 * _r(2048 * kc(2048) * 4) + 2048 * (65536 + 64) * 4 + slab(2048) + flags
     # the row chunk bounds the workspace; the number of keys does not enter
     p2 = _problem(T=16384, L=487936)
     assert lib.idx_workspace_size(2, ctypes.byref(p2), 512, 32768, 4096, 0, 0, 0, ctypes.byref(n)) == 0
-    assert n.value == head + 2 * _r(4096 * kc(512) * 4) + 4096 * (65536 + 64) * 4 + slab(4096)
+    assert n.value == head + 2 * _r(4096 * kc(512) * 4) + 4096 * (65536 + 64) * 4 + slab(4096) + flags
     p3 = _problem(T=16384, L=65536)
     m = ctypes.c_size_t()
     assert lib.idx_workspace_size(2, ctypes.byref(p3), 512, 32768, 4096, 0, 0, 0, ctypes.byref(m)) == 0
     assert m.value == n.value
     assert lib.idx_workspace_size(3, ctypes.byref(p), 0, 32768, 0, 8, 2048, 0, ctypes.byref(n)) == 0
-    assert n.value == head + 2 * _r(2048 * kc(2048) * 4) + 2048 * (4096 + 64) * 4 + 2048 * 2048 * 4
+    assert n.value == head + 2 * _r(2048 * kc(2048) * 4) + 2048 * (4096 + 64) * 4 + 2048 * 2048 * 4 + flags
     assert lib.idx_workspace_size(4, ctypes.byref(p), 0, 0, 1024, 8, 2048, 65536, ctypes.byref(n)) == 0
     assert n.value == head + 2 * _r(1024 * kc(2048) * 4) + 1024 * (8192 + 64) * 4 + 1024 * 2048 * 4
     assert lib.idx_workspace_size(0, ctypes.byref(p), 0, 0, 0, 0, 0, 0, ctypes.byref(n)) == 0 and n.value == 0
