@@ -50,6 +50,7 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 
 namespace idx {
@@ -428,19 +429,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((MODE =
 
 // Workgroups of one kernel the current device runs at once (CUs x workgroups per CU),
 // queried once per device and kernel.
+// Host threads may call concurrently: entries are atomics, and a race only repeats the query.
 template <class Kern>
 int resident_workgroups(Kern kern, int threads) {
-  static int cached[64];
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0) != hipSuccess)
       return 0;
-    cached[dev] = cus * per_cu;
+    n = cus * per_cu;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 constexpr int NW_LAUNCH = 4;   // 4 waves: up to 3 workgroups per CU, so a stage barrier never idles the CU
