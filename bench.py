@@ -232,11 +232,24 @@ COPY_BYTES = 256 << 20   # calibration copy of the traffic probe
 
 
 def traffic_probe(dev):
-    """Launches for a rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE run: the scoring kernel on the
-    glm_chunk key blocks (as the fused path launches it), then a device-to-device copy of
-    COPY_BYTES that calibrates what those counters read for a known number of bytes."""
+    """Launches for a rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE run: one fused glm_chunk call and
+    the ragged workload's candidate source (the selection, refinement, pooling and mask kernels),
+    then the scoring kernel on the glm_chunk key blocks (as the fused path launches it) twice, then
+    two device-to-device copies of COPY_BYTES that calibrate what those counters read for a known
+    number of bytes."""
     p = synth.make_config("glm_chunk")
     d = idx.Inputs.from_host(p, device=dev)
+    K, Bk = p.meta["K"], p.meta["block_k"]
+    idx.idx_logits_topk_fused(d, K, block_k=Bk)
+    p5 = synth.make_config("ragged_cand")
+    c5 = p5.meta
+    d5 = idx.Inputs.from_host(p5, device=dev)
+    blocks5 = torch.empty((p5.T, c5["n_blocks"]), dtype=torch.int32, device=dev)
+    idx.idx_block_candidates(d5, p5.W, pool=c5["pool"], n_blocks=c5["n_blocks"], block_k=c5["block_k"],
+                             row_chunk=4096, out_blocks=blocks5)
+    torch.cuda.synchronize()
+    del d5, blocks5
+    torch.cuda.empty_cache()
     lk = launch_keys(p.L, p.meta["block_k"])
     scratch = launch_scratch(p.T, lk)
     for rep in range(2):
@@ -257,18 +270,22 @@ def traffic_summary(fetch_dir, write_dir):
     import csv
 
     def read(dirname, counter):
-        rows = []
+        acc = {}
         for r in csv.DictReader(open(os.path.join(dirname, "run_counter_collection.csv"))):
             if r["Counter_Name"] == counter:
-                rows.append((r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0))  # KiB -> bytes
-        return rows
+                k = int(r["Dispatch_Id"])
+                n, v, t0, t1 = acc.get(k, (r["Kernel_Name"], 0.0, int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+                acc[k] = (n, v + float(r["Counter_Value"]) * 1024.0, t0, t1)   # KiB -> bytes, summed over instances
+        return [acc[k] for k in sorted(acc)]
 
     out = {}
+    per_dispatch = {}
     for counter, dirname in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = read(dirname, counter)
-        lk = [v for n, v in rows if "logits_kernel" in n]
-        cp = [v for n, v in rows if "copyBuffer" in n]
-        calib = max(cp)                      # the 256 MiB copies are the largest copy dispatches
+        per_dispatch[counter] = rows
+        lk = [v for n, v, _, _ in rows if "logits_kernel<0, 32, 1, 4>" in n]
+        cp = [v for n, v, _, _ in rows if "copyBuffer" in n]
+        calib = max(cp[-2:])                 # the probe's last two dispatches are the 256 MiB calibration copies
         factor = COPY_BYTES / calib
         out[counter] = {"raw_per_launch": lk, "copy_raw": calib, "factor": factor,
                         "bytes_per_launch": [v * factor for v in lk]}
@@ -299,6 +316,32 @@ def traffic_summary(fetch_dir, write_dir):
               + ", ".join(f"{x / 2**20:.1f} MiB" for x in v["bytes_per_launch"]) + " |")
     print(f"\nAverage HBM traffic per scoring launch: {avg / 2**20:.1f} MiB "
           f"(kernel source hash {rec['kernel_source_hash']}).")
+    # the other kernels of the probe: bytes per dispatch and the rate over its (profiled) duration
+    import re
+    f_rows, w_rows = per_dispatch["FETCH_SIZE"], per_dispatch["WRITE_SIZE"]
+    groups = {}
+    workload = "glm_chunk fused"      # the probe's first call; the second key-bound launch starts the ragged one
+    nkb = 0
+    for (n, fv, t0, t1), (_, wv, _, _) in zip(f_rows, w_rows):
+        m = re.search(r"namespace\)::(\w+(?:<[^>]*>)?)", n)
+        name = m.group(1) if m else n.split("(")[0]
+        if name.startswith("key_bound_kernel"):
+            nkb += 1
+            if nkb == 2:
+                workload = "ragged_cand candidates"
+        if name.startswith("logits_kernel<0, 32, 1, 4>") or "copyBuffer" in n or not n.startswith("void idx") and \
+                not n.startswith("idx::"):
+            continue
+        g = groups.setdefault((workload, name), [0, 0.0, 0.0, 0.0])
+        g[0] += 1
+        g[1] += fv * out["FETCH_SIZE"]["factor"]
+        g[2] += wv * out["WRITE_SIZE"]["factor"]
+        g[3] += (t1 - t0) * 1e-9
+    print("\n| workload | kernel | dispatches | fetched MiB per dispatch | written MiB per dispatch | us per dispatch | GB/s |")
+    print("|---|---|---|---|---|---|---|")
+    for (wl, name), (cnt, fb, wb, t) in sorted(groups.items(), key=lambda x: (x[0][0], -x[1][3])):
+        print(f"| {wl} | {name} | {cnt} | {fb / cnt / 2**20:.1f} | {wb / cnt / 2**20:.1f} | {t / cnt * 1e6:.1f} | "
+              f"{(fb + wb) / t / 1e9:.0f} |")
 
 
 def fused_line(p, d, K, block_k, row_chunk, reps, stream):
