@@ -65,6 +65,28 @@ __global__ __launch_bounds__(256) void expand_mask_kernel(const int32_t *blocks,
   __syncthreads();
   uint8_t *mrow = mask + (int64_t)t * ld_mask;
   const bool vec = ((uintptr_t)mrow & 15) == 0;
+  if (pool == 8 && vec) {
+    // 16 aligned bytes are blocks 2c and 2c + 1 of 8 keys: two bits of one bitmap word
+    for (int j0 = threadIdx.x * 16; j0 < W; j0 += 256 * 16) {
+      const uint32_t wd = bits[j0 >> 8] >> ((j0 >> 3) & 31);
+      const uint32_t lo = (wd & 1u) ? 0x01010101u : 0u, hi = (wd & 2u) ? 0x01010101u : 0u;
+      uint4 v = make_uint4(lo, lo, hi, hi);
+      if (j0 + 16 > win) {   // the window ends inside these bytes (or before them)
+        uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (j0 + e >= win) w4[e >> 2] &= ~(0xFFu << (8 * (e & 3)));
+        v = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+      }
+      if (j0 + 16 <= W) {
+        *(uint4 *)(mrow + j0) = v;
+      } else {
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+        for (int e = 0; e < 16 && j0 + e < W; ++e) mrow[j0 + e] = (uint8_t)(w4[e >> 2] >> (8 * (e & 3)));
+      }
+    }
+    return;
+  }
   for (int j0 = threadIdx.x * 16; j0 < W; j0 += 256 * 16) {
     uint32_t w4[4];
 #pragma unroll
