@@ -51,9 +51,10 @@ struct Smem {
   // slot per lane for writes that are dropped.  A merge compacts them in place.
   alignas(16) uint32_t ikey[NI + 64];
   alignas(16) int32_t iid[NI + 64];
+  // histogram bins (+ one spare slot per lane); the first CAP words double as the
+  // ranking list
   alignas(16) uint32_t hist[NB + 64];
-  uint32_t bmap[BMAP_BITS / 32];  // the row's allowed blocks over the launch's columns (block consumer) // histogram bins (+ one spare slot per lane); the first CAP words
-                          // double as the ranking list
+  uint32_t bmap[BMAP_BITS / 32];  // the row's allowed blocks over the launch's columns (block consumer)
   uint32_t red[3][NWV];
   uint32_t wsum[2][NWV];
   uint32_t bcast[4];
