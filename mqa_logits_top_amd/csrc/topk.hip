@@ -408,6 +408,8 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
             raw[c][4 * q + 2] = v.z;
             raw[c][4 * q + 3] = v.w;
           });
+        } else if (cb >= s1 || cb + VPT <= s0) {
+          static_for<VPT>([&](auto j) __attribute__((always_inline)) { raw[c][j] = 0.f; });   // outside the window
         } else {
           static_for<VPT>([&](auto j) __attribute__((always_inline)) {
             const int col = cb + j;
@@ -428,6 +430,9 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         if (cb >= s0 && cb + VPT <= s1 && !mrow && !BLOCKS) {
           // the whole chunk lies in the window and no consumer filter applies: no per-column tests
           static_for<VPT>([&](auto j) __attribute__((always_inline)) { keep(key[c][j], fkey(raw[c][j])); });
+        } else if (cb >= s1 || cb + VPT <= s0) {
+          // the whole chunk lies outside the window: no keys (short rows of ragged batches)
+          static_for<VPT>([&](auto j) __attribute__((always_inline)) { key[c][j] = 0u; });
         } else {
           static_for<VPT>([&](auto j) __attribute__((always_inline)) {
             const int col = cb + j;
