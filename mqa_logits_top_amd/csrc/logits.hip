@@ -123,6 +123,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((MODE =
   constexpr int RPW = NW * QR;           // rows per workgroup
   constexpr int KB = KF == 0 ? 128 : 64; // key bytes
   constexpr int TK = KF == 0 ? 128 : 256; // keys per LDS stage (16 KiB either way)
+  constexpr int BY_ROW_MIN_TILES = 4;
   constexpr int STAGE = TK * KB;
   constexpr int LPT = STAGE / 16 / (NW * 64);  // 16-byte chunks per thread per stage
   constexpr int ST = MODE == STORE_SLAB ? 0 : TK / 64;  // stores per stage and wave, at least (candidate stores on top)
@@ -159,7 +160,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((MODE =
   // fastest within groups of 8, item = (group * nsplit + split) * 8 + rb % 8, so workgroup b
   // takes row blocks == b (mod 8).  Row blocks are padded to whole groups of 8.
   int split_i, rb;
-  if (a.by_row && *a.by_row != 0u) {   // uniform
+  const bool by_row = a.by_row && *a.by_row != 0u;   // uniform
+  if (by_row) {
     const int grp = item / (8 * a.nsplit), rem8 = item % (8 * a.nsplit);
     split_i = rem8 >> 3;
     rb = grp * 8 + (rem8 & 7);
@@ -186,10 +188,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((MODE =
     if (lane == 0) { wg_range[0] = lo; wg_range[1] = hi; }
   }
   __syncthreads();
-  const int split_lo = a.key_lo + split_i * a.split;
-  const int split_hi = min(split_lo + a.split, a.key_hi);
-  const int s_lo = max(split_lo, wg_range[0]);
-  const int s_hi = min(split_hi, wg_range[1]);
+  int s_lo, s_hi;
+  if (by_row) {
+    // The row block's items share the tiles of its rows' window union evenly, in key
+    // order, at least BY_ROW_MIN_TILES each: the short windows of a ragged batch then
+    // spread over several workgroups instead of leaving one or two long items per block.
+    const int u_lo = max(a.key_lo, wg_range[0]), u_hi = min(a.key_hi, wg_range[1]);
+    const int ut0 = u_lo & ~(TK - 1);
+    const int unt = u_lo < u_hi ? (u_hi - ut0 + TK - 1) / TK : 0;
+    const int nact = min(a.nsplit, (unt + BY_ROW_MIN_TILES - 1) / BY_ROW_MIN_TILES);
+    const int a0 = split_i < nact ? split_i * unt / nact : 0;
+    const int a1 = split_i < nact ? (split_i + 1) * unt / nact : 0;
+    s_lo = max(u_lo, ut0 + a0 * TK);
+    s_hi = min(u_hi, ut0 + a1 * TK);
+  } else {
+    const int split_lo = a.key_lo + split_i * a.split;
+    const int split_hi = min(split_lo + a.split, a.key_hi);
+    s_lo = max(split_lo, wg_range[0]);
+    s_hi = min(split_hi, wg_range[1]);
+  }
   // this part's tiles of the item: [tile0, tile0 + ntiles * TK)
   const int itile0 = s_lo & ~(TK - 1);
   const int intiles = s_lo < s_hi ? (s_hi - itile0 + TK - 1) / TK : 0;

@@ -443,3 +443,37 @@ def test_topk_selection_exact_long_rows(K, block_k):
         oi, ov = oracle.topk_row(win, int(ks[t]), K)
         assert np.array_equal(gi[t], oi), f"row {t}"
         assert np.array_equal(gv[t], ov.astype(np.float32)) or np.array_equal(np.abs(gv[t]), np.abs(ov)), f"row {t}"
+
+
+def test_ragged_short_requests_row_block_layout():
+    """A ragged batch of short requests (and one on a prefix) covers a small part of each
+    launch's (rows x keys) rectangle, so the scoring launches take the row-block layout, in
+    which a row block's workgroups split its rows' window union between them.  Every row
+    matches the oracle, the fused result equals the dense path refined, bitwise, for two
+    key-block and row-chunk shapes, and the fused candidate source matches the oracle."""
+    cu_q = np.array([0, 704, 1408, 1508], np.int32)
+    cu_k = np.array([0, 704, 1408, 3008], np.int32)   # request 2: 100 new tokens on a 1500-token prefix
+    ks, ke = synth.ragged_windows(cu_q, cu_k)
+    T, L = int(cu_q[-1]), int(cu_k[-1])
+    p = synth.make_problem(T, L, 64, k_fmt=synth.K_FP8, seed=77, ks=ks, ke=ke)
+    d = dev(p)
+    dq = oracle.Dequantised(p)
+    o = Windows([oracle.row_logits(dq, t) for t in range(T)], [oracle.row_magnitude(dq, t) for t in range(T)])
+    K = 64
+    W = max(p.W, 1)
+    lg = idx.idx_mqa_logits(d, W)
+    ci, cv = idx.idx_topk(lg, d.ks, d.ke, idx.candidate_capacity(K))
+    di, dv = idx.idx_refine_topk(d, ci, cv, K)
+    del lg
+    for block_k, row_chunk in ((4096, 0), (1024, 512)):
+        ws = torch.empty(idx.idx_workspace_size(idx.IDX_OP_LOGITS_TOPK_FUSED, d, K=K, block_k=block_k,
+                                                row_chunk=row_chunk), dtype=torch.uint8, device="cuda")
+        fi, fv = idx.idx_logits_topk_fused(d, K, block_k=block_k, row_chunk=row_chunk, ws=ws)
+        torch.cuda.synchronize()
+        assert idx.overflow_count(ws) == 0
+        assert torch.equal(di, fi) and torch.equal(dv.view(torch.int32), fv.view(torch.int32)), (block_k, row_chunk)
+    topk_ok(fi.cpu().numpy(), fv.cpu().numpy(), o, p.ks, K)
+    n_blocks = 16
+    blocks = torch.empty((T, n_blocks), dtype=torch.int32, device="cuda")
+    mask, _ = idx.idx_block_candidates(d, W, n_blocks=n_blocks, block_k=1024, row_chunk=512, out_blocks=blocks)
+    _check_candidates(p, o, mask.cpu().numpy(), blocks.cpu().numpy(), n_blocks)
