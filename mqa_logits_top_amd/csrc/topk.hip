@@ -396,6 +396,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     // their count and range are taken as each chunk converts, while later chunks still load
     uint32_t key[NCH][VPT];
     uint32_t seg_n = 0, seg_lo = 0xFFFFFFFFu, seg_hi = 0;
+    uint32_t live = 0;   // bit c: this thread's chunk c holds a nonzero key
     {
       float raw[NCH][VPT];
       static_for<NCH>([&](auto c) __attribute__((always_inline)) {
@@ -427,6 +428,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       };
       static_for<NCH>([&](auto c) __attribute__((always_inline)) {
         const int cb = S + c * SPAN + tid * VPT;
+        const uint32_t n0 = seg_n;
         if (cb >= s0 && cb + VPT <= s1 && !mrow && !BLOCKS) {
           // the whole chunk lies in the window and no consumer filter applies: no per-column tests
           static_for<VPT>([&](auto j) __attribute__((always_inline)) { keep(key[c][j], fkey(raw[c][j])); });
@@ -446,6 +448,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
             keep(key[c][j], k);
           });
         }
+        live |= (uint32_t)(seg_n != n0) << c;
       });
       seg_lo = seg_lm1 == 0xFFFFFFFFu ? 0xFFFFFFFFu : seg_lm1 + 1u;
     }
@@ -501,7 +504,8 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
           if (k >= clo && k <= chi) atomicAdd(&sm.hist[bin_of(k, chi, sh)], 1u);
         }
         static_for<NCH>([&](auto c) __attribute__((always_inline)) {
-          static_for<VPT>([&](auto j) __attribute__((always_inline)) {
+          // chunks without keys are skipped (whole waves of them in short windows)
+          if ((live >> c) & 1u) static_for<VPT>([&](auto j) __attribute__((always_inline)) {
             const uint32_t k = key[c][j];
             if (k >= clo && k <= chi) atomicAdd(&sm.hist[bin_of(k, chi, sh)], 1u);
           });
@@ -587,7 +591,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       const uint32_t X = decided ? thk + 1u : theta;
       static_for<NCH>([&](auto c) __attribute__((always_inline)) {
         tb[c] = 0;
-        static_for<VPT>([&](auto j) __attribute__((always_inline)) {
+        if ((live >> c) & 1u) static_for<VPT>([&](auto j) __attribute__((always_inline)) {
           tb[c] |= (uint32_t)(key[c][j] >= X && !none) << j;
         });
         nt[c] = __builtin_popcount(tb[c]);
@@ -608,7 +612,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     // every entry is written: taken ones to their slot, the rest to this lane's spare slot
     static_for<NCH>([&](auto c) __attribute__((always_inline)) {
       uint32_t pos = posb[c];
-      static_for<VPT>([&](auto j) __attribute__((always_inline)) {
+      if (tb[c] != 0u) static_for<VPT>([&](auto j) __attribute__((always_inline)) {
         const bool tk = (tb[c] >> j) & 1u;
         if (tk && pos < (uint32_t)CAPK) {
           sm.ikey[run_n + pos] = key[c][j];
