@@ -139,12 +139,28 @@ class Inputs:
                            ks=self.ks.data_ptr(), ke=self.ke.data_ptr(), T=self.T, H=self.H,
                            D=int(self.q.shape[2]), L=self.L, scale=self.scale)
 
+    @property
+    def W(self) -> int:
+        """Longest row window (max_seqlen_k), read from the device windows."""
+        return int((self.ke - self.ks).max().item()) if self.T else 0
+
+    @property
+    def pairs(self) -> int:
+        """In-window (row, key) pairs, read from the device windows."""
+        return int((self.ke.to(torch.int64) - self.ks).sum().item()) if self.T else 0
+
     @staticmethod
     def from_host(p, device="cuda") -> "Inputs":
-        """Copy a host problem (numpy arrays with the same field names) to the device."""
+        """Copy a host problem (numpy arrays with the same field names) to the device.  A problem
+        without ks / ke gives its batch as cu_q / cu_k; the windows are then built on the device
+        by idx_ragged_windows."""
         t = lambda a: torch.from_numpy(a).to(device)
-        return Inputs(q=t(p.q), q_scale=t(p.q_scale), k=t(p.k), k_scale=t(p.k_scale), w=t(p.w), ks=t(p.ks),
-                      ke=t(p.ke), k_fmt=int(p.k_fmt), scale=float(p.scale))
+        if getattr(p, "ks", None) is not None:
+            ks, ke = t(p.ks), t(p.ke)
+        else:
+            ks, ke = idx_ragged_windows(t(p.cu_q), t(p.cu_k), int(p.q.shape[0]))
+        return Inputs(q=t(p.q), q_scale=t(p.q_scale), k=t(p.k), k_scale=t(p.k_scale), w=t(p.w), ks=ks,
+                      ke=ke, k_fmt=int(p.k_fmt), scale=float(p.scale))
 
 
 def idx_workspace_size(op: int, p: Inputs, K: int = 0, block_k: int = 0, row_chunk: int = 0, pool: int = 0,

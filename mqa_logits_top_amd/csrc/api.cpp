@@ -9,6 +9,7 @@
 #include <cstdint>
 
 #include "../../include/idx.h"
+#include "api_internal.h"
 #include "kernels.h"
 
 namespace {
@@ -359,13 +360,13 @@ idx_status idx_logits_topk_fused(const idx_problem *p, int32_t K, int32_t block_
 
 }  // extern "C"
 
-namespace {
+namespace idx {
 // The fused indexer with its optional consumers: a byte mask or a block list restricting
 // the selectable keys, and the index -> KV-slot transform of the final write.
 idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t row_chunk, const uint8_t *mask,
                       int64_t ld_mask, const int32_t *blocks, int64_t ld_blocks, int32_t n_blocks, int32_t pool,
                       const int32_t *slot_of_key, int32_t *out_idx, float *out_val, int32_t *out_slot, void *ws,
-                      size_t ws_bytes, void *stream) {
+                      size_t ws_bytes, void *stream, WorkspaceSource ws_source) {
   idx_status st = check_problem(p, true);
   if (st) return st;
   if (!out_idx) return IDX_E_NULL;
@@ -391,8 +392,10 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
   }
   const size_t need = fused_ws(Tc, LB, K);
   if (p->T == 0) return IDX_OK;
-  if (!ws) return IDX_E_NULL;
   if (ws_bytes < need) return IDX_E_WORKSPACE;
+  // a workspace the library provides is looked up only once every host check has passed
+  if (ws_source && ws_source(&ws) != hipSuccess) return IDX_E_LAUNCH;
+  if (!ws) return IDX_E_NULL;
   if (!aligned(ws, 256)) return IDX_E_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   const int32_t Kc = cand_cap(K);
@@ -489,7 +492,7 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
   }
   return IDX_OK;
 }
-}  // namespace
+}  // namespace idx
 
 extern "C" {
 
@@ -497,16 +500,16 @@ idx_status idx_logits_topk_fused_paged(const idx_problem *p, int32_t K, int32_t 
                                        const uint8_t *mask, int64_t ld_mask, const int32_t *slot_of_key,
                                        int32_t *out_idx, float *out_val, int32_t *out_slot, void *ws,
                                        size_t ws_bytes, void *stream) {
-  return fused_impl(p, K, block_k, row_chunk, mask, ld_mask, nullptr, 0, 0, 1, slot_of_key, out_idx, out_val,
-                    out_slot, ws, ws_bytes, stream);
+  return idx::fused_impl(p, K, block_k, row_chunk, mask, ld_mask, nullptr, 0, 0, 1, slot_of_key, out_idx, out_val,
+                         out_slot, ws, ws_bytes, stream, nullptr);
 }
 
 idx_status idx_logits_topk_fused_blocks(const idx_problem *p, int32_t K, int32_t block_k, int32_t row_chunk,
                                         const int32_t *blocks, int64_t ld_blocks, int32_t n_blocks, int32_t pool,
                                         int32_t *out_idx, float *out_val, void *ws, size_t ws_bytes, void *stream) {
   if (!blocks) return IDX_E_NULL;
-  return fused_impl(p, K, block_k, row_chunk, nullptr, 0, blocks, ld_blocks, n_blocks, pool, nullptr, out_idx,
-                    out_val, nullptr, ws, ws_bytes, stream);
+  return idx::fused_impl(p, K, block_k, row_chunk, nullptr, 0, blocks, ld_blocks, n_blocks, pool, nullptr, out_idx,
+                         out_val, nullptr, ws, ws_bytes, stream, nullptr);
 }
 
 idx_status idx_refine_topk(const idx_problem *p, const int32_t *cand_idx, const float *cand_val, int64_t ld_cand,

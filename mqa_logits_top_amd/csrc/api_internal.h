@@ -1,0 +1,22 @@
+// Declarations shared by the C ABI's source files (not part of the public interface).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/idx.h"
+
+namespace idx {
+
+// Supplies a workspace the library owns, once every host check of a call has passed.
+typedef hipError_t (*WorkspaceSource)(void **ws);
+
+// The fused indexer (idx_logits_topk_fused and its variants): optional byte mask or block
+// list consumer, optional index -> slot transform.  ws_source (nullable) replaces `ws` by the
+// workspace it returns; ws_bytes is then that workspace's size.
+idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t row_chunk, const uint8_t *mask,
+                      int64_t ld_mask, const int32_t *blocks, int64_t ld_blocks, int32_t n_blocks, int32_t pool,
+                      const int32_t *slot_of_key, int32_t *out_idx, float *out_val, int32_t *out_slot, void *ws,
+                      size_t ws_bytes, void *stream, WorkspaceSource ws_source);
+
+}  // namespace idx

@@ -2,7 +2,8 @@
 
 This module only draws random numbers and stores them in the input formats the
 indexer consumes (fp8 E4M3 codes with per-row fp32 scales, MXFP4 codes with
-E8M0 block scales, fp32 head weights, int32 key windows).  It holds none of the
+E8M0 block scales, fp32 head weights, int32 key windows or a batch's
+cu_seqlens).  It holds none of the
 indexer's arithmetic; the GPU library and the CPU oracle both read the arrays
 it returns.  The heavy loops live in ``gen.c`` (built with gcc + OpenMP).
 
@@ -130,16 +131,22 @@ def mxfp4_normal_rows(seed: int, stream: int, rows: int, cols: int):
 # ---------------------------------------------------------------- problems
 @dataclass
 class Problem:
-    """Host arrays of one indexer call (all C-contiguous numpy)."""
+    """Host arrays of one indexer call (all C-contiguous numpy).
+
+    Row windows are given either directly (ks, ke: explicit draws) or as the batch's
+    cu_seqlens (cu_q, cu_k), from which each side derives them itself: the library with
+    idx_ragged_windows, the oracle with its own row-by-row definition."""
     q: np.ndarray          # u8 [T, H, D]   E4M3 codes
     q_scale: np.ndarray    # f32 [T, H]
     k: np.ndarray          # u8 [L, D] (fp8) or [L, D/2] (MXFP4 packed)
     k_scale: np.ndarray    # f32 [L] (fp8) or u8 [L, D/32] (E8M0)
     k_fmt: int
     w: np.ndarray          # f32 [T, H]
-    ks: np.ndarray         # i32 [T]
-    ke: np.ndarray         # i32 [T]
+    ks: Optional[np.ndarray] = None   # i32 [T] (or None: windows from cu_q / cu_k)
+    ke: Optional[np.ndarray] = None   # i32 [T]
     scale: float = 1.0
+    cu_q: Optional[np.ndarray] = None  # i32 [B + 1] query rows of each request
+    cu_k: Optional[np.ndarray] = None  # i32 [B + 1] key rows of each request
     meta: dict = field(default_factory=dict)
 
     @property
@@ -158,49 +165,17 @@ class Problem:
     def L(self):
         return self.k.shape[0]
 
-    @property
-    def W(self):
-        """Row-relative output width: the longest window (max_seqlen_k)."""
-        return int((self.ke - self.ks).max()) if self.T else 0
-
-    @property
-    def pairs(self) -> int:
-        return int((self.ke.astype(np.int64) - self.ks).sum())
-
-
-def causal_windows(T: int, L: int):
-    """A chunk of T rows at the tail of an L-key prefix: ks = 0, ke = L - T + t + 1."""
-    t = np.arange(T, dtype=np.int64)
-    ks = np.zeros(T, np.int32)
-    ke = (L - T + t + 1).astype(np.int32)
-    return ks, ke
-
-
-def ragged_windows(cu_q, cu_k):
-    """Per-row windows of a varlen batch: request i owns key rows [cu_k[i], cu_k[i+1]),
-    its new tokens are the last len_q of them, row j sees keys up to its own position."""
-    cu_q = np.asarray(cu_q, np.int64)
-    cu_k = np.asarray(cu_k, np.int64)
-    T = int(cu_q[-1])
-    ks = np.zeros(T, np.int32)
-    ke = np.zeros(T, np.int32)
-    for i in range(len(cu_q) - 1):
-        lq = cu_q[i + 1] - cu_q[i]
-        lk = cu_k[i + 1] - cu_k[i]
-        prefix = lk - lq
-        j = np.arange(lq)
-        ks[cu_q[i]:cu_q[i + 1]] = cu_k[i]
-        ke[cu_q[i]:cu_q[i + 1]] = cu_k[i] + prefix + j + 1
-    return ks, ke
-
 
 def make_problem(T: int, L: int, H: int, D: int = 128, k_fmt: int = K_FP8, seed: int = 0,
                  ks: Optional[np.ndarray] = None, ke: Optional[np.ndarray] = None,
+                 cu_q=None, cu_k=None,
                  dup_rows: int = 0, w_lo: float = 0.0, w_hi: float = 1.0,
                  q_stream: int = S_Q, w_stream: int = S_W, keys: Optional[tuple] = None,
                  scale: float = 1.0) -> Problem:
     """q, k ~ N(0,1) quantised (fp8 per-row amax/448, or MXFP4 for keys); w ~ U(w_lo, w_hi).
 
+    Windows: explicit ks / ke, or a varlen batch's cu_q / cu_k; with neither, one request
+    cu_q = [0, T], cu_k = [0, L] (the chunk is the tail of its prefix).
     ``keys`` reuses (k, k_scale) from another problem (same prefix, new layer).
     ``dup_rows`` > 0 byte-copies that many key rows (codes and scales) from
     other, non-copied rows, so those keys score exactly alike.
@@ -234,11 +209,19 @@ def make_problem(T: int, L: int, H: int, D: int = 128, k_fmt: int = K_FP8, seed:
         meta["dup_dst"] = dst
         meta["dup_src"] = src
     w = uniform_f32(seed, w_stream, (T, H), w_lo, w_hi)
-    if ks is None or ke is None:
-        ks, ke = causal_windows(T, L)
+    if ks is not None or ke is not None:
+        assert ks is not None and ke is not None
+        ks = np.ascontiguousarray(ks, np.int32)
+        ke = np.ascontiguousarray(ke, np.int32)
+        cu_q = cu_k = None
+    else:
+        if cu_q is None:
+            cu_q, cu_k = [0, T], [0, L]
+        cu_q = np.ascontiguousarray(cu_q, np.int32)
+        cu_k = np.ascontiguousarray(cu_k, np.int32)
+        assert int(cu_q[-1]) == T and int(cu_k[-1]) <= L
     return Problem(q=q8, q_scale=qs, k=np.ascontiguousarray(k), k_scale=np.ascontiguousarray(ksc),
-                   k_fmt=k_fmt, w=w, ks=np.ascontiguousarray(ks, np.int32),
-                   ke=np.ascontiguousarray(ke, np.int32), scale=scale, meta=meta)
+                   k_fmt=k_fmt, w=w, ks=ks, ke=ke, scale=scale, cu_q=cu_q, cu_k=cu_k, meta=meta)
 
 
 # The five workloads (shapes of the pages' indexer calls).  Seed 0 throughout.
@@ -261,10 +244,9 @@ CONFIGS = {
 def make_config(name: str, seed: int = 0) -> Problem:
     c = CONFIGS[name]
     if "cu_q" in c:
-        ks, ke = ragged_windows(c["cu_q"], c["cu_k"])
         T = int(c["cu_q"][-1])
         L = int(c["cu_k"][-1])
-        p = make_problem(T, L, c["H"], k_fmt=c["k_fmt"], seed=seed, ks=ks, ke=ke)
+        p = make_problem(T, L, c["H"], k_fmt=c["k_fmt"], seed=seed, cu_q=c["cu_q"], cu_k=c["cu_k"])
     else:
         p = make_problem(c["T"], c["L"], c["H"], k_fmt=c["k_fmt"], seed=seed,
                          dup_rows=c.get("dup_rows", 0))
@@ -274,5 +256,5 @@ def make_config(name: str, seed: int = 0) -> Problem:
 
 def consumer_layer(p: Problem, seed: int = 0) -> Problem:
     """A later indexer layer of the same batch: fresh q and w (streams 5, 6), same keys and windows."""
-    return make_problem(p.T, p.L, p.H, p.D, p.k_fmt, seed, ks=p.ks, ke=p.ke,
+    return make_problem(p.T, p.L, p.H, p.D, p.k_fmt, seed, ks=p.ks, ke=p.ke, cu_q=p.cu_q, cu_k=p.cu_k,
                         q_stream=S_Q2, w_stream=S_W2, keys=(p.k, p.k_scale), scale=p.scale)

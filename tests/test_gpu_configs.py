@@ -1,8 +1,9 @@
 """The five workloads at full size, in the launch configuration the benchmark
-uses, checked against the fp64 oracle on sampled rows (first and last rows of
-each request, rows next to row-chunk and key-block boundaries, and a stride),
-plus properties that hold at any size: fused == dense + refine bitwise,
-row-count invariance, and the candidate mask's internal consistency."""
+uses, checked against the fp64 oracle: every row of the tiny and GLM-shaped
+chunks, sampled rows elsewhere (first and last rows of each request, rows next
+to row-chunk and key-block boundaries, and a stride), plus properties that hold
+at any size: fused == dense + refine bitwise, row-count invariance over row
+chunks of 128 .. 4096 rows, and the candidate mask's internal consistency."""
 import numpy as np
 import pytest
 import torch
@@ -10,7 +11,7 @@ import torch
 import mqa_logits_top_amd as idx
 import oracle
 import synth
-from checks import logits_ok, topk_ok
+from checks import dense_ref, logits_ok, topk_ok, windows_match
 
 pytestmark = pytest.mark.gpu
 
@@ -19,22 +20,26 @@ _cache = {}
 
 def prob(name):
     if name not in _cache:
-        p = synth.make_config(name)
         _cache.clear()
-        _cache[name] = (p, idx.Inputs.from_host(p), oracle.Dequantised(p))
+        torch.cuda.empty_cache()
+        p = synth.make_config(name)
+        d = idx.Inputs.from_host(p)
+        dq = oracle.Dequantised(p)
+        windows_match(d, dq)
+        _cache[name] = (p, d, dq)
     return _cache[name]
 
 
-def sample_rows(p, extra=(), n_stride=12):
-    T = p.T
-    rows = {0, T - 1, *extra}
+def sample_rows(dq, meta, n_stride=12):
+    T = dq.T
+    rows = {0, T - 1}
     rows.update(range(0, T, max(1, T // n_stride)))
-    for b in (1024, 1100, 2048, 4096):
+    for b in (128, 1024, 1100, 2048, 4096, 8192):
         for r in (b - 1, b):
             if r < T:
                 rows.add(r)
-    if "cu_q" in p.meta:
-        for c in p.meta["cu_q"]:
+    if "cu_q" in meta:
+        for c in meta["cu_q"]:
             for r in (c - 1, c):
                 if 0 <= r < T:
                     rows.add(r)
@@ -50,29 +55,47 @@ def fused(d, K, block_k, row_chunk=0, mask=None):
     return gi, gv
 
 
+def _check_rows(d, dq, rows, gi, gv, K, lg=None, chunk=256):
+    """Oracle rows in chunks (bounded host memory): fused top-K sets and values, and the dense
+    logits of the same rows when lg is given."""
+    rows = list(rows)
+    for c0 in range(0, len(rows), chunk):
+        rs = rows[c0:c0 + chunk]
+        o = oracle.rows_logits(dq, rs)
+        topk_ok(gi[rs], gv[rs], o, dq.ks[rs], K, what=f"rows {rs[0]}..{rs[-1]}")
+        if lg is not None:
+            g = lg[rs].cpu().numpy()
+            logits_ok(g, dense_ref(o, g.shape[1]), what=f"logits rows {rs[0]}..{rs[-1]}")
+
+
 @pytest.mark.parametrize("name", ["tiny", "glm_chunk", "dsv4_mxfp4"])
 def test_config_fused_vs_oracle(name):
+    """tiny and glm_chunk: every row; dsv4_mxfp4: sampled rows.  Fused top-K and dense
+    logits against the oracle; the dense comparator (top-(K + 512) of the dense logits,
+    then the exact boundary) equals the fused result bitwise."""
     p, d, dq = prob(name)
     K, Bk = p.meta["K"], p.meta["block_k"]
     gi, gv = fused(d, K, Bk)
-    rows = range(p.T) if p.T <= 64 else sample_rows(p)
-    o = [oracle.row_logits(dq, t) for t in rows]
-    gi, gv = gi.cpu().numpy(), gv.cpu().numpy()
-    topk_ok(gi[list(rows)], gv[list(rows)], o, p.ks[list(rows)], K)
-    # dense logits of the same rows
-    W = p.W
-    lg = idx.idx_mqa_logits(d, W)
-    g = lg[list(rows)].cpu().numpy()
-    ref = np.full(g.shape, -np.inf)
-    for i, v in enumerate(o):
-        ref[i, :len(v)] = v
-    logits_ok(g, ref)
-    # the dense comparator (top-K + 512 of the dense logits, then the exact boundary) matches bitwise
+    rows = range(dq.T) if name in ("tiny", "glm_chunk") else sample_rows(dq, p.meta)
+    lg = idx.idx_mqa_logits(d, d.W)
+    gin, gvn = gi.cpu().numpy(), gv.cpu().numpy()
+    _check_rows(d, dq, rows, gin, gvn, K, lg)
     ci, cv = idx.idx_topk(lg, d.ks, d.ke, idx.candidate_capacity(K))
     del lg
     di, dv = idx.idx_refine_topk(d, ci, cv, K)
-    assert np.array_equal(di.cpu().numpy(), gi)
-    assert np.array_equal(dv.cpu().numpy().view(np.int32), gv.view(np.int32))
+    assert torch.equal(di, gi)
+    assert torch.equal(dv.view(torch.int32), gv.view(torch.int32))
+
+
+def test_dsv4_row_count_invariance():
+    """P2 Accuracy/equivalence: scoring all rows in one call or in row chunks of 128 .. 4096
+    gives identical output (bitwise), here at the DeepSeek-V4-like MXFP4 shape."""
+    p, d, dq = prob("dsv4_mxfp4")
+    K, Bk = p.meta["K"], p.meta["block_k"]
+    gi, gv = fused(d, K, Bk, row_chunk=0)
+    for rc in (128, 256, 512, 1024, 2048, 4096):
+        ci, cv = fused(d, K, Bk, row_chunk=rc)
+        assert torch.equal(ci, gi) and torch.equal(cv.view(torch.int32), gv.view(torch.int32)), rc
 
 
 def test_dsv4_duplicate_keys_tie_by_index():
@@ -84,9 +107,9 @@ def test_dsv4_duplicate_keys_tie_by_index():
     # a duplicated key scores exactly like its source: when both are in a row's window,
     # either both are selected, or only the lower index, or neither
     bad = 0
-    for t in sample_rows(p):
+    for t in sample_rows(dq, p.meta):
         sel = set(gi[t][gi[t] >= 0].tolist())
-        ke = int(p.ke[t])
+        ke = int(dq.ke[t])
         for a_, b_ in zip(dst, src):
             if a_ < ke and b_ < ke:
                 lo, hi = min(a_, b_), max(a_, b_)
@@ -98,14 +121,13 @@ def test_long_ctx_fused_vs_rowchunked_dense():
     p, d, dq = prob("long_ctx")
     K, Bk = p.meta["K"], p.meta["block_k"]
     gi, gv = fused(d, K, Bk, row_chunk=4096)
-    rows = sample_rows(p, n_stride=6)
-    o = [oracle.row_logits(dq, t) for t in rows]
-    topk_ok(gi.cpu().numpy()[rows], gv.cpu().numpy()[rows], o, p.ks[rows], K)
+    rows = sample_rows(dq, p.meta, n_stride=8)
+    _check_rows(d, dq, rows, gi.cpu().numpy(), gv.cpu().numpy(), K)
     # row-count invariance: other row chunks give identical bits
     gi2, gv2 = fused(d, K, Bk, row_chunk=1024)
     assert torch.equal(gi, gi2) and torch.equal(gv.view(torch.int32), gv2.view(torch.int32))
     # the row-chunked dense comparator under a 2 GiB fp32 logits budget
-    W = p.W
+    W = d.W
     chunk = (2 << 30) // (4 * W)
     buf = torch.empty((chunk, W), dtype=torch.float32, device="cuda")
     Kc = idx.candidate_capacity(K)
@@ -125,12 +147,7 @@ def test_long_ctx_fused_vs_rowchunked_dense():
 def test_ragged_candidates_and_masked_consumer():
     p, d, dq = prob("ragged_cand")
     c = p.meta
-    # windows built on the device from cu_seqlens match the host reading
-    cu_q = torch.tensor(c["cu_q"], dtype=torch.int32, device="cuda")
-    cu_k = torch.tensor(c["cu_k"], dtype=torch.int32, device="cuda")
-    ks, ke = idx.idx_ragged_windows(cu_q, cu_k, p.T)
-    assert torch.equal(ks.cpu(), torch.from_numpy(p.ks)) and torch.equal(ke.cpu(), torch.from_numpy(p.ke))
-    W = p.W
+    W = d.W
     n_blocks, pool, K = c["n_blocks"], c["pool"], c["K"]
     blocks = torch.empty((p.T, n_blocks), dtype=torch.int32, device="cuda")
     ws = torch.empty(idx.idx_workspace_size(idx.IDX_OP_BLOCK_CANDIDATES, d, block_k=c["block_k"], row_chunk=4096,
@@ -139,8 +156,8 @@ def test_ragged_candidates_and_masked_consumer():
                                        out_blocks=blocks, ws=ws)
     torch.cuda.synchronize()
     assert idx.overflow_count(ws) == 0
-    rows = sample_rows(p, n_stride=8)
-    o = [oracle.row_logits(dq, t) for t in rows]
+    rows = sample_rows(dq, p.meta, n_stride=8)
+    o = oracle.rows_logits(dq, rows)
     mk = mask[rows].cpu().numpy()
     bk = blocks[rows].cpu().numpy()
     for i, (t, v) in enumerate(zip(rows, o)):
@@ -158,9 +175,9 @@ def test_ragged_candidates_and_masked_consumer():
     d2 = idx.Inputs.from_host(p2)
     gi, gv = fused(d2, K, c["block_k"], row_chunk=4096, mask=mask)
     dq2 = oracle.Dequantised(p2)
-    o2 = [oracle.row_logits(dq2, t) for t in rows]
+    o2 = oracle.rows_logits(dq2, rows)
     allowed = [mk[i][:len(o2[i])].astype(bool) for i in range(len(rows))]
-    topk_ok(gi.cpu().numpy()[rows], gv.cpu().numpy()[rows], o2, p.ks[rows], K, allowed=allowed)
+    topk_ok(gi.cpu().numpy()[rows], gv.cpu().numpy()[rows], o2, dq.ks[rows], K, allowed=allowed)
     # the same consumer reading the block ids instead of the byte mask: identical output
     bi, bv = idx.idx_logits_topk_fused_blocks(d2, K, blocks, pool=pool, block_k=c["block_k"], row_chunk=4096)
     assert torch.equal(bi, gi) and torch.equal(bv.view(torch.int32), gv.view(torch.int32))

@@ -1,6 +1,7 @@
-"""Pins of the fp64 CPU oracle against things other than itself: library decoders,
-hand-worked fixtures (tests/golden), closed forms, invariants and the pages'
-key-blocked top-k identity.  CPU only."""
+"""Pins of the fp64 CPU oracle (oracle/oracle.cpp) against things other than itself:
+library decoders, hand-worked fixtures (tests/golden), numpy's fp64 einsum and sort
+on small inputs, closed forms, invariants and the pages' key-blocked top-k identity.
+CPU only."""
 import json
 import os
 
@@ -144,7 +145,7 @@ def test_nonnegative_inputs_are_linear():
     for t in range(p.T):
         got = oracle.row_logits(dq, t)
         qsum = (dq.w[t][:, None] * dq.qd[t]).sum(0)
-        want = dq.kd[p.ks[t]:p.ke[t]] @ qsum
+        want = dq.kd[dq.ks[t]:dq.ke[t]] @ qsum
         np.testing.assert_allclose(got, want, rtol=1e-12, atol=0)
 
 
@@ -159,30 +160,31 @@ def test_relu_kills_negated_heads():
     p2.q[0, 1] ^= 0x80
     p2.q[0, 1][p.q[0, 1] == 0] = 0
     neg = oracle.row_logits(oracle.Dequantised(p2), 0)
-    d1 = dq.qd[0, 1] @ dq.kd[:p.ke[0]].T
+    d1 = dq.qd[0, 1] @ dq.kd[:dq.ke[0]].T
     np.testing.assert_allclose(base - neg, dq.w[0, 1] * d1, rtol=1e-12, atol=1e-9)
 
 
 def test_scale_homogeneity_and_head_permutation():
     p = _small(T=4, L=256, H=8)
-    base = oracle.dense_logits(oracle.Dequantised(p), range(p.T), p.W)
+    W = oracle.Dequantised(p).W
+    base = oracle.dense_logits(oracle.Dequantised(p), range(p.T), W)
     for field in ("w", "k_scale", "q_scale"):
         p2 = synth.Problem(**{**p.__dict__})
         setattr(p2, field, getattr(p, field) * np.float32(2))
-        got = oracle.dense_logits(oracle.Dequantised(p2), range(p.T), p.W)
+        got = oracle.dense_logits(oracle.Dequantised(p2), range(p.T), W)
         assert np.array_equal(got, 2 * base), field
     p2 = synth.Problem(**{**p.__dict__})
     p2.scale = 4.0
-    assert np.array_equal(oracle.dense_logits(oracle.Dequantised(p2), range(p.T), p.W), 4 * base)
+    assert np.array_equal(oracle.dense_logits(oracle.Dequantised(p2), range(p.T), W), 4 * base)
     perm = np.random.default_rng(0).permutation(p.H)
     p3 = synth.Problem(**{**p.__dict__})
     p3.q, p3.q_scale, p3.w = p.q[:, perm], p.q_scale[:, perm], p.w[:, perm]
-    np.testing.assert_allclose(oracle.dense_logits(oracle.Dequantised(p3), range(p.T), p.W), base,
+    np.testing.assert_allclose(oracle.dense_logits(oracle.Dequantised(p3), range(p.T), W), base,
                                rtol=1e-12)
     # weights permuted alone must change the result (w is tied to its head)
     p4 = synth.Problem(**{**p.__dict__})
     p4.w = p.w[:, perm]
-    assert not np.allclose(oracle.dense_logits(oracle.Dequantised(p4), range(p.T), p.W), base)
+    assert not np.allclose(oracle.dense_logits(oracle.Dequantised(p4), range(p.T), W), base)
 
 
 def test_key_permutation_equivariance():
@@ -205,8 +207,9 @@ def test_mxfp4_equals_fp8_when_representable():
     assert np.array_equal(oracle.decode_e4m3(codes) * s[:, None], kd)   # exact re-encoding
     p8 = synth.Problem(**{**p.__dict__})
     p8.k, p8.k_scale, p8.k_fmt = codes, s.astype(np.float32), 0
-    a = oracle.dense_logits(oracle.Dequantised(p), range(p.T), p.W)
-    b = oracle.dense_logits(oracle.Dequantised(p8), range(p.T), p.W)
+    W = oracle.Dequantised(p).W
+    a = oracle.dense_logits(oracle.Dequantised(p), range(p.T), W)
+    b = oracle.dense_logits(oracle.Dequantised(p8), range(p.T), W)
     np.testing.assert_allclose(a, b, rtol=1e-13)
 
 
@@ -215,15 +218,15 @@ def test_windows_bound_the_row():
     dq = oracle.Dequantised(p)
     for t in range(p.T):
         v = oracle.row_logits(dq, t)
-        assert len(v) == p.ke[t] - p.ks[t] == p.L - p.T + t + 1
+        assert len(v) == dq.ke[t] - dq.ks[t] == p.L - p.T + t + 1
     # shrinking a window from either side keeps the surviving keys' logits
     full = oracle.row_logits(dq, 5)
     p2 = synth.Problem(**{**p.__dict__})
-    p2.ks = p.ks.copy()
-    p2.ke = p.ke.copy()
+    p2.ks = dq.ks.astype(np.int32)
+    p2.ke = dq.ke.astype(np.int32)
     p2.ks[5], p2.ke[5] = 17, 311
     part = oracle.row_logits(oracle.Dequantised(p2), 5)
-    np.testing.assert_allclose(part, full[17:311], rtol=1e-13)  # BLAS blocking may differ
+    assert np.array_equal(part, full[17:311])
 
 
 # ----------------------------------------------------------------- top-K
@@ -310,15 +313,15 @@ def test_candidates_counts_and_noop_invariant():
     for t in range(p.T):
         v = oracle.row_logits(dq, t)
         for nb in (16, 64, 1000):
-            mask, blocks = oracle.block_candidates_row(v, 8, nb, p.W)
+            mask, blocks = oracle.block_candidates_row(v, 8, nb, dq.W)
             assert len(blocks) == min(nb, -(-len(v) // 8))
             assert not mask[len(v):].any()
             assert mask.sum() == sum(min(8, len(v) - 8 * b) for b in blocks)
             if nb >= K:
                 # each selected key's block has max >= v_K, so at most K blocks precede or tie it:
                 # masking with the candidates of the same logits is a no-op for top-K (K <= n_blocks)
-                a, _ = oracle.topk_row(v, p.ks[t], K, mask[:len(v)].astype(bool))
-                b, _ = oracle.topk_row(v, p.ks[t], K)
+                a, _ = oracle.topk_row(v, dq.ks[t], K, mask[:len(v)].astype(bool))
+                b, _ = oracle.topk_row(v, dq.ks[t], K)
                 assert np.array_equal(a, b)
 
 
@@ -370,46 +373,61 @@ def test_ratio_windows_invariants():
                     assert ke[rows[-1]] == cu_c[i + 1]
 
 
-# ----------------------------------------------------------------- head-term size
-def test_magnitude_closed_form_and_sign_pins():
-    """oracle.row_magnitude = sum_h |w_h| ReLU(dot_h).  Pinned against: a hand-worked
-    one-hot case with a negative weight; |w| == w for non-negative weights (equal to the
-    logits bitwise); negating every weight negates the logits and keeps the sizes; the
-    sizes bound the logits (triangle inequality); splitting the weights by sign gives the
-    logits as (positive part) - (negative part) and the sizes as their sum."""
-    T, L, H, D = 1, 4, 2, 128
-    q = np.zeros((T, H, D), np.uint8)
-    q[0, :, 5] = [0x38, 0x40]                      # head 0: 1, head 1: 2
-    k = np.zeros((L, D), np.uint8)
-    k[:, 5] = [0x38, 0xB8, 0x40, 0x00]             # 1, -1, 2, 0
-    w = np.array([[0.5, -0.25]], np.float32)
-    p = synth.Problem(q=q, q_scale=np.ones((T, H), np.float32), k=k, k_scale=np.ones(L, np.float32), k_fmt=0,
-                      w=w, ks=np.array([0], np.int32), ke=np.array([L], np.int32))
+# ----------------------------------------------------------------- library routines
+@pytest.mark.parametrize("k_fmt,H", [(0, 4), (1, 8), (0, 32)])
+def test_row_logits_match_numpy_einsum(k_fmt, H):
+    """The C++ loops against numpy's fp64 einsum over dequantised arrays that numpy builds
+    itself (torch's E4M3 / E8M0 conversions, the E2M1 table): a dropped term, a swapped
+    operand, a wrong scale or nibble order fails here."""
+    T, L, D = 5, 700, 128
+    rng = np.random.default_rng(k_fmt * 10 + H)
+    cu_q = np.array([0, 2, 5], np.int32)
+    cu_k = np.array([0, 301, 700], np.int32)
+    p = synth.make_problem(T, L, H, k_fmt=k_fmt, seed=H + k_fmt, cu_q=cu_q, cu_k=cu_k, w_lo=-1.0, scale=0.625)
+    p.q_scale = (p.q_scale * np.exp2(rng.integers(-3, 4, p.q_scale.shape))).astype(np.float32)
+    q = torch.from_numpy(p.q).view(torch.float8_e4m3fn).to(torch.float64).numpy() * p.q_scale[..., None]
+    if k_fmt == 0:
+        k = torch.from_numpy(p.k).view(torch.float8_e4m3fn).to(torch.float64).numpy() * p.k_scale[:, None]
+    else:
+        table = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0.0, -.5, -1, -1.5, -2, -3, -4, -6])
+        el = np.stack([table[p.k & 0xF], table[p.k >> 4]], axis=-1).reshape(L, D)
+        sc = torch.from_numpy(p.k_scale).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+        k = el * np.repeat(sc, 32, axis=1)
     dq = oracle.Dequantised(p)
-    # dots: head 0 -> [1, -1, 2, 0], head 1 -> [2, -2, 4, 0]
-    assert oracle.row_logits(dq, 0).tolist() == [0.5 - 0.5, 0.0, 1.0 - 1.0, 0.0]
-    assert oracle.row_magnitude(dq, 0).tolist() == [0.5 + 0.5, 0.0, 1.0 + 1.0, 0.0]
+    for t in range(T):
+        lo, hi = dq.ks[t], dq.ke[t]
+        dots = np.einsum("hd,sd->hs", q[t], k[lo:hi]) * p.scale
+        want = np.einsum("h,hs->s", p.w[t].astype(np.float64), np.maximum(dots, 0.0))
+        np.testing.assert_allclose(oracle.row_logits(dq, t), want, rtol=1e-12, atol=1e-12)
 
-    p = _small(T=3, L=300, H=8)
-    dq = oracle.Dequantised(p)
-    for t in range(p.T):
-        assert np.array_equal(oracle.row_magnitude(dq, t), oracle.row_logits(dq, t))   # w >= 0 here
-    pn = synth.Problem(**{**p.__dict__})
-    pn.w = -p.w
-    dqn = oracle.Dequantised(pn)
-    pm = synth.Problem(**{**p.__dict__})
-    sign = np.where(np.random.default_rng(2).random(p.w.shape) < 0.5, -1.0, 1.0).astype(np.float32)
-    pm.w = p.w * sign
-    dqm = oracle.Dequantised(pm)
-    pp, pq = synth.Problem(**{**p.__dict__}), synth.Problem(**{**p.__dict__})
-    pp.w = np.where(sign > 0, p.w, 0).astype(np.float32)
-    pq.w = np.where(sign < 0, p.w, 0).astype(np.float32)
-    dqp, dqq = oracle.Dequantised(pp), oracle.Dequantised(pq)
-    for t in range(p.T):
-        assert np.array_equal(oracle.row_logits(dqn, t), -oracle.row_logits(dq, t))
-        assert np.array_equal(oracle.row_magnitude(dqn, t), oracle.row_magnitude(dq, t))
-        m, v = oracle.row_magnitude(dqm, t), oracle.row_logits(dqm, t)
-        assert (m >= np.abs(v) - 1e-12 * m).all()
-        a, b = oracle.row_logits(dqp, t), oracle.row_logits(dqq, t)
-        np.testing.assert_allclose(v, a - b, rtol=1e-12, atol=1e-12 * m.max())
-        np.testing.assert_allclose(m, a + b, rtol=1e-12, atol=0)
+
+def test_topk_row_matches_numpy_sort():
+    """Selection against numpy's lexsort on the fp32-rounded values (value desc, index asc),
+    rows with exact ties, signed zeros and masks."""
+    rng = np.random.default_rng(23)
+    for trial in range(40):
+        n = int(rng.integers(1, 600))
+        K = int(rng.integers(1, 80))
+        v = np.round(rng.normal(size=n), int(rng.integers(0, 4)))
+        v[rng.random(n) < 0.1] = -0.0
+        allowed = rng.random(n) < 0.7 if trial % 2 else None
+        idx, val = oracle.topk_row(v, 9, K, allowed)
+        pos = np.arange(n) if allowed is None else np.nonzero(allowed)[0]
+        v32 = v[pos].astype(np.float32).astype(np.float64)
+        order = np.lexsort((pos, -v32))
+        want = np.sort(pos[order[:K]])
+        assert idx[:len(want)].tolist() == (want + 9).tolist() and (idx[len(want):] == -1).all()
+        assert np.array_equal(val[:len(want)], v[want].astype(np.float32))
+
+
+def test_ragged_windows_hand_examples():
+    """Worked by hand: one request is the chunk at the tail of its prefix (ks = 0,
+    ke = L - T + t + 1); a batch of a 3-token request and a 2-new-token request on a
+    5-token prefix; an empty request."""
+    ks, ke = oracle.ragged_windows([0, 4], [0, 10])
+    assert ks.tolist() == [0, 0, 0, 0] and ke.tolist() == [7, 8, 9, 10]
+    ks, ke = oracle.ragged_windows([0, 3, 5], [0, 3, 10])
+    assert ks.tolist() == [0, 0, 0, 3, 3]
+    assert ke.tolist() == [1, 2, 3, 9, 10]
+    ks, ke = oracle.ragged_windows([0, 2, 2, 3], [0, 2, 6, 8])
+    assert ks.tolist() == [0, 0, 6] and ke.tolist() == [1, 2, 8]

@@ -55,12 +55,6 @@ def test_reproducible_and_seed_dependent():
     assert np.array_equal(synth.normal(3, 4, 10, first=500), synth.normal(3, 4, 1000)[500:510])
 
 
-def test_ragged_windows_layout():
-    ks, ke = synth.ragged_windows([0, 3, 5], [0, 3, 10])
-    assert ks.tolist() == [0, 0, 0, 3, 3]
-    assert ke.tolist() == [1, 2, 3, 9, 10]   # request 1: prefix 5, rows see 6 and 7 keys
-
-
 def test_duplicate_rows_are_byte_copies():
     p = synth.make_problem(4, 1000, 4, k_fmt=synth.K_MXFP4, dup_rows=50)
     dst, src = p.meta["dup_dst"], p.meta["dup_src"]
