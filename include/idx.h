@@ -162,6 +162,24 @@ idx_status idx_logits_topk_fused(const idx_problem *p, int32_t K, int32_t block_
                                  const uint8_t *mask, int64_t ld_mask, int32_t *out_idx,
                                  float *out_val, void *ws, size_t ws_bytes, void *stream);
 
+/* Size of the library's own workspace for idx_logits_topk_fused_static: 128 MiB of device
+ * memory per GPU the library is loaded on, held until the process ends. */
+#define IDX_STATIC_WS_BYTES (128u << 20)
+
+/* For callers that cannot allocate device memory (code under stream capture, tight serving
+ * loops, harnesses that forbid hipMalloc): idx_logits_topk_fused with the library's static
+ * workspace instead of a caller buffer.  Arguments, outputs and results are those of
+ * idx_logits_topk_fused.  Returns IDX_E_WORKSPACE (nothing enqueued) when the call needs more
+ * than IDX_STATIC_WS_BYTES, i.e. idx_workspace_size(IDX_OP_LOGITS_TOPK_FUSED, ...) is larger:
+ * a smaller row_chunk fits (256 rows do for block_k 32768 at any K).  No memory is
+ * allocated or freed.  The workspace keeps the last
+ * call's contents, and the overflow word that idx_logits_topk_fused leaves in its first 4
+ * bytes is not visible to the caller.  Every call on one GPU shares the workspace: calls
+ * that overlap in time on the same GPU (two streams, two host threads) race. */
+idx_status idx_logits_topk_fused_static(const idx_problem *p, int32_t K, int32_t block_k, int32_t row_chunk,
+                                        const uint8_t *mask, int64_t ld_mask, int32_t *out_idx, float *out_val,
+                                        void *stream);
+
 /* The fused indexer with the index -> KV-slot transform in its final write (P3:
  * the top-k kernel with the transform fused in; P2 Accuracy/equivalence:
  * page_indices published next to raw_indices).  As idx_logits_topk_fused, plus

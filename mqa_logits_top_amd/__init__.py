@@ -34,7 +34,8 @@ STATUS = {0: "IDX_OK", 1: "IDX_E_NULL", 2: "IDX_E_SHAPE", 3: "IDX_E_PARAM", 4: "
           5: "IDX_E_WORKSPACE", 6: "IDX_E_UNSUPPORTED", 7: "IDX_E_LAUNCH", 8: "IDX_E_ALIGN"}
 
 EXPORTS = ("idx_mqa_logits", "idx_mqa_logits_block", "idx_topk", "idx_logits_topk_fused",
-           "idx_logits_topk_fused_paged", "idx_logits_topk_fused_blocks", "idx_refine_topk",
+           "idx_logits_topk_fused_paged", "idx_logits_topk_fused_blocks", "idx_logits_topk_fused_static",
+           "idx_refine_topk",
            "idx_block_candidates", "idx_workspace_size", "idx_ragged_windows", "idx_ragged_windows_ratio",
            "idx_gather_rows", "idx_tail_rows", "idx_status_str")
 
@@ -71,6 +72,7 @@ def load_library():
     lib.idx_logits_topk_fused.argtypes = [P, i32, i32, i32, VP, i64, VP, VP, VP, sz, VP]
     lib.idx_logits_topk_fused_paged.argtypes = [P, i32, i32, i32, VP, i64, VP, VP, VP, VP, VP, sz, VP]
     lib.idx_logits_topk_fused_blocks.argtypes = [P, i32, i32, i32, VP, i64, i32, i32, VP, VP, VP, sz, VP]
+    lib.idx_logits_topk_fused_static.argtypes = [P, i32, i32, i32, VP, i64, VP, VP, VP]
     lib.idx_refine_topk.argtypes = [P, VP, VP, i64, i32, i32, i32, VP, VP, VP, sz, VP]
     lib.idx_block_candidates.argtypes = [P, VP, i64, i32, i32, i32, i32, VP, i64, i32, VP, VP, sz, VP]
     lib.idx_workspace_size.argtypes = [i32, P, i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
@@ -279,6 +281,27 @@ def idx_logits_topk_fused_blocks(p: Inputs, K: int, blocks: torch.Tensor, pool: 
     _check("idx_logits_topk_fused_blocks", load_library().idx_logits_topk_fused_blocks(
         ctypes.byref(s), K, block_k, row_chunk, _ptr(blocks), blocks.stride(0), int(blocks.shape[1]), pool,
         _ptr(out_idx), _ptr(out_val), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+    return out_idx, out_val
+
+
+STATIC_WS_BYTES = 128 << 20   # IDX_STATIC_WS_BYTES
+
+
+def idx_logits_topk_fused_static(p: Inputs, K: int, block_k: int = 32768, row_chunk: int = 0,
+                                 mask: Optional[torch.Tensor] = None, out_idx: Optional[torch.Tensor] = None,
+                                 out_val: Optional[torch.Tensor] = None, with_values: bool = True, stream=None):
+    """idx_logits_topk_fused on the library's static workspace: no workspace argument, and the
+    library allocates nothing (the outputs are the caller's; they are allocated here only when
+    not given)."""
+    dev = p.q.device
+    if out_idx is None:
+        out_idx = torch.empty((p.T, K), dtype=torch.int32, device=dev)
+    if out_val is None and with_values:
+        out_val = torch.empty((p.T, K), dtype=torch.float32, device=dev)
+    s = p.struct()
+    _check("idx_logits_topk_fused_static", load_library().idx_logits_topk_fused_static(
+        ctypes.byref(s), K, block_k, row_chunk, _ptr(mask), mask.stride(0) if mask is not None else 0,
+        _ptr(out_idx), _ptr(out_val), _stream(stream)))
     return out_idx, out_val
 
 

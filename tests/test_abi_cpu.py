@@ -174,6 +174,22 @@ def test_workspace_sizes(lib):
     assert lib.idx_workspace_size(9, ctypes.byref(p), 1, 256, 0, 0, 0, 0, ctypes.byref(n)) == 3
 
 
+def test_static_workspace_limit(lib):
+    """The allocation-free fused entry refuses, on the host, a call whose workspace would exceed
+    IDX_STATIC_WS_BYTES, and checks its arguments like the entry with a caller workspace."""
+    f = 1 << 20
+    big = _problem(T=2048, L=65536)
+    call = lambda p, K=2048, bk=32768, rc=0, oi=f: lib.idx_logits_topk_fused_static(
+        ctypes.byref(p), K, bk, rc, None, 0, oi, None, None)
+    assert call(big) == 5                      # WORKSPACE: 2048 rows x 65536 keys per launch
+    assert call(big, rc=256, oi=None) == 1     # NULL output, checked before the workspace lookup
+    assert call(big, rc=256, K=0) == 3         # PARAM
+    assert call(_problem(D=64), rc=256) == 6   # UNSUPPORTED
+    n = ctypes.c_size_t()
+    assert lib.idx_workspace_size(2, ctypes.byref(big), 2048, 32768, 256, 0, 0, 0, ctypes.byref(n)) == 0
+    assert n.value <= idx.STATIC_WS_BYTES
+
+
 def test_refine_validation(lib):
     p = _problem()
     f = 1 << 20
