@@ -229,7 +229,8 @@ idx_status idx_refine_topk(const idx_problem *p, const int32_t *cand_idx, const 
  * logits != NULL: read dense row-relative logits [T, ld] (idx_mqa_logits layout;
  * q/k/w of p are not read) and select exactly on them.  logits == NULL: score
  * from p block by block (block_k keys, row_chunk rows) and settle the block
- * boundary exactly as idx_refine_topk does; requires ks[t] % pool == 0.
+ * boundary exactly as idx_refine_topk does; blocks start at each row's ks[t] whatever its
+ * alignment.
  * out_blocks (nullable): [T, n_blocks] int32 kept block ids, ascending, -1 padded. */
 idx_status idx_block_candidates(const idx_problem *p, const float *logits, int64_t ld, int32_t pool,
                                 int32_t n_blocks, int32_t block_k, int32_t row_chunk, uint8_t *mask,

@@ -71,7 +71,8 @@ hipError_t launch_slab_check(const uint32_t *ccnt, int32_t nshares, const float 
 //   TOPK_DENSE:        ks[t] + c              (absolute key; row-relative logits)
 //   TOPK_BLOCK:        key0 + c               (absolute key; key-block scratch)
 //   TOPK_POOL_DENSE:   c                      (pooled block id; row-relative)
-//   TOPK_POOL_BLOCK:   (key0 - ks[t]) / pool + c   (pooled block id; key-block scratch)
+//   TOPK_POOL_BLOCK:   key0 / pool - ks[t] / pool + c   (pooled block id; key-block scratch whose
+//                      column c holds the block that starts in key group key0 / pool + c)
 // Valid ids are [ks, ke) for keys and [0, ceil((ke - ks) / pool)) for blocks.
 enum TopkMode { TOPK_DENSE = 0, TOPK_BLOCK = 1, TOPK_POOL_DENSE = 2, TOPK_POOL_BLOCK = 3 };
 struct TopkArgs {

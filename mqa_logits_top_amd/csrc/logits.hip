@@ -132,7 +132,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((MODE =
 
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf[3][STAGE];
   __shared__ __attribute__((aligned(256))) uint32_t sbuf[3][TK];
-  __shared__ int32_t wg_range[2];
+  __shared__ int32_t wg_range[3];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -176,16 +176,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((MODE =
 
   // ---- key range of this workgroup: its split, clipped to the union of its rows' windows
   if (wave == 0) {
-    int lo = INT_MAX, hi = INT_MIN;
+    int lo = INT_MAX, hi = INT_MIN, odd = 0;
     if (lane < RPW && r_begin + lane < r_end) {
       const int kst = max(a.ks[r_begin + lane], 0), ket = min(a.ke[r_begin + lane], a.L);
-      if (ket > kst) { lo = kst; hi = ket; }
+      if (ket > kst) { lo = kst; hi = ket; odd = kst & 7; }
     }
     for (int off = 32; off > 0; off >>= 1) {
       lo = min(lo, __shfl_xor(lo, off));
       hi = max(hi, __shfl_xor(hi, off));
+      odd |= __shfl_xor(odd, off);
     }
-    if (lane == 0) { wg_range[0] = lo; wg_range[1] = hi; }
+    if (lane == 0) { wg_range[0] = lo; wg_range[1] = hi; wg_range[2] = odd; }
   }
   __syncthreads();
   int s_lo, s_hi;
@@ -212,7 +213,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((MODE =
   const int intiles = s_lo < s_hi ? (s_hi - itile0 + TK - 1) / TK : 0;
   const int pt0 = part * intiles / nparts, pt1 = (part + 1) * intiles / nparts;
   const int tile0 = itile0 + pt0 * TK;
-  const int ntiles = pt1 - pt0;
+  // Pooled blocks start at each row's ks; this part stores the blocks that start in its own
+  // keys [own_lo, own_hi).  When a row's ks is not a multiple of 8, the last such block ends
+  // past own_hi, so the part scores one more tile (its keys only complete that block).
+  const int own_lo = max(s_lo, tile0), own_hi = min(s_hi, tile0 + (pt1 - pt0) * TK);
+  const bool extend = MODE == STORE_POOL8 && wg_range[2] != 0 && pt1 > pt0 && tile0 + (pt1 - pt0) * TK < a.L;
+  const int ntiles = pt1 - pt0 + (extend ? 1 : 0);
   // candidate share of this part in each of its rows' slabs
   const int share0 = part * a.caps / nparts, share = (part + 1) * a.caps / nparts - share0;
   constexpr bool cand = MODE == STORE_CAND || MODE == STORE_SLAB;
@@ -319,6 +325,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((MODE =
   if (ntiles > 1) vm_wait_barrier<LPT>();
   else vm_wait_barrier<0>();
 
+  // pooled blocks: this row's block offset inside an octet, and (lanes 14, 15) the head of the
+  // block that started in the last octet of the previous batch, completed in the next one
+  const int rr = kst & 7;
+  float pend = -__builtin_inff();
   // 16-byte stores need a 16-byte aligned element offset
   const bool row_al = (((uintptr_t)a.out & 15) == 0) && ((ld & 3) == 0) &&
                       ((MODE == STORE_DENSE ? kst : a.key_lo) & 3) == 0;
@@ -415,14 +425,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((MODE =
           }
         }
       } else {
-        // max over the 8 aligned keys s0 & ~7 .. + 7: this lane's 4, then its neighbour's
-        float m = -__builtin_inff();
+        // 8-key blocks of the row start at ks: the block starting in octet o (keys 8 o .. 8 o + 7,
+        // held by lanes 2 m, 2 m + 1) is keys 8 o + r .. 8 o + r + 7, r = ks & 7.  hi: the octet's
+        // in-window keys at positions >= r (the head of its block); lo: those at positions < r
+        // (the tail of the block that started one octet before).
+        float hi = -__builtin_inff(), lo = -__builtin_inff();
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (s0 + j >= v_lo && s0 + j < v_hi) m = __builtin_fmaxf(m, val[j]);
-        m = __builtin_fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, false)));
-        const int col = (s0 - a.key_lo) >> 3;
-        const bool st = writer && (n16 & 1) == 0 && m != -__builtin_inff() && col < a.wcols;
+        for (int j = 0; j < 4; ++j) {
+          const int s = s0 + j;
+          const bool in = s >= kst && s < ket;
+          if (in && (s & 7) >= rr) hi = __builtin_fmaxf(hi, val[j]);
+          if (in && (s & 7) < rr) lo = __builtin_fmaxf(lo, val[j]);
+        }
+        hi = __builtin_fmaxf(hi, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(hi), 0xB1, 0xF, 0xF, false)));
+        lo = __builtin_fmaxf(lo, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(lo), 0xB1, 0xF, 0xF, false)));
+        // the next octet's tail: two lanes up (row rotate right by 14); lanes 14, 15 receive the
+        // tail of this batch's first octet, which completes the block they held back last batch
+        const float nlo = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(lo), 0x12E, 0xF, 0xF, false));
+        int bo = s0 >> 3;   // octet of the block start stored now
+        float m = rr ? __builtin_fmaxf(hi, nlo) : hi;
+        if (rr && n16 >= 14) {
+          m = __builtin_fmaxf(pend, nlo);
+          bo -= 8;
+          pend = hi;
+        }
+        const int bs = 8 * bo + rr;                  // the block's first key
+        const int col = bo - (a.key_lo >> 3);
+        const bool st = writer && (n16 & 1) == 0 && bs >= kst && bs < ket && bs >= own_lo && bs < own_hi &&
+                        col < a.wcols;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), orsrc, st ? (obase + col) * 4 : OOB, 0, 0);
       }
     }

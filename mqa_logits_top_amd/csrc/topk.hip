@@ -252,7 +252,9 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     case TOPK_DENSE: off = ks; id_lo = ks; id_hi = ke; break;
     case TOPK_BLOCK: off = a.key0; id_lo = ks; id_hi = ke; break;
     case TOPK_POOL_DENSE: off = 0; id_lo = 0; id_hi = (ke - ks + a.pool - 1) / a.pool; break;
-    default: off = (a.key0 - ks) / a.pool; id_lo = 0; id_hi = (ke - ks + a.pool - 1) / a.pool; break;
+    // column c holds the block whose first key lies in octet key0 / pool + c; the row's block b
+    // starts in octet ks / pool + b (blocks start at ks)
+    default: off = a.key0 / a.pool - ks / a.pool; id_lo = 0; id_hi = (ke - ks + a.pool - 1) / a.pool; break;
   }
   const int c_lo = max(id_lo - off, 0);
   const int c_hi = min(id_hi - off, a.ncols);
@@ -332,7 +334,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     if (osum == 0 && tot_c <= (uint32_t)CAPK && a.caps <= CAPS_MAX && ne <= NTH) {  // uniform
       // the shares hold their candidates in id order and cover consecutive key ranges,
       // so appending them after the running list keeps the items in id order
-      if (tid < ne) { sm.hist[tid] = ex; sm.hist[NTH + tid] = cw & 0xFFFF0000u | cs; }
+      if (tid < ne) { sm.hist[tid] = ex; sm.hist[NTH + tid] = (cw & 0xFFFF0000u) | cs; }
       __syncthreads();
       // wave w gathers shares w, w + 8, ..., all of a share's loads in flight at once
       for (int e = wave; e < ne; e += NWV) {

@@ -73,10 +73,6 @@ def case(request):
     return _make_case(request.param)
 
 
-def _pool_aligned(dq):
-    return bool((dq.ks % 8 == 0).all())
-
-
 def _vals(c, gv):
     """Selected values are held to the logit bar only for non-negative head weights."""
     return None if c.mixed else gv
@@ -219,8 +215,6 @@ def test_gathered_rows_equal_full_rows(case):
             assert (si[r] == -1).all()
         else:
             assert torch.equal(si[r], fi[t]) and torch.equal(sv[r].view(torch.int32), fv[t].view(torch.int32))
-    if not _pool_aligned(case.dq):
-        return
     mf, _ = idx.idx_block_candidates(d, W, n_blocks=16, block_k=512)
     ms, _ = idx.idx_block_candidates(sub, W, n_blocks=16, block_k=512)
     for r, t in enumerate(rows):
@@ -314,9 +308,8 @@ def test_candidates_dense_and_fused(case, n_blocks):
         om, ob = oracle.block_candidates_row(win, 8, n_blocks, W)
         assert np.array_equal(md[t], om), f"dense mask row {t}"
         assert bd[t][bd[t] >= 0].tolist() == ob.tolist(), f"dense blocks row {t}"
-    if not _pool_aligned(dq):
-        return
-    # fused: scored from q/k with an exact boundary, against the fp64 oracle
+    # fused: scored from q/k with an exact boundary, against the fp64 oracle (random windows:
+    # blocks start at ks, which is mostly not a multiple of 8)
     blocks_f = torch.empty((p.T, n_blocks), dtype=torch.int32, device="cuda")
     mask_f, _ = idx.idx_block_candidates(d, W, n_blocks=n_blocks, block_k=512, row_chunk=16, out_blocks=blocks_f)
     _check_candidates(dq, o, mask_f.cpu().numpy(), blocks_f.cpu().numpy(), n_blocks)
@@ -514,3 +507,44 @@ def test_ragged_short_requests_row_block_layout():
     blocks = torch.empty((T, n_blocks), dtype=torch.int32, device="cuda")
     mask, _ = idx.idx_block_candidates(d, W, n_blocks=n_blocks, block_k=1024, row_chunk=512, out_blocks=blocks)
     _check_candidates(dq, o, mask.cpu().numpy(), blocks.cpu().numpy(), n_blocks)
+
+
+@pytest.mark.parametrize("k_fmt,H,block_k,row_chunk,n_blocks", [
+    (synth.K_FP8, 64, 1024, 0, 40),
+    (synth.K_MXFP4, 32, 512, 16, 7),
+    (synth.K_FP8, 32, 4096, 64, 300),
+])
+def test_fused_candidates_unaligned_windows(k_fmt, H, block_k, row_chunk, n_blocks):
+    """Candidate blocks start at each row's ks, here mostly not a multiple of 8: requests of a
+    varlen batch that start at odd key rows, one of them on a prefix, an empty one, so blocks
+    straddle key splits, key launches and the row-block layout's ranges.  The fused candidate
+    source matches the oracle's blocks and masks; the block-list consumer reads them back."""
+    cu_q = np.array([0, 37, 80, 80, 141, 190], np.int32)
+    cu_k = np.array([0, 1003, 2701, 3105, 6007, 9999], np.int32)
+    T, L = int(cu_q[-1]), int(cu_k[-1])
+    p = synth.make_problem(T, L, H, k_fmt=k_fmt, seed=H + block_k, cu_q=cu_q, cu_k=cu_k)
+    d = dev(p)
+    dq = oracle.Dequantised(p)
+    windows_match(d, dq)
+    assert (dq.ks % 8 != 0).sum() >= T // 2
+    o = oracle.rows_logits(dq, range(T))
+    W = max(d.W, 1)
+    blocks = torch.empty((T, n_blocks), dtype=torch.int32, device="cuda")
+    ws = torch.empty(idx.idx_workspace_size(idx.IDX_OP_BLOCK_CANDIDATES, d, block_k=block_k, row_chunk=row_chunk,
+                                            pool=8, n_blocks=n_blocks), dtype=torch.uint8, device="cuda")
+    mask, _ = idx.idx_block_candidates(d, W, n_blocks=n_blocks, block_k=block_k, row_chunk=row_chunk,
+                                       out_blocks=blocks, ws=ws)
+    torch.cuda.synchronize()
+    assert idx.overflow_count(ws) == 0
+    _check_candidates(dq, o, mask.cpu().numpy(), blocks.cpu().numpy(), n_blocks)
+    # another key blocking gives the same blocks
+    m2, _ = idx.idx_block_candidates(d, W, n_blocks=n_blocks, block_k=256, row_chunk=0)
+    assert torch.equal(m2, mask)
+    # the consumer of those block ids equals the byte-mask consumer and the oracle's masked top-K
+    K = 24
+    bi, bv = idx.idx_logits_topk_fused_blocks(d, K, blocks, pool=8, block_k=block_k, row_chunk=row_chunk)
+    mi, mv = idx.idx_logits_topk_fused(d, K, block_k=block_k, row_chunk=row_chunk, mask=mask)
+    assert torch.equal(bi, mi) and torch.equal(bv.view(torch.int32), mv.view(torch.int32))
+    mk = mask.cpu().numpy()
+    allowed = [mk[t, :len(o[t])].astype(bool) for t in range(T)]
+    topk_ok(bi.cpu().numpy(), bv.cpu().numpy(), o, dq.ks, K, allowed=allowed)
