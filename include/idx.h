@@ -64,7 +64,11 @@
  *     (0 <= ks[t] <= ke[t] <= L, finite inputs, q_scale/k_scale >= 0, window
  *     length <= W where a W is given) are the caller's; violating them gives
  *     undefined results but no out-of-bounds access of q/k (key rows are
- *     clamped to [0, L)).
+ *     clamped to [0, L)).  With the environment variable IDX_DEBUG set (to
+ *     anything but "0"), every entry point that reads windows first checks
+ *     them, and the scales and weights of its problem, on the device,
+ *     synchronises the stream, and returns IDX_E_DEVICE_CHECK without
+ *     enqueueing its own kernels if one fails.
  *   - Supported: D = 128; H in {32, 64}; 1 <= K <= 2048; block_k a multiple of
  *     256 in [256, 32768]; pool = 8; 1 <= n_blocks <= 2048.
  */
@@ -88,7 +92,8 @@ enum {
   IDX_E_WORKSPACE = 5,   /* ws_bytes below idx_workspace_size()                 */
   IDX_E_UNSUPPORTED = 6, /* valid but not provided (D != 128, H, ...)           */
   IDX_E_LAUNCH = 7,      /* a kernel launch failed                              */
-  IDX_E_ALIGN = 8        /* a pointer lacks the required alignment              */
+  IDX_E_ALIGN = 8,       /* a pointer lacks the required alignment              */
+  IDX_E_DEVICE_CHECK = 9 /* IDX_DEBUG: a precondition in device memory failed   */
 };
 
 enum { IDX_K_FP8_E4M3 = 0, IDX_K_MXFP4 = 1 };

@@ -31,7 +31,7 @@ IDX_OP_BLOCK_CANDIDATES_DENSE = 4
 IDX_OP_GATHER_ROWS = 5
 
 STATUS = {0: "IDX_OK", 1: "IDX_E_NULL", 2: "IDX_E_SHAPE", 3: "IDX_E_PARAM", 4: "IDX_E_FORMAT",
-          5: "IDX_E_WORKSPACE", 6: "IDX_E_UNSUPPORTED", 7: "IDX_E_LAUNCH", 8: "IDX_E_ALIGN"}
+          5: "IDX_E_WORKSPACE", 6: "IDX_E_UNSUPPORTED", 7: "IDX_E_LAUNCH", 8: "IDX_E_ALIGN", 9: "IDX_E_DEVICE_CHECK"}
 
 EXPORTS = ("idx_mqa_logits", "idx_mqa_logits_block", "idx_topk", "idx_logits_topk_fused",
            "idx_logits_topk_fused_paged", "idx_logits_topk_fused_blocks", "idx_logits_topk_fused_static",

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdint>
 
@@ -242,6 +243,7 @@ const char *idx_status_str(idx_status s) {
     case IDX_E_UNSUPPORTED: return "unsupported configuration";
     case IDX_E_LAUNCH: return "kernel launch failed";
     case IDX_E_ALIGN: return "pointer not aligned";
+    case IDX_E_DEVICE_CHECK: return "a device-side precondition failed (IDX_DEBUG)";
     default: return "unknown status";
   }
 }
@@ -292,6 +294,7 @@ idx_status idx_mqa_logits(const idx_problem *p, float *logits, int64_t ld, int32
   if (W < 0 || ld < W || W > MAX_W) return IDX_E_SHAPE;
   if (!aligned(logits, 16)) return IDX_E_ALIGN;
   if (p->T == 0 || W == 0) return IDX_OK;
+  if ((st = idx::debug_check(p->ks, p->ke, p->T, p->L, W, p, stream))) return st;
   hipStream_t s = (hipStream_t)stream;
   if (p->L > 0) {
     idx::LogitsArgs a = logits_args(p, 0, p->T, 0, p->L, logits, ld, W);
@@ -312,6 +315,7 @@ idx_status idx_mqa_logits_block(const idx_problem *p, int32_t row0, int32_t nrow
   if (!aligned(out, 16)) return IDX_E_ALIGN;
   const int32_t key_hi = (int32_t)std::min<int64_t>((int64_t)key0 + nkeys, p->L);
   if (nrows == 0 || key_hi <= key0) return IDX_OK;
+  if ((st = idx::debug_check(p->ks, p->ke, p->T, p->L, -1, p, stream))) return st;
   idx::LogitsArgs a = logits_args(p, row0, nrows, key0, key_hi, out, ld, nkeys);
   return launched(idx::launch_logits(a, p->k_fmt, p->H, idx::STORE_BLOCK, (hipStream_t)stream));
 }
@@ -329,6 +333,8 @@ idx_status idx_topk(const float *logits, int64_t ld, int32_t W, const int32_t *k
   if (block_k > MAX_BLOCK) return IDX_E_PARAM;
   if (!aligned(logits, 4) || !aligned(out_idx, 4) || (out_val && !aligned(out_val, 4))) return IDX_E_ALIGN;
   if (T == 0) return IDX_OK;
+  idx_status st = idx::debug_check(ks, ke, T, INT32_MAX, W, nullptr, stream);
+  if (st) return st;
   idx::TopkArgs a{};
   a.vals = logits;
   a.ld = ld;
@@ -397,6 +403,7 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
   if (ws_source && ws_source(&ws) != hipSuccess) return IDX_E_LAUNCH;
   if (!ws) return IDX_E_NULL;
   if (!aligned(ws, 256)) return IDX_E_ALIGN;
+  if ((st = debug_check(p->ks, p->ke, p->T, p->L, -1, p, stream))) return st;
   hipStream_t s = (hipStream_t)stream;
   const int32_t Kc = cand_cap(K);
   Carve cv{(uint8_t *)ws};
@@ -527,6 +534,7 @@ idx_status idx_refine_topk(const idx_problem *p, const int32_t *cand_idx, const 
   if (!ws) return IDX_E_NULL;
   if (ws_bytes < HEAD) return IDX_E_WORKSPACE;
   if (!aligned(ws, 256)) return IDX_E_ALIGN;
+  if ((st = idx::debug_check(p->ks, p->ke, p->T, p->L, -1, p, stream))) return st;
   hipStream_t s = (hipStream_t)stream;
   Carve cv{(uint8_t *)ws};
   RefineWs rw;
@@ -564,6 +572,8 @@ idx_status idx_block_candidates(const idx_problem *p, const float *logits, int64
   if (!ws) return IDX_E_NULL;
   if (ws_bytes < need) return IDX_E_WORKSPACE;
   if (!aligned(ws, 256)) return IDX_E_ALIGN;
+  if ((st = idx::debug_check(p->ks, p->ke, p->T, logits ? INT32_MAX : p->L, W, logits ? nullptr : p, stream)))
+    return st;
   hipStream_t s = (hipStream_t)stream;
   Carve cv{(uint8_t *)ws};
   const int32_t Kc = logits ? n_blocks : cand_cap(n_blocks);

@@ -19,4 +19,13 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
                       const int32_t *slot_of_key, int32_t *out_idx, float *out_val, int32_t *out_slot, void *ws,
                       size_t ws_bytes, void *stream, WorkspaceSource ws_source);
 
+// IDX_DEBUG set (and not "0") in the environment, read on every call.
+bool debug_enabled();
+// In debug mode: check on the device that 0 <= ks[t] <= ke[t] <= L and ke[t] - ks[t] <= W (W >= 0)
+// for t < T, and, with a problem p, that its q_scale are >= 0, its w finite and its key scales
+// valid; synchronises `stream` and returns IDX_E_DEVICE_CHECK on a failure.  IDX_OK otherwise,
+// and always when debug mode is off (nothing is enqueued then).
+idx_status debug_check(const int32_t *ks, const int32_t *ke, int32_t T, int32_t L, int64_t W, const idx_problem *p,
+                       void *stream);
+
 }  // namespace idx

@@ -31,7 +31,7 @@ def test_exports_match_header(lib):
 
 def test_status_strings(lib):
     assert idx.status_str(0) == "ok"
-    for s in range(1, 9):
+    for s in range(1, 10):
         assert idx.status_str(s) not in ("ok", "unknown status")
     assert idx.status_str(99) == "unknown status"
 
