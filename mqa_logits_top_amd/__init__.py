@@ -306,7 +306,7 @@ def idx_logits_topk_fused_static(p: Inputs, K: int, block_k: int = 32768, row_ch
 
 
 RESERVE = 512   # extra candidates the exact boundary refinement keeps per row
-REFINE_WS = 1280
+REFINE_WS = 2304
 
 
 def candidate_capacity(K: int) -> int:

@@ -111,10 +111,10 @@ int32_t cand_cap(int32_t K) { return K + RESERVE < MAX_KC ? K + RESERVE : MAX_KC
 
 // Workspace layout (every region 256-byte aligned):
 //   [0, 256)            uint32 overflow counter of the last call, then free
-//   key-bound partials  256 floats
+//   key-bound partials  256 floats of max |k|, then 256 floats of the largest per-key factor
 //   candidate ids/vals  [Tc, Kc] each
 //   scratch             [Tc, pitch(Bk)] fp32 scores (or [Tc, pitch(Bk / pool)] pooled maxima)
-constexpr size_t HEAD = 256 + 1024;
+constexpr size_t HEAD = 256 + 2048;
 // Row pitch of scratch rows: 256 bytes beyond the row, so that the rows that
 // the selection kernel streams at the same time start on different HBM channels
 // instead of all sitting a power of two apart.
@@ -124,12 +124,9 @@ size_t refine_ws(int32_t Tc, int32_t Kc) { return HEAD + 2 * round_up_sz((size_t
 // kernel appends each row's values above its running list's smallest entry to one
 // slab of CAPS entries per key split; the top-K merges them instead of the keys.
 constexpr int32_t CAPS = 512;
-// The candidate-writing scoring variant keeps 3 workgroups per CU except for fp8 keys
-// with H = 32, whose registers only fit 2: there it costs about a quarter of the
-// scoring time, more than the slab merge saves right after the first launch (whose
-// running list has seen few keys, so many scores beat the threshold), and it starts
-// with the third launch.
-int32_t slab_from(const idx_problem *p) { return p->k_fmt == IDX_K_FP8_E4M3 && p->H == 32 ? 2 : 1; }
+// Launches from the second on write slabs: the first leaves each row's running list full
+// and its threshold known.
+int32_t slab_from(const idx_problem *) { return 1; }
 int32_t block_slabs(int32_t Bk) {
   int32_t split, nsplit;
   plan_splits(Bk, split, nsplit);
@@ -192,7 +189,7 @@ struct RefineWs {
 RefineWs carve_refine(Carve &cv, int32_t Tc, int32_t Kc) {
   RefineWs w;
   w.overflow = cv.take<uint32_t>(64);
-  w.kpart = cv.take<float>(256);
+  w.kpart = cv.take<float>(512);
   w.cidx = cv.take<int32_t>((size_t)Tc * Kc);
   w.cval = cv.take<float>((size_t)Tc * Kc);
   return w;
@@ -539,7 +536,7 @@ idx_status idx_refine_topk(const idx_problem *p, const int32_t *cand_idx, const 
   Carve cv{(uint8_t *)ws};
   RefineWs rw;
   rw.overflow = cv.take<uint32_t>(64);
-  rw.kpart = cv.take<float>(256);
+  rw.kpart = cv.take<float>(512);
   rw.cidx = const_cast<int32_t *>(cand_idx);
   rw.cval = const_cast<float *>(cand_val);
   if ((st = launched(idx::launch_key_bound((const uint8_t *)p->k, (const uint8_t *)p->k_scale, p->k_fmt, p->L,

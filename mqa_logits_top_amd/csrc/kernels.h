@@ -126,7 +126,8 @@ struct RefineArgs {
   int64_t ld_cand;
   int32_t Kc, K;
   int32_t pool;             // 1: ids are keys; > 1: ids are pooled blocks of `pool` keys from ks
-  const float *kmax_part;   // partial maxima of |k| (launch_key_bound)
+  const float *kmax_part;   // partial maxima of |k| (launch_key_bound), then at +256 those of the per-key
+                            // factor the scoring kernel's F16 form applies after its head sum
   int32_t npart;
   uint32_t *overflow;       // rows whose band may extend below the list
   int32_t *out_idx;         // row r at out_idx + r * K

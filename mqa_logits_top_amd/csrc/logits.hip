@@ -52,6 +52,7 @@
 #include <algorithm>
 #include <atomic>
 #include <climits>
+#include <type_traits>
 
 namespace idx {
 namespace {
@@ -61,6 +62,20 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+// Two fp32 values to packed f16, rounded to nearest even, each clamped to [0, 1]: the
+// compiler folds the clamp into the conversion's clamp bit (one v_cvt_pk_f16_f32 ... clamp).
+// With every score term scaled into [-1, 1] beforehand, this is the ReLU and the f16
+// rounding in one VALU operation.
+__device__ __forceinline__ uint32_t cvt_relu_f16x2(float lo, float hi) {
+  v2h h = __builtin_convertvector((v2f){lo, hi}, v2h);
+  h = __builtin_elementwise_min(__builtin_elementwise_max(h, (v2h){0, 0}), (v2h){1, 1});
+  return __builtin_bit_cast(uint32_t, h);
+}
 
 // ReLU as one integer max: a float with the sign bit set is a negative int32
 // and becomes +0, a non-negative float keeps its bits (fmaxf would add a NaN
@@ -99,6 +114,7 @@ __device__ __forceinline__ uint32_t row16_scan(uint32_t x, uint32_t &total) {
 
 // The value is in registers here (a use the compiler cannot move or drop).
 __device__ __forceinline__ void in_regs(v8i x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void in_regs(v4i x) { asm volatile("" ::"v"(x)); }
 __device__ __forceinline__ void in_regs(float x) { asm volatile("" ::"v"(x)); }
 __device__ __forceinline__ void in_regs(int x) { asm volatile("" ::"v"(x)); }
 // Wait until at most N of this wave's memory operations are outstanding (they complete
@@ -115,8 +131,8 @@ constexpr int RSRC3 = 0x00020000;     // raw buffer, 32-bit elements
 __device__ __forceinline__ int swz8(int n) { return (n & 7) ^ ((n >> 3) & 1); }
 __device__ __forceinline__ int swz4(int n) { return ((n >> 1) ^ (n >> 3)) & 3; }
 
-template <int KF, int H, int MODE, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((MODE == STORE_CAND || MODE == STORE_SLAB) && H == 32 ? 2 : 3))) void logits_kernel(LogitsArgs a) {
+template <int KF, int H, int MODE, int NW, bool F16>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(!F16 && (MODE == STORE_CAND || MODE == STORE_SLAB) && H == 32 ? 2 : 3))) void logits_kernel(LogitsArgs a) {
   constexpr int QR = 128 / H;            // query rows per wave
   constexpr int HPT = 16 / QR;           // heads of one row in a 16-row A tile
   constexpr int NT = H / HPT;            // A tiles per wave (8)
@@ -132,7 +148,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((MODE =
 
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf[3][STAGE];
   __shared__ __attribute__((aligned(256))) uint32_t sbuf[3][TK];
-  __shared__ int32_t wg_range[3];
+  __shared__ int32_t wg_range[4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -186,9 +202,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((MODE =
       hi = max(hi, __shfl_xor(hi, off));
       odd |= __shfl_xor(odd, off);
     }
-    if (lane == 0) { wg_range[0] = lo; wg_range[1] = hi; wg_range[2] = odd; }
+    // any head weight of the workgroup's rows below zero (or not a number)
+    int neg = 0;
+    for (int i = lane; i < RPW * H; i += 64)
+      if (r_begin + i / H < r_end) neg |= !(a.w[(int64_t)(r_begin + i / H) * H + i % H] >= 0.f);
+    neg = __builtin_amdgcn_ballot_w64(neg != 0) != 0;
+    if (lane == 0) { wg_range[0] = lo; wg_range[1] = hi; wg_range[2] = odd; wg_range[3] = neg; }
   }
   __syncthreads();
+  // the launch pair splits the workgroups by their rows' head weights: the F16 form takes those
+  // whose weights are all >= 0, the fp32 form the others
+  if ((wg_range[3] != 0) == F16) return;   // uniform
   int s_lo, s_hi;
   if (by_row) {
     // The row block's items share the tiles of its rows' window union evenly, in key
@@ -277,17 +301,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((MODE =
   const int hbase = (4 * g) % HPT;
   const int t_out = wr + qo;
   const bool row_ok = t_out < r_end;
-  float wv[NT][4];
   int kst, ket;
   {
     const int t = min(t_out, r_end - 1);
-#pragma unroll
-    for (int i = 0; i < NT; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int h = HPT * i + hbase + j;
-        wv[i][j] = a.w[(int64_t)t * H + h] * a.q_scale[(int64_t)t * H + h] * a.scale;
-      }
     kst = max(a.ks[t], 0);
     ket = min(a.ke[t], a.L);
   }
@@ -312,19 +328,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((MODE =
       __builtin_amdgcn_make_buffer_rsrc(a.out + (int64_t)wrow * ld, 0, (int)(QR * ld * 4), RSRC3);
   const int obase = (t_out - a.row0 - wrow) * (int)ld;   // element offset of this lane's row
 
-  // Every value the prologue loads is in registers before the loop, so that no wait
-  // for those loads is placed inside it; then stage 0 is complete.
-#pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    in_regs(qa[i]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) in_regs(wv[i][j]);
-  }
-  in_regs(kst);
-  in_regs(ket);
-  if (ntiles > 1) vm_wait_barrier<LPT>();
-  else vm_wait_barrier<0>();
-
   // pooled blocks: this row's block offset inside an octet, and (lanes 14, 15) the head of the
   // block that started in the last octet of the previous batch, completed in the next one
   const int rr = kst & 7;
@@ -335,137 +338,255 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((MODE =
   // exclusive key limit of this lane's stores
   const int lim = MODE == STORE_DENSE ? min(v_hi, kst + a.wcols) : v_hi;
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it % 3;
-    if (it + 2 < ntiles) request(it + 2, (it + 2) % 3);  // its buffer was last read in iteration it - 1
-    const int ts = tile0 + it * TK;
-#pragma unroll
-    for (int b = 0; b < TK / 64; ++b) {
-      const int s0 = ts + 64 * b + 4 * n16;                       // this lane's first key
-      const v4i sc = *(const v4i *)&sbuf[buf][64 * b + 4 * n16];  // its 4 keys' scale words
-      float val[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int p = (4 * b + j) * 16 + n16;   // LDS row of key s0 + j
-        v8i bk;
-        int bscale = 0;
-        if (KF == 0) {
-          const int sw = swz8(p);
-          const v4i lo = *(const v4i *)&kbuf[buf][p * 128 + ((g ^ sw) << 4)];
-          const v4i hi = *(const v4i *)&kbuf[buf][p * 128 + (((4 + g) ^ sw) << 4)];
-          bk = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        } else {
-          const v4i v = *(const v4i *)&kbuf[buf][p * 64 + ((g ^ swz4(p)) << 4)];
-          bk = (v8i){v.x, v.y, v.z, v.w, 0, 0, 0, 0};
-          bscale = (sc[j] >> (8 * g)) & 0xFF;
-        }
-        v4f c[NT];
-#pragma unroll
-        for (int i = 0; i < NT; ++i) {
-          if (KF == 0)
-            c[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[i], bk, (v4f){0, 0, 0, 0}, 0, 0, 0, 0, 0, 0);
-          else
-            c[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[i], bk, (v4f){0, 0, 0, 0}, 0, 4, 0, 127, 0,
-                                                                    bscale);
-        }
-        float acc = 0.f;
-#pragma unroll
-        for (int i = 0; i < NT; ++i)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) acc = __builtin_fmaf(relu(c[i][jj]), wv[i][jj], acc);
-        if (QR == 2) {
-          const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc), __float_as_uint(acc), false, false);
-          acc = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-        }
-        val[j] = acc;
+  // The tile loop in one of two forms (template argument F16).  F16: the ReLU is the
+  // clamp of a conversion to f16 and the weighted head sum runs on an f16 MFMA, two VALU
+  // operations per fp8 MFMA instead of eight; the terms are rounded to f16 (relative error
+  // at most 2^-11 each), so this form needs head weights >= 0, where that bounds the score's
+  // relative error.  Otherwise: ReLU and head sum in fp32 on the VALU.
+  {
+    constexpr int SA = KF == 0 ? 25 : 19;   // |<q8, k8>| <= 128 * 448^2 < 2^25; fp8 x e2m1 < 2^19
+    float wv[F16 ? 1 : NT][4];
+    v8h wa[F16 ? NT / 2 : 1];
+    float fback = 1.f;
+    int eback = 0;
+    (void)fback;
+    (void)eback;
+    if constexpr (F16) {
+      // row weight exponents: w'' = w' 2^mrow keeps each row's largest weight in [2^13, 2^14);
+      // lanes [t LPR, (t + 1) LPR) take row t's maximum over its H heads, two heads each
+      constexpr int LPR = 64 / QR;
+      int mexp;
+      {
+        const int tr = min(wr + lane / LPR, r_end - 1), h0 = (lane % LPR) * 2;
+        const float w0 = a.w[(int64_t)tr * H + h0] * a.q_scale[(int64_t)tr * H + h0] * a.scale;
+        const float w1 = a.w[(int64_t)tr * H + h0 + 1] * a.q_scale[(int64_t)tr * H + h0 + 1] * a.scale;
+        float mx = __builtin_fmaxf(__builtin_fabsf(w0), __builtin_fabsf(w1));
+        for (int off = LPR / 2; off > 0; off >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, off));
+        int e = 0;
+        (void)__builtin_frexpf(mx, &e);
+        mexp = mx > 0.f ? 14 - e : 0;
       }
-      if (KF == 0) {
+      // A of the head-sum MFMAs: row R = HPT tq + part holds query tq's weights (part 0: hi,
+      // part 1: lo f16 parts of w''; other rows zero); element (g, e) of tile pair m pairs
+      // with fp8 tile 2 m + e / 4, C row 4 g + e % 4, i.e. query (4 g + e % 4) / HPT and
+      // head HPT (2 m + e / 4) + (4 g + e % 4) % HPT
+      const int tq = n16 / HPT, part = n16 % HPT;
+      const int mq = __shfl(mexp, tq * LPR);
+      const int tA = min(wr + tq, r_end - 1);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) val[j] *= __int_as_float(sc[j]);
-      }
-      if (cand) {
-        // values above the row's running threshold also go to its slab, in key order
-        uint32_t pm = 0;
+      for (int m = 0; m < NT / 2; ++m)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          pm |= (uint32_t)(writer && s0 + j >= v_lo && s0 + j < v_hi && val[j] > thr_row) << j;
-        // wave-uniform tests: at high thresholds most batches have no candidate at all, and
-        // a store is issued only for a j that some lane of the wave needs (lanes without a
-        // candidate there, or past the slab, are dropped)
-        if (__builtin_amdgcn_ballot_w64(pm != 0u)) {
-          const uint32_t c = __builtin_popcount(pm);
-          uint32_t tot;
-          const uint32_t incl = row16_scan(c, tot);
-          uint32_t pos = crow + incl - c;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const bool bit = (pm >> j) & 1u;
-            if (__builtin_amdgcn_ballot_w64(bit)) {
-              const v2u e = {__float_as_uint(val[j]), (uint32_t)(s0 + j)};
-              __builtin_amdgcn_raw_buffer_store_b64(e, crsrc,
-                                                    bit && pos < (uint32_t)share ? (slab + (int)pos) * 8 : OOB, 0, 0);
-            }
-            pos += bit;
+        for (int e = 0; e < 8; ++e) {
+          const int r = 4 * g + e % 4, h = HPT * (2 * m + e / 4) + r % HPT;
+          float v = 0.f;
+          if (part < 2 && r / HPT == tq) {
+            const float ww = __builtin_ldexpf(a.w[(int64_t)tA * H + h] * a.q_scale[(int64_t)tA * H + h] * a.scale, mq);
+            const _Float16 whi = (_Float16)ww;
+            v = part == 0 ? (float)whi : ww - (float)whi;
           }
-          crow += tot;
+          wa[m][e] = (_Float16)v;
         }
-      }
-      if (MODE != STORE_POOL8 && MODE != STORE_SLAB) {
-        const int col = MODE == STORE_DENSE ? s0 - kst : s0 - a.key_lo;   // column of key s0
-        if (writer && row_al && s0 >= v_lo && s0 + 4 <= lim) {
-          const v4u d = {__float_as_uint(val[0]), __float_as_uint(val[1]), __float_as_uint(val[2]),
-                         __float_as_uint(val[3])};
-          __builtin_amdgcn_raw_buffer_store_b128(d, orsrc, (obase + col) * 4, 0, 0);
-        } else {
+      // output rows: this lane's query qo, exponent 2^(SA - mrow)
+      const int mo = __shfl(mexp, qo * LPR);
+      eback = SA - mo;
+      fback = __builtin_ldexpf(1.f, eback);
+    } else {
+      const int t = min(t_out, r_end - 1);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const bool ok = writer && s0 + j >= v_lo && s0 + j < lim;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val[j]), orsrc, ok ? (obase + col + j) * 4 : OOB,
-                                                  0, 0);
-          }
-        }
-      } else {
-        // 8-key blocks of the row start at ks: the block starting in octet o (keys 8 o .. 8 o + 7,
-        // held by lanes 2 m, 2 m + 1) is keys 8 o + r .. 8 o + r + 7, r = ks & 7.  hi: the octet's
-        // in-window keys at positions >= r (the head of its block); lo: those at positions < r
-        // (the tail of the block that started one octet before).
-        float hi = -__builtin_inff(), lo = -__builtin_inff();
+      for (int i = 0; i < NT; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int s = s0 + j;
-          const bool in = s >= kst && s < ket;
-          if (in && (s & 7) >= rr) hi = __builtin_fmaxf(hi, val[j]);
-          if (in && (s & 7) < rr) lo = __builtin_fmaxf(lo, val[j]);
+          const int h = HPT * i + hbase + j;
+          wv[i][j] = a.w[(int64_t)t * H + h] * a.q_scale[(int64_t)t * H + h] * a.scale;
         }
-        hi = __builtin_fmaxf(hi, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(hi), 0xB1, 0xF, 0xF, false)));
-        lo = __builtin_fmaxf(lo, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(lo), 0xB1, 0xF, 0xF, false)));
-        // the next octet's tail: two lanes up (row rotate right by 14); lanes 14, 15 receive the
-        // tail of this batch's first octet, which completes the block they held back last batch
-        const float nlo = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(lo), 0x12E, 0xF, 0xF, false));
-        int bo = s0 >> 3;   // octet of the block start stored now
-        float m = rr ? __builtin_fmaxf(hi, nlo) : hi;
-        if (rr && n16 >= 14) {
-          m = __builtin_fmaxf(pend, nlo);
-          bo -= 8;
-          pend = hi;
-        }
-        const int bs = 8 * bo + rr;                  // the block's first key
-        const int col = bo - (a.key_lo >> 3);
-        const bool st = writer && (n16 & 1) == 0 && bs >= kst && bs < ket && bs >= own_lo && bs < own_hi &&
-                        col < a.wcols;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), orsrc, st ? (obase + col) * 4 : OOB, 0, 0);
-      }
     }
-    // stage it + 1 is complete once no more than the memory operations issued after its
-    // request are outstanding: >= ST stores of iteration it - 1, stage it + 2's request
-    // (>= LPT copies), >= ST stores of this iteration
-    if (it + 1 < ntiles) {
-      if (it + 2 < ntiles) {
-        if (it > 0) vm_wait_barrier<2 * ST + LPT>();
-        else vm_wait_barrier<ST + LPT>();
-      } else {
-        if (it > 0) vm_wait_barrier<2 * ST>();
-        else vm_wait_barrier<ST>();
+    // Every value the prologue loads is in registers before the loop, so that no wait
+    // for those loads is placed inside it; then stage 0 is complete.
+#pragma unroll
+    for (int i = 0; i < NT; ++i) in_regs(qa[i]);
+    if constexpr (F16) {
+#pragma unroll
+      for (int m = 0; m < NT / 2; ++m) in_regs(__builtin_bit_cast(v4i, wa[m]));
+      in_regs(fback);
+      in_regs(eback);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) in_regs(wv[i][j]);
+    }
+    in_regs(kst);
+    in_regs(ket);
+    if (ntiles > 1) vm_wait_barrier<LPT>();
+    else vm_wait_barrier<0>();
+
+    for (int it = 0; it < ntiles; ++it) {
+      const int buf = it % 3;
+      if (it + 2 < ntiles) request(it + 2, (it + 2) % 3);  // its buffer was last read in iteration it - 1
+      const int ts = tile0 + it * TK;
+  #pragma unroll
+      for (int b = 0; b < TK / 64; ++b) {
+        const int s0 = ts + 64 * b + 4 * n16;                       // this lane's first key
+        const v4i sc = *(const v4i *)&sbuf[buf][64 * b + 4 * n16];  // its 4 keys' scale words
+        float val[4];
+        int ebk[4] = {0, 0, 0, 0};   // MXFP4, f16 path: each key's largest block-scale code
+        (void)ebk;
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int p = (4 * b + j) * 16 + n16;   // LDS row of key s0 + j
+          v8i bk;
+          int bscale = 0;
+          if (KF == 0) {
+            const int sw = swz8(p);
+            const v4i lo = *(const v4i *)&kbuf[buf][p * 128 + ((g ^ sw) << 4)];
+            const v4i hi = *(const v4i *)&kbuf[buf][p * 128 + (((4 + g) ^ sw) << 4)];
+            bk = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          } else {
+            const v4i v = *(const v4i *)&kbuf[buf][p * 64 + ((g ^ swz4(p)) << 4)];
+            bk = (v8i){v.x, v.y, v.z, v.w, 0, 0, 0, 0};
+            bscale = (sc[j] >> (8 * g)) & 0xFF;
+          }
+          v4f c[NT];
+          if constexpr (F16) {
+            // every term scaled by 2^-SA into [-1, 1]; an MXFP4 key's block scales relative to its
+            // largest (the factor comes back after the head sum)
+            int emax = 0;
+            if (KF != 0) {
+              const uint32_t w4 = (uint32_t)sc[j];
+              emax = (int)max(max(w4 & 0xFFu, (w4 >> 8) & 0xFFu), max((w4 >> 16) & 0xFFu, w4 >> 24));
+              bscale = max(bscale - emax + 127, 0);
+              ebk[j] = emax;
+            }
+  #pragma unroll
+            for (int i = 0; i < NT; ++i)
+              c[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[i], bk, (v4f){0, 0, 0, 0}, 0, KF == 0 ? 0 : 4, 0,
+                                                                      127 - SA, 0, KF == 0 ? 127 : bscale);
+            // ReLU and f16 rounding in one conversion, then the weighted head sum on the f16 MFMA:
+            // B element (g, e) of tile pair m is C row 4 g + e % 4 of fp8 tile 2 m + e / 4 (wa
+            // uses the same pairing), and C rows 4 g, 4 g + 1 collect the hi and lo weights' sums
+            v4f hsum = {0, 0, 0, 0};
+  #pragma unroll
+            for (int m = 0; m < NT / 2; ++m) {
+              const v4u bu = {cvt_relu_f16x2(c[2 * m][0], c[2 * m][1]), cvt_relu_f16x2(c[2 * m][2], c[2 * m][3]),
+                              cvt_relu_f16x2(c[2 * m + 1][0], c[2 * m + 1][1]),
+                              cvt_relu_f16x2(c[2 * m + 1][2], c[2 * m + 1][3])};
+              hsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[m], __builtin_bit_cast(v8h, bu), hsum, 0, 0, 0);
+            }
+            val[j] = hsum[0] + hsum[1];
+          } else {
+  #pragma unroll
+            for (int i = 0; i < NT; ++i) {
+              if (KF == 0)
+                c[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[i], bk, (v4f){0, 0, 0, 0}, 0, 0, 0, 0, 0, 0);
+              else
+                c[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[i], bk, (v4f){0, 0, 0, 0}, 0, 4, 0, 127, 0,
+                                                                        bscale);
+            }
+            float acc = 0.f;
+  #pragma unroll
+            for (int i = 0; i < NT; ++i)
+  #pragma unroll
+              for (int jj = 0; jj < 4; ++jj) acc = __builtin_fmaf(relu(c[i][jj]), wv[i][jj], acc);
+            if (QR == 2) {
+              const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc), __float_as_uint(acc), false, false);
+              acc = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+            }
+            val[j] = acc;
+          }
+        }
+        if constexpr (F16) {
+          // undo the scalings: 2^(SA - mrow) for the terms and weights, then the key's own scale
+  #pragma unroll
+          for (int j = 0; j < 4; ++j)
+            val[j] = KF == 0 ? val[j] * fback * __int_as_float(sc[j]) : __builtin_ldexpf(val[j], eback + ebk[j] - 127);
+        } else if (KF == 0) {
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) val[j] *= __int_as_float(sc[j]);
+        }
+        if (cand) {
+          // values above the row's running threshold also go to its slab, in key order
+          uint32_t pm = 0;
+  #pragma unroll
+          for (int j = 0; j < 4; ++j)
+            pm |= (uint32_t)(writer && s0 + j >= v_lo && s0 + j < v_hi && val[j] > thr_row) << j;
+          // wave-uniform tests: at high thresholds most batches have no candidate at all, and
+          // a store is issued only for a j that some lane of the wave needs (lanes without a
+          // candidate there, or past the slab, are dropped)
+          if (__builtin_amdgcn_ballot_w64(pm != 0u)) {
+            const uint32_t c = __builtin_popcount(pm);
+            uint32_t tot;
+            const uint32_t incl = row16_scan(c, tot);
+            uint32_t pos = crow + incl - c;
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const bool bit = (pm >> j) & 1u;
+              if (__builtin_amdgcn_ballot_w64(bit)) {
+                const v2u e = {__float_as_uint(val[j]), (uint32_t)(s0 + j)};
+                __builtin_amdgcn_raw_buffer_store_b64(e, crsrc,
+                                                      bit && pos < (uint32_t)share ? (slab + (int)pos) * 8 : OOB, 0, 0);
+              }
+              pos += bit;
+            }
+            crow += tot;
+          }
+        }
+        if (MODE != STORE_POOL8 && MODE != STORE_SLAB) {
+          const int col = MODE == STORE_DENSE ? s0 - kst : s0 - a.key_lo;   // column of key s0
+          if (writer && row_al && s0 >= v_lo && s0 + 4 <= lim) {
+            const v4u d = {__float_as_uint(val[0]), __float_as_uint(val[1]), __float_as_uint(val[2]),
+                           __float_as_uint(val[3])};
+            __builtin_amdgcn_raw_buffer_store_b128(d, orsrc, (obase + col) * 4, 0, 0);
+          } else {
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const bool ok = writer && s0 + j >= v_lo && s0 + j < lim;
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val[j]), orsrc, ok ? (obase + col + j) * 4 : OOB,
+                                                    0, 0);
+            }
+          }
+        } else {
+          // 8-key blocks of the row start at ks: the block starting in octet o (keys 8 o .. 8 o + 7,
+          // held by lanes 2 m, 2 m + 1) is keys 8 o + r .. 8 o + r + 7, r = ks & 7.  hi: the octet's
+          // in-window keys at positions >= r (the head of its block); lo: those at positions < r
+          // (the tail of the block that started one octet before).
+          float hi = -__builtin_inff(), lo = -__builtin_inff();
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int s = s0 + j;
+            const bool in = s >= kst && s < ket;
+            if (in && (s & 7) >= rr) hi = __builtin_fmaxf(hi, val[j]);
+            if (in && (s & 7) < rr) lo = __builtin_fmaxf(lo, val[j]);
+          }
+          hi = __builtin_fmaxf(hi, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(hi), 0xB1, 0xF, 0xF, false)));
+          lo = __builtin_fmaxf(lo, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(lo), 0xB1, 0xF, 0xF, false)));
+          // the next octet's tail: two lanes up (row rotate right by 14); lanes 14, 15 receive the
+          // tail of this batch's first octet, which completes the block they held back last batch
+          const float nlo = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(lo), 0x12E, 0xF, 0xF, false));
+          int bo = s0 >> 3;   // octet of the block start stored now
+          float m = rr ? __builtin_fmaxf(hi, nlo) : hi;
+          if (rr && n16 >= 14) {
+            m = __builtin_fmaxf(pend, nlo);
+            bo -= 8;
+            pend = hi;
+          }
+          const int bs = 8 * bo + rr;                  // the block's first key
+          const int col = bo - (a.key_lo >> 3);
+          const bool st = writer && (n16 & 1) == 0 && bs >= kst && bs < ket && bs >= own_lo && bs < own_hi &&
+                          col < a.wcols;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), orsrc, st ? (obase + col) * 4 : OOB, 0, 0);
+        }
+      }
+      // stage it + 1 is complete once no more than the memory operations issued after its
+      // request are outstanding: >= ST stores of iteration it - 1, stage it + 2's request
+      // (>= LPT copies), >= ST stores of this iteration
+      if (it + 1 < ntiles) {
+        if (it + 2 < ntiles) {
+          if (it > 0) vm_wait_barrier<2 * ST + LPT>();
+          else vm_wait_barrier<ST + LPT>();
+        } else {
+          if (it > 0) vm_wait_barrier<2 * ST>();
+          else vm_wait_barrier<ST>();
+        }
       }
     }
   }
@@ -496,11 +617,11 @@ int resident_workgroups(Kern kern, int threads) {
 
 constexpr int NW_LAUNCH = 4;   // 4 waves: up to 3 workgroups per CU, so a stage barrier never idles the CU
 
-template <int KF, int H, int MODE>
-hipError_t launch3(const LogitsArgs &a0, hipStream_t s) {
+template <int KF, int H, int MODE, bool F16>
+hipError_t launch4(const LogitsArgs &a0, hipStream_t s) {
   constexpr int NW = NW_LAUNCH;
   constexpr int RPW = NW * (128 / H);
-  auto kern = logits_kernel<KF, H, MODE, NW>;
+  auto kern = logits_kernel<KF, H, MODE, NW, F16>;
   const int nrb = (a0.nrows + RPW - 1) / RPW;
   const int64_t items = (int64_t)((nrb + 7) / 8) * 8 * a0.nsplit;   // row blocks padded to whole groups of 8
   if (items <= 0) return hipSuccess;
@@ -515,6 +636,14 @@ hipError_t launch3(const LogitsArgs &a0, hipStream_t s) {
   const int64_t grid = a.nfull + rem * a.parts;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
+}
+
+// Both forms over the same grid: each workgroup works in exactly one of them.
+template <int KF, int H, int MODE>
+hipError_t launch3(const LogitsArgs &a, hipStream_t s) {
+  const hipError_t e = launch4<KF, H, MODE, true>(a, s);
+  if (e != hipSuccess) return e;
+  return launch4<KF, H, MODE, false>(a, s);
 }
 
 template <int KF, int H>

@@ -108,7 +108,7 @@ struct Smem {
   __attribute__((aligned(16))) uint32_t ovl[OVL];
   double part[2][KB][NWV];     // per batch parity, key and head tile: head-sum partials
   uint32_t red[3][NWV];
-  float fred[NWV];
+  float fred[NWV], fred2[NWV];
   uint32_t misc[8];
 };
 
@@ -307,16 +307,42 @@ __global__ __launch_bounds__(NTH) void refine_kernel(RefineArgs a) {
     mq = fmaxf(mq, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mq), 0x4E, 0xF, 0xF, false)));
     float part = (cc == 0 && wave < HW) ? fabsf(wh * qsh * a.scale) * mq : 0.f;
     part = wave_reduce_f32(part, [](float x, float y) { return x + y; });
-    float kmax = 0.f;
-    for (int i = lane; i < a.npart; i += 64) kmax = fmaxf(kmax, a.kmax_part[i]);
+    // sum_h |w'_h| and whether any head weight is below zero (the scoring kernel's F16 form
+    // serves only rows whose weights are all >= 0)
+    float wsum = (cc == 0 && wave < HW) ? fabsf(wh * qsh * a.scale) : 0.f;
+    wsum = wave_reduce_f32(wsum, [](float x, float y) { return x + y; });
+    const uint32_t neg = (uint32_t)(__builtin_amdgcn_ballot_w64(cc == 0 && wave < HW && !(wh >= 0.f)) != 0);
+    float kmax = 0.f, kfac = 0.f;
+    for (int i = lane; i < a.npart; i += 64) {
+      kmax = fmaxf(kmax, a.kmax_part[i]);
+      kfac = fmaxf(kfac, a.kmax_part[256 + i]);
+    }
     kmax = wave_reduce_f32(kmax, [](float x, float y) { return fmaxf(x, y); });
-    if (lane == 0) sm.fred[wave] = part;
+    kfac = wave_reduce_f32(kfac, [](float x, float y) { return fmaxf(x, y); });
+    if (lane == 0) {
+      sm.fred[wave] = part;
+      sm.fred2[wave] = wsum;
+      sm.red[0][wave] = neg;
+    }
     if (tid == 0) sm.misc[2] = 0;
     __syncthreads();
-    float S = 0.f;
+    float S = 0.f, WS = 0.f;
+    uint32_t anyneg = 0;
 #pragma unroll
-    for (int w = 0; w < NWV; ++w) S += sm.fred[w];
-    const double D = (double)GAMMA * 0.0001220703125 * (double)kmax * (double)S * 1.0000001;
+    for (int w = 0; w < NWV; ++w) {
+      S += sm.fred[w];
+      WS += sm.fred2[w];
+      anyneg |= sm.red[0][w];
+    }
+    double D = (double)GAMMA * 0.0001220703125 * (double)kmax * (double)S * 1.0000001;
+    // Rows whose weights are all >= 0 may have been scored in F16 form: each ReLU term rounded
+    // to f16 (relative error <= 2^-11 of the term, so <= 2^-11 of the score when all weights are
+    // >= 0; counted twice here), or, below f16's normal range, by at most 2^-25 of the term's
+    // 2^-SA scale (its score-unit size is |w'_h| 2^(SA - 25) times the key's factor).
+    if (!anyneg) {
+      const double SA = a.k_fmt == 0 ? 25.0 : 19.0;
+      D += 0.0009765625 * fabs((double)theta) + 2.0 * ldexp((double)WS * (double)kfac, (int)SA - 25);
+    }
     const double lo = (double)theta - 2.0 * D, hi = (double)theta + 2.0 * D;
 
     // ---- classify; list the band; check that the list reaches below the band
@@ -557,13 +583,14 @@ __device__ void window_flag(const WindowFlags wf, int L, int f) {
 // workgroups after them compute the window flags, one each.
 __global__ __launch_bounds__(256) void key_bound_kernel(const uint8_t *k, const uint8_t *k_scale, int k_fmt, int L,
                                                         float *part, uint32_t *overflow, int np, WindowFlags wf) {
-  __shared__ float red[4];
+  __shared__ float red[4], redf[4];
   if ((int)blockIdx.x >= np) {   // uniform
     window_flag(wf, L, (int)blockIdx.x - np);
     return;
   }
   if (blockIdx.x == 0 && threadIdx.x == 0 && overflow) *overflow = 0;  // runs before the refinement in stream order
   float m = 0.f;
+  float f = 0.f;   // largest per-key factor of the scoring kernel's F16 form: k_scale, or 2^(emax - 127)
   for (int s = blockIdx.x * 256 + threadIdx.x; s < L; s += np * 256) {
     if (k_fmt == 0) {
       const uint4 *row = (const uint4 *)(k + (int64_t)s * 128);
@@ -578,6 +605,7 @@ __global__ __launch_bounds__(256) void key_bound_kernel(const uint8_t *k, const 
           for (int b = 0; b < 4; ++b) bm = max(bm, (w4[j] >> (8 * b)) & 0x7Fu);  // |E4M3| is monotone in the low 7 bits
       }
       m = fmaxf(m, e4m3(bm) * ((const float *)k_scale)[s]);
+      f = fmaxf(f, ((const float *)k_scale)[s]);
     } else {
       const uint4 *row = (const uint4 *)(k + (int64_t)s * 64);
       const uint32_t sc = *(const uint32_t *)(k_scale + (int64_t)s * 4);
@@ -592,12 +620,23 @@ __global__ __launch_bounds__(256) void key_bound_kernel(const uint8_t *k, const 
           for (int b = 0; b < 8; ++b) nm = max(nm, (w4[j] >> (4 * b)) & 0x7u);  // |E2M1| monotone in low 3 bits
         m = fmaxf(m, e2m1(nm) * e8m0((sc >> (8 * blk)) & 0xFFu));
       }
+      const uint32_t emax = max(max(sc & 0xFFu, (sc >> 8) & 0xFFu), max((sc >> 16) & 0xFFu, sc >> 24));
+      f = fmaxf(f, e8m0(emax));
     }
   }
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  for (int o = 32; o > 0; o >>= 1) {
+    m = fmaxf(m, __shfl_xor(m, o));
+    f = fmaxf(f, __shfl_xor(f, o));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[threadIdx.x >> 6] = m;
+    redf[threadIdx.x >> 6] = f;
+  }
   __syncthreads();
-  if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  if (threadIdx.x == 0) {
+    part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    part[256 + blockIdx.x] = fmaxf(fmaxf(redf[0], redf[1]), fmaxf(redf[2], redf[3]));
+  }
 }
 
 }  // namespace

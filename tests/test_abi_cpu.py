@@ -147,7 +147,7 @@ def _r(x):
 
 
 def test_workspace_sizes(lib):
-    head = 1280
+    head = 2304
     kc = lambda K: min(K + 512, 2560)
     p = _problem(T=2048, L=65536)
     n = ctypes.c_size_t()
