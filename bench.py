@@ -288,7 +288,17 @@ def cpu_baseline(p, K, g_idx, budget_s, workers):
 
 
 COPY_BYTES = 256 << 20   # calibration copy of the traffic probe
-PROBE = {"glm_chunk": "logits_kernel<0, 32, 1, 4>", "long_ctx": "logits_kernel<0, 64, 1, 4>"}
+# A scoring launch is two dispatches over one grid, the f16 head-sum form, then the fp32 form
+# (each workgroup works in one of them); these prefixes name both.
+PROBE = {"glm_chunk": "logits_kernel<0, 32, 1, 4, ", "long_ctx": "logits_kernel<0, 64, 1, 4, ",
+         "dsv4_mxfp4": "logits_kernel<1, 64, 1, 4, "}
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_MFMA",
+                 "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "GRBM_COUNT")
+
+
+def launch_pairs(values):
+    """Per-launch sums of the (f16 form, fp32 form) dispatch pairs of a scoring launch, in order."""
+    return [values[i] + values[i + 1] for i in range(0, len(values) - 1, 2)]
 
 
 def traffic_probe(dev):
@@ -309,7 +319,7 @@ def traffic_probe(dev):
     torch.cuda.synchronize()
     del d5, blocks5
     torch.cuda.empty_cache()
-    for name in ("glm_chunk", "long_ctx"):
+    for name in PROBE:
         pw = p if name == "glm_chunk" else synth.make_config(name)
         dw = d if name == "glm_chunk" else idx.Inputs.from_host(pw, device=dev)
         r0, nr, kb, nk = max(launch_rects(dw, pw.meta["block_k"], ROW_CHUNK[name]), key=lambda r: r[1] * r[3])
@@ -358,8 +368,8 @@ def traffic_summary(fetch_dir, write_dir):
           "written MiB per launch | HBM MiB per launch |")
     print("|---|---|---|---|---|---|---|")
     for name, kname in PROBE.items():
-        f = [v * factor["FETCH_SIZE"] for n, v, _, _ in rows["FETCH_SIZE"] if kname in n][-2:]
-        w = [v * factor["WRITE_SIZE"] for n, v, _, _ in rows["WRITE_SIZE"] if kname in n][-2:]
+        f = launch_pairs([v * factor["FETCH_SIZE"] for n, v, _, _ in rows["FETCH_SIZE"] if kname in n])[-2:]
+        w = launch_pairs([v * factor["WRITE_SIZE"] for n, v, _, _ in rows["WRITE_SIZE"] if kname in n])[-2:]
         p = synth.make_config(name)
         Tc = p.T if ROW_CHUNK[name] <= 0 else min(ROW_CHUNK[name], p.T)
         rect = [Tc, min(launch_keys(p.L, p.meta["block_k"]), p.L)]
@@ -399,6 +409,95 @@ def traffic_summary(fetch_dir, write_dir):
     for (w_, name), (cnt, fb, wb, t) in sorted(groups.items(), key=lambda x: (x[0][0], -x[1][3])):
         print(f"| {w_} | {name} | {cnt} | {fb / cnt / 2**20:.1f} | {wb / cnt / 2**20:.1f} | {t / cnt * 1e6:.1f} | "
               f"{(fb + wb) / t / 1e9:.0f} |")
+
+
+def mfma_summary(pmc_dir):
+    """Markdown summary of a traffic-probe run under rocprofv3 --pmc with MFMA_COUNTERS: for the
+    last two scoring launches of each probed workload, the issued MFMA work, MFMA-busy cycles,
+    VALU instructions and the shader clock (GRBM_COUNT over the dispatch's duration, 8 XCDs)."""
+    import csv
+    acc = {}
+    for r in csv.DictReader(open(os.path.join(pmc_dir, "run_counter_collection.csv"))):
+        k = int(r["Dispatch_Id"])
+        e = acc.setdefault(k, {"name": r["Kernel_Name"], "t": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9})
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    disp = [acc[k] for k in sorted(acc)]
+    cols = ("SQ_INSTS_MFMA", "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_VALU_MFMA_BUSY_CYCLES",
+            "SQ_INSTS_VALU", "GRBM_COUNT")
+    print("| workload | form | duration us | " + " | ".join(cols) + " | clock GHz | MFMA busy | VALU per MFMA |")
+    print("|---|---|---|" + "---|" * (len(cols) + 3))
+    for name, kname in PROBE.items():
+        ds = [e for e in disp if kname in e["name"]][-4:]
+        for e in ds:
+            cyc = e.get("GRBM_COUNT", 0.0) / 8.0                      # per XCD
+            busy = e.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / 1024.0    # per SIMD
+            form = "f16" if "true>" in e["name"] else "fp32"
+            print(f"| {name} | {form} | {e['t'] * 1e6:.1f} | " + " | ".join(f"{e.get(c, 0.0):.4g}" for c in cols)
+                  + f" | {cyc / e['t'] / 1e9 if e['t'] > 0 else 0:.2f} | {busy / cyc if cyc else 0:.3f} | "
+                  f"{e.get('SQ_INSTS_VALU', 0.0) / max(1.0, e.get('SQ_INSTS_MFMA', 0.0)):.2f} |")
+
+
+def _short_kernel(n):
+    import re
+    m = re.search(r"namespace\)::(\w+(?:<[^>]*>)?)", n)
+    return m.group(1) if m else n.split("(")[0][:48]
+
+
+def trace_summary(trace_dir, scoring="logits_kernel<0, 64, 1, 4, "):
+    """Markdown summary of a rocprofv3 --kernel-trace run of the default headline bench: each
+    fused step (from its window kernel to its last refinement) by kernel, then the roofline's
+    block-store scoring launches, each the pair (f16 form, fp32 form) of dispatches."""
+    import csv
+    rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    ev = [(_short_kernel(r["Kernel_Name"]), int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows]
+    ours = ("logits", "topk", "refine", "slab", "key_bound")
+    steps, i = [], 0
+    while i < len(ev):
+        if not ev[i][0].startswith("ragged_kernel"):
+            i += 1
+            continue
+        k = i
+        while k + 1 < len(ev) and ev[k + 1][0].startswith(ours):
+            k += 1
+        steps.append(ev[i:k + 1])
+        i = k + 1
+    print(f"{len(steps)} fused steps (each from its window kernel to its last refinement)\n")
+    if steps:
+        names = []
+        for st in steps:
+            for n, _, _ in st:
+                if n not in names:
+                    names.append(n)
+        print("| kernel | dispatches per step | mean us per dispatch | us per step |")
+        print("|---|---|---|---|")
+        for n in names:
+            per = [[(b - a) / 1e3 for m, a, b in st if m == n] for st in steps]
+            allv = [x for v in per for x in v]
+            print(f"| `{n}` | {len(allv) / len(steps):.0f} | {np.mean(allv):.1f} | {np.mean([sum(v) for v in per]):.0f} |")
+        spans = [(st[-1][2] - st[0][1]) / 1e3 for st in steps]
+        busy = [sum(b - a for _, a, b in st) / 1e3 for st in steps]
+        print("\nstep spans (us): " + ", ".join(f"{x:.0f}" for x in spans)
+              + "; kernel time per step (us): " + ", ".join(f"{x:.0f}" for x in busy))
+    # roofline: runs of consecutive block-store scoring dispatches
+    runs, cur = [], []
+    for n, a, b in ev:
+        if n.startswith(scoring):
+            cur.append((n, a, b))
+        else:
+            if len(cur) >= 16:
+                runs.append(cur)
+            cur = []
+    if len(cur) >= 16:
+        runs.append(cur)
+    for r in runs:
+        f16 = [(b - a) / 1e3 for n, a, b in r if n.endswith("true>")]
+        f32 = [(b - a) / 1e3 for n, a, b in r if n.endswith("false>")]
+        pairs = [(r[j + 1][2] - r[j][1]) / 1e3 for j in range(0, len(r) - 1, 2)
+                 if r[j][0].endswith("true>") and r[j + 1][0].endswith("false>")]
+        print(f"\nroofline run: {len(pairs)} launches of `{scoring}...>`: f16 form mean {np.mean(f16):.1f} us "
+              f"(median {np.median(f16):.1f}), fp32 form mean {np.mean(f32):.1f} us, launch (first start to "
+              f"second end) mean {np.mean(pairs):.1f} us, median {np.median(pairs):.1f} us")
 
 
 def extras(dev, stream, glm, dsv4):
@@ -526,9 +625,19 @@ def main():
     ap.add_argument("--traffic-probe", action="store_true", help="only the launches for a counter run")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two traffic-probe counter runs (no GPU)")
+    ap.add_argument("--mfma-summary", metavar="PMC_DIR",
+                    help="summarise a traffic-probe run with the MFMA counters (no GPU)")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR",
+                    help="summarise a rocprofv3 --kernel-trace run of the headline bench (no GPU)")
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the indexer shards by "

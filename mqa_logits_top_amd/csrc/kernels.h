@@ -55,6 +55,12 @@ struct LogitsArgs {
   // only a small part of the keys (a ragged batch of short requests) then spreads its active
   // workgroups over every XCD instead of the few that own the splits those windows touch.
   const uint32_t *by_row;
+  // Launch pair marker (filled by launch_logits): a scoring launch is an f16 form and an fp32
+  // form over the same grid.  An f16-form workgroup whose rows hold a head weight below zero
+  // raises *neg_seq to seq (atomic max, a device word); fp32-form workgroups find nothing to
+  // do unless *neg_seq >= seq.  seq grows with every launch pair in the process.
+  unsigned long long *neg_seq;
+  unsigned long long seq;
 };
 
 hipError_t launch_logits(const LogitsArgs &a, int k_fmt, int H, int mode, hipStream_t s);

@@ -4,8 +4,18 @@
 // Folding the positive scales out of the ReLU is exact in real arithmetic
 // (max(0, a x) = a max(0, x) for a >= 0).  The contraction over D = 128 runs on
 // v_mfma_scale_f32_16x16x128_f8f6f4; the ReLU, head weighting and head sum run
-// on the VALU straight from the accumulators (P1 section 1: the dense indexer
-// scores T rows against the whole prefix; P2 Motivation: fp8 q x fp4 k).
+// straight from the accumulators, on an f16 MFMA or on the VALU (P1 section 1: the
+// dense indexer scores T rows against the whole prefix; P2 Motivation: fp8 q x fp4 k).
+//
+// Two forms of the kernel serve one launch, over the same grid; each workgroup
+// works in one of them, by its rows' head weights.
+//   f16 form (every weight >= 0): the fp8 MFMA runs with an A-scale of 2^-SA, so
+//   every possible dot lies in (-1, 1); one clamping conversion to f16 per two
+//   values is the ReLU; an f16 MFMA whose A holds each query's weights (hi and lo
+//   f16 parts, block-diagonal) sums the heads, one per two fp8 MFMAs.  The terms
+//   carry f16 rounding (2^-11 relative), which bounds the score's relative error
+//   only when no weight is negative.
+//   fp32 form (any other row): ReLU and weighted head sum as an fp32 FMA chain.
 //
 // Operand layout of v_mfma_scale_f32_16x16x128_f8f6f4, as measured on gfx950:
 // lane l holds row (A) / column (B) l % 16; for fp8, byte b of lane group
@@ -19,8 +29,8 @@
 // (QR = 128 / H: HPT = 4 for H = 32, 8 for H = 64), and a wave owns NT = 8
 // such tiles: all H heads of its QR query rows, held in registers (64 VGPRs of
 // q, 32 of w') for the whole launch.  Lane l then accumulates heads of query
-// (4 (l / 16)) / HPT for key l % 16, so the head sum is an in-lane FMA chain
-// plus, for H = 64, one v_permlane16_swap add.
+// (4 (l / 16)) / HPT for key l % 16, so the fp32 form's head sum is an in-lane FMA
+// chain plus, for H = 64, one v_permlane16_swap add.
 //
 // Keys stream through LDS in 16 KiB stages (128 fp8 keys or 256 MXFP4 keys),
 // triple buffered and written by the memory system directly
@@ -34,9 +44,9 @@
 // consecutive keys of its query row (one 16-byte store, one 16-byte k_scale
 // read, an in-lane 8-key max).
 // Output stores go through a buffer resource; lanes with nothing to store get
-// an out-of-range offset, so stores never branch.  The ReLU is one integer max
-// on the bits, and MFMA results land in VGPRs (built with VGPR-form MFMA), so
-// the epilogue costs 2 VALU ops per (t, h, s).
+// an out-of-range offset, so stores never branch.  MFMA results land in VGPRs
+// (VGPR-form MFMA): the fp32 form's epilogue costs 2 VALU ops per (t, h, s) (a
+// max and an FMA), the f16 form's half an op plus a quarter of an f16 MFMA.
 //
 // Grid: (row blocks of RPW rows) x (nsplit key splits), in one of two layouts
 // (workgroup b runs on XCD b % 8, round-robin dispatch).  By key split (the
@@ -132,7 +142,7 @@ __device__ __forceinline__ int swz8(int n) { return (n & 7) ^ ((n >> 3) & 1); }
 __device__ __forceinline__ int swz4(int n) { return ((n >> 1) ^ (n >> 3)) & 3; }
 
 template <int KF, int H, int MODE, int NW, bool F16>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(!F16 && (MODE == STORE_CAND || MODE == STORE_SLAB) && H == 32 ? 2 : 3))) void logits_kernel(LogitsArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(!F16 && MODE != STORE_DENSE && MODE != STORE_BLOCK ? 2 : 3))) void logits_kernel(LogitsArgs a) {
   constexpr int QR = 128 / H;            // query rows per wave
   constexpr int HPT = 16 / QR;           // heads of one row in a 16-row A tile
   constexpr int NT = H / HPT;            // A tiles per wave (8)
@@ -157,6 +167,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(!F16 &&
   // take part `part` of `nparts` of a later item.  With splits and remainder in whole
   // multiples of 8, a remainder workgroup stays on the XCD of its item's split
   // (workgroup b runs on XCD b % 8, and so do the splits s with s % 8 == b % 8).
+  // fp32 form: nothing to do unless an f16-form workgroup of this launch pair found rows
+  // with a negative head weight (uniform)
+  if (!F16 && *a.neg_seq < a.seq) return;
   const int b = blockIdx.x;
   int item = b, part = 0, nparts = 1;
   if (b >= a.nfull) {
@@ -212,7 +225,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(!F16 &&
   __syncthreads();
   // the launch pair splits the workgroups by their rows' head weights: the F16 form takes those
   // whose weights are all >= 0, the fp32 form the others
-  if ((wg_range[3] != 0) == F16) return;   // uniform
+  if (F16 && wg_range[3] != 0) {   // uniform
+    if (tid == 0) atomicMax(a.neg_seq, a.seq);
+    return;
+  }
+  if (!F16 && wg_range[3] == 0) return;   // uniform
   int s_lo, s_hi;
   if (by_row) {
     // The row block's items share the tiles of its rows' window union evenly, in key
@@ -638,10 +655,40 @@ hipError_t launch4(const LogitsArgs &a0, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Both forms over the same grid: each workgroup works in exactly one of them.
+// The launch pair marker word, one per device (its address looked up once per device).
+static __device__ unsigned long long neg_seq_word;
+std::atomic<unsigned long long *> neg_seq_on_device[64];
+std::atomic<unsigned long long> neg_seq_next{0};
+
+hipError_t neg_seq_address(unsigned long long **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  unsigned long long *p = neg_seq_on_device[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void *v = nullptr;
+    e = hipGetSymbolAddress(&v, HIP_SYMBOL(neg_seq_word));
+    if (e != hipSuccess) return e;
+    if (!v) return hipErrorInvalidSymbol;
+    p = (unsigned long long *)v;
+    neg_seq_on_device[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+// Both forms over the same grid: each workgroup works in exactly one of them.  The fp32 form
+// leaves at once unless the f16 form marked the pair.  Concurrent launch pairs on one device
+// (other streams) can only make an fp32 form look at its rows' weights needlessly: the word
+// only grows, and a pair's own mark is in place before its fp32 form starts.
 template <int KF, int H, int MODE>
-hipError_t launch3(const LogitsArgs &a, hipStream_t s) {
-  const hipError_t e = launch4<KF, H, MODE, true>(a, s);
+hipError_t launch3(const LogitsArgs &a0, hipStream_t s) {
+  LogitsArgs a = a0;
+  hipError_t e = neg_seq_address(&a.neg_seq);
+  if (e != hipSuccess) return e;
+  a.seq = neg_seq_next.fetch_add(1, std::memory_order_relaxed) + 1;
+  e = launch4<KF, H, MODE, true>(a, s);
   if (e != hipSuccess) return e;
   return launch4<KF, H, MODE, false>(a, s);
 }

@@ -335,13 +335,17 @@ __global__ __launch_bounds__(NTH) void refine_kernel(RefineArgs a) {
       anyneg |= sm.red[0][w];
     }
     double D = (double)GAMMA * 0.0001220703125 * (double)kmax * (double)S * 1.0000001;
-    // Rows whose weights are all >= 0 may have been scored in F16 form: each ReLU term rounded
-    // to f16 (relative error <= 2^-11 of the term, so <= 2^-11 of the score when all weights are
-    // >= 0; counted twice here), or, below f16's normal range, by at most 2^-25 of the term's
-    // 2^-SA scale (its score-unit size is |w'_h| 2^(SA - 25) times the key's factor).
+    // Rows whose weights are all >= 0 may have been scored in the f16 form: each ReLU term is
+    // rounded to f16, off by at most 2^-11 of itself (so, with no weight below zero, by at most
+    // 2^-11 of the score) or, below f16's normal range, by at most 2^-25 of the 2^SA-sized unit
+    // the terms are scaled by (|w'_h| 2^(SA - 25) times the key's scale factor in score units);
+    // the truncation error above passes through that rounding (factor 1 + 2^-11).  A key on
+    // either side of the band then stays on its side when D covers 2^-11 of the scores near
+    // theta plus the absolute terms; 2^-9 more covers theta's own error and the fp32 sums.
     if (!anyneg) {
-      const double SA = a.k_fmt == 0 ? 25.0 : 19.0;
-      D += 0.0009765625 * fabs((double)theta) + 2.0 * ldexp((double)WS * (double)kfac, (int)SA - 25);
+      const int SA = a.k_fmt == 0 ? 25 : 19;
+      D = (D * (1.0 + 0x1p-10) + 0x1p-11 * fabs((double)theta) + ldexp((double)WS * (double)kfac, SA - 25)) *
+          (1.0 + 0x1p-9);
     }
     const double lo = (double)theta - 2.0 * D, hi = (double)theta + 2.0 * D;
 

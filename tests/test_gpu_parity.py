@@ -554,3 +554,35 @@ def test_fused_candidates_unaligned_windows(k_fmt, H, block_k, row_chunk, n_bloc
     mk = mask.cpu().numpy()
     allowed = [mk[t, :len(o[t])].astype(bool) for t in range(T)]
     topk_ok(bi.cpu().numpy(), bv.cpu().numpy(), o, dq.ks, K, allowed=allowed)
+
+
+@pytest.mark.parametrize("H,fmt", [(32, synth.K_FP8), (64, synth.K_MXFP4)])
+def test_rows_of_both_scoring_forms_in_one_launch(H, fmt):
+    """A few rows carry one negative head weight among rows that carry none: one scoring
+    launch then has workgroups in its f16 form and in its fp32 form.  Rows whose own weights
+    are all >= 0 meet the plain logit bar whichever form scored them; every row's selection
+    is exact; calls repeated around a call whose weights are all >= 0 give the same bits."""
+    import dataclasses
+    T, L, K = 70, 3000, 300
+    p = synth.make_problem(T, L, H, k_fmt=fmt, seed=91 + H)
+    w = p.w.copy()
+    neg_rows = np.arange(3, T, 23)
+    w[neg_rows, 5] = -0.7
+    pm = dataclasses.replace(p, w=w)
+    dm, dp = dev(pm), dev(p)
+    dq = oracle.Dequantised(pm)
+    o = oracle.rows_logits(dq, range(T))
+    lg = idx.idx_mqa_logits(dm, dm.W).cpu().numpy()
+    ref = dense_ref(o, dm.W)
+    pos = np.setdiff1d(np.arange(T), neg_rows)
+    logits_ok(lg[pos], ref[pos], "logits of rows with weights >= 0")
+    fi, fv = idx.idx_logits_topk_fused(dm, K, block_k=1024)
+    topk_ok(fi.cpu().numpy(), None, o, dq.ks, K)
+    for i in pos:
+        topk_ok(fi[i:i + 1].cpu().numpy(), fv[i:i + 1].cpu().numpy(), o[i:i + 1], dq.ks[i:i + 1], K,
+                what=f"row {i}")
+    idx.idx_logits_topk_fused(dp, K, block_k=1024)
+    fi2, fv2 = idx.idx_logits_topk_fused(dm, K, block_k=1024)
+    assert torch.equal(fi, fi2) and torch.equal(fv.view(torch.int32), fv2.view(torch.int32))
+    lg2 = idx.idx_mqa_logits(dm, dm.W).cpu().numpy()
+    assert np.array_equal(lg.view(np.int32), lg2.view(np.int32))
