@@ -102,16 +102,21 @@ def time_events(fn, n, stream):
     return [a.elapsed_time(b) for a, b in evs]
 
 
-def launch_keys(L, block_k):
-    """Keys per scoring launch of the fused path: key blocks go in pairs."""
-    return max(block_k, min(2 * block_k, (L + 255) // 256 * 256))
+def key_launches(L, block_k):
+    """(key0, keys) of the fused path's scoring launches over one row chunk: B_k keys first,
+    then up to two blocks per launch, spread evenly over the keys left."""
+    if L <= block_k:
+        return [(0, L)]
+    rest = L - block_k
+    n2 = -(-rest // (2 * block_k))
+    step = -(-(-(-rest // n2)) // 256) * 256
+    return [(0, block_k)] + [(kb, min(step, L - kb)) for kb in range(block_k, L, step)]
 
 
 def launch_rects(d, block_k, row_chunk):
     """The (row0, rows, key0, keys) rectangles the fused path scores, one per launch."""
     Tc = d.T if row_chunk <= 0 else min(row_chunk, d.T)
-    lk = launch_keys(d.L, block_k)
-    return [(r0, min(Tc, d.T - r0), kb, min(lk, d.L - kb)) for r0 in range(0, d.T, Tc) for kb in range(0, d.L, lk)]
+    return [(r0, min(Tc, d.T - r0), kb, nk) for r0 in range(0, d.T, Tc) for kb, nk in key_launches(d.L, block_k)]
 
 
 def rect_pairs(d, r0, nr, kb, nk):
@@ -372,7 +377,7 @@ def traffic_summary(fetch_dir, write_dir):
         w = launch_pairs([v * factor["WRITE_SIZE"] for n, v, _, _ in rows["WRITE_SIZE"] if kname in n])[-2:]
         p = synth.make_config(name)
         Tc = p.T if ROW_CHUNK[name] <= 0 else min(ROW_CHUNK[name], p.T)
-        rect = [Tc, min(launch_keys(p.L, p.meta["block_k"]), p.L)]
+        rect = [Tc, max(nk for _, nk in key_launches(p.L, p.meta["block_k"]))]
         rec = {"kernel_source_hash": kernel_source_hash(), "rect": rect,
                "bytes_per_launch": float(np.mean(f) + np.mean(w)), "fetch_bytes_per_launch": float(np.mean(f)),
                "write_bytes_per_launch": float(np.mean(w)), "fetch_factor": factor["FETCH_SIZE"],

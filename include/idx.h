@@ -159,12 +159,15 @@ idx_status idx_topk(const float *logits, int64_t ld, int32_t W, const int32_t *k
                     const uint8_t *mask, int64_t ld_mask, int32_t T, int32_t K, int32_t block_k,
                     int32_t *out_idx, float *out_val, void *ws, size_t ws_bytes, void *stream);
 
-/* Fused key-blocked indexer (P1 section 2.3): for each chunk of row_chunk rows
- * and each key block of block_k keys, score the block into workspace and merge
- * its top-(K + 512) into the running candidates of those rows; then settle the
- * boundary exactly (idx_refine_topk).  Blocks are scored two per launch.  [T, L]
- * logits are never materialised: workspace is O(row_chunk * (block_k + K)),
- * independent of L.  The result
+/* Fused key-blocked indexer (P1 section 2.3): for each chunk of row_chunk rows,
+ * score its first key block of block_k keys into a [row_chunk, block_k] fp32
+ * scratch and take each row's top-(K + 512) from it; every later launch (up to
+ * two blocks of keys) writes only the scores above each row's running
+ * (K + 512)-th to per-row candidate slabs, which are merged into the running
+ * lists (rows whose slabs overflow are scored again into the scratch, one block
+ * at a time); then settle the boundary exactly (idx_refine_topk).  [T, L] logits
+ * are never materialised: the workspace is O(row_chunk * (block_k + K)) and
+ * stops growing with L once L exceeds 3 block_k.  The result
  * equals idx_mqa_logits + idx_topk (K + 512 columns) + idx_refine_topk
  * bitwise.  mask (nullable):
  * [T, ld_mask] bytes, column j <-> key ks[t] + j (the candidate mask of

@@ -132,22 +132,45 @@ int32_t block_slabs(int32_t Bk) {
   plan_splits(Bk, split, nsplit);
   return nsplit;
 }
-size_t slab_ws(int32_t Tc, int32_t Bk) {
-  const size_t ns = (size_t)block_slabs(Bk);
+// Thresholds, slab-check flags, count words and (value, id) pairs of ns slabs per row;
+// then the per-row words of the two-call top-K of a launch wider than B_k.
+size_t slab_ws(int32_t Tc, int32_t ns) {
   return round_up_sz((size_t)Tc * 4, 256) + round_up_sz((size_t)(Tc / 8 + 1) * 4, 256) +
          round_up_sz((size_t)Tc * ns * idx::CAND_PARTS * 4, 256) +
-         round_up_sz((size_t)Tc * ns * CAPS * 8, 256);
+         round_up_sz((size_t)Tc * ns * CAPS * 8, 256) + round_up_sz((size_t)Tc * 4, 256);
 }
-// Keys per scoring and top-K launch of the fused path: key blocks go in pairs (the
-// top-K still merges block by block), so that a launch holds twice the work items.
-// Its last wave of workgroups, which drains with fewer workgroups per CU, is then a
-// smaller share of the launch (glm_chunk fused step -4%, dsv4_mxfp4 -6%).  The
-// workspace stays proportional to the row chunk times B_k, whatever the keys.
-constexpr int32_t BLOCKS_PER_LAUNCH = 2;
-int32_t launch_keys(const idx_problem *p, int32_t Bk) {
-  const int32_t all = round_up(p->L > 0 ? p->L : 1, KEY_ALIGN);
-  return std::max(Bk, std::min(BLOCKS_PER_LAUNCH * Bk, all));
+// Key launches of the fused path (P1 section 2.3: key blocks scored one after another, each
+// row's running top-K merged across them; memory c * T * B_k).  The first launch of a row
+// chunk scores B_k keys into the [Tc, B_k] score scratch, from which the top-K builds each
+// row's running list and threshold.  Every later launch writes only the scores above that
+// threshold, to candidate slabs, and takes up to two blocks' keys (spread evenly over the
+// keys left), so that it holds more work items: its last wave of workgroups, which drains
+// with fewer workgroups per CU, is then a smaller share of it.  Rows whose slabs overflow
+// are scored again into the scratch, one block at a time.  Without slabs (a consumer mask,
+// or too many rows for the slab index range) every launch takes one block.
+struct KeySchedule {
+  int32_t first, step, n;   // keys of launch 0, of every later launch; launches
+  int32_t start(int32_t l) const { return l == 0 ? 0 : first + (l - 1) * step; }
+};
+KeySchedule key_schedule(const idx_problem *p, int32_t Bk, bool pairs) {
+  KeySchedule k{Bk, Bk, 1};
+  const int64_t L = p->L > 0 ? p->L : 0;
+  if (L <= Bk) return k;
+  const int64_t rest = L - Bk;
+  if (pairs) {
+    const int64_t n2 = (rest + 2 * (int64_t)Bk - 1) / (2 * (int64_t)Bk);
+    k.step = (int32_t)(((rest + n2 - 1) / n2 + KEY_ALIGN - 1) / KEY_ALIGN * KEY_ALIGN);   // <= 2 B_k
+  }
+  k.n = (int32_t)(1 + (rest + k.step - 1) / k.step);
+  return k;
 }
+// Slabs per row of the widest later launch.
+int32_t schedule_slabs(const KeySchedule &k, int32_t L) {
+  if (k.n <= 1) return 0;
+  return std::max(block_slabs(std::min(k.step, L - k.start(1))), block_slabs(L - k.start(k.n - 1)));
+}
+// Slab pair indices of a launch stay within int32 for row chunks below this.
+bool slabs_fit(int32_t Tc, int32_t ns) { return (int64_t)Tc * ns * CAPS * 8 < INT32_MAX; }
 // Row gather: q [R, H, D] bytes, q_scale and w [R, H] floats, ks and ke [R].
 size_t gather_ws(int32_t R, int32_t H, int32_t D) {
   return round_up_sz((size_t)R * H * D, 256) + 2 * round_up_sz((size_t)R * H * 4, 256) +
@@ -155,29 +178,34 @@ size_t gather_ws(int32_t R, int32_t H, int32_t D) {
 }
 // Window flags of the scoring launches (idx::WindowFlags), a fixed region.
 constexpr size_t FLAGS_WS = (size_t)idx::MAX_WINDOW_FLAGS * 4;
-size_t fused_ws(int32_t Tc, int32_t Bk, int32_t K) {
-  return refine_ws(Tc, cand_cap(K)) + round_up_sz((size_t)Tc * pitch(Bk) * 4, 256) + slab_ws(Tc, Bk) + FLAGS_WS;
+// The fused path's workspace: refinement, the [Tc, B_k] score scratch, the slabs of the
+// two-block schedule (the widest the call can take) and the window flags.
+size_t fused_ws(const idx_problem *p, int32_t Tc, int32_t Bk, int32_t K) {
+  const int32_t ns = schedule_slabs(key_schedule(p, Bk, true), p->L);
+  return refine_ws(Tc, cand_cap(K)) + round_up_sz((size_t)Tc * pitch(Bk) * 4, 256) + slab_ws(Tc, ns) + FLAGS_WS;
 }
 size_t cand_ws(int32_t Tc, int32_t pooled_cols, int32_t n_blocks, bool fused) {
   return refine_ws(Tc, cand_cap(n_blocks)) + round_up_sz((size_t)Tc * pitch(pooled_cols) * 4, 256) +
          round_up_sz((size_t)Tc * n_blocks * 4, 256) + (fused ? FLAGS_WS : 0);
 }
-// The flags of a call whose row chunks of Tc rows meet key launches of LB keys (nullptr in
+// The flags of a call whose row chunks of Tc rows meet the key launches of `k` (nullptr in
 // `flags` when there would be more than the region holds: the launches then stay by key split).
-idx::WindowFlags window_flags(const idx_problem *p, int32_t Tc, int32_t LB, uint32_t *region) {
+idx::WindowFlags window_flags(const idx_problem *p, int32_t Tc, const KeySchedule &k, uint32_t *region) {
   idx::WindowFlags f{};
   f.ks = p->ks;
   f.ke = p->ke;
   f.T = p->T;
   f.Tc = Tc;
-  f.LB = LB;
-  f.nlaunch = p->L > 0 ? (p->L + LB - 1) / LB : 0;
+  f.first = k.first;
+  f.LB = k.step;
+  f.nlaunch = p->L > 0 ? k.n : 0;
   const int64_t n = (int64_t)((p->T + Tc - 1) / Tc) * f.nlaunch;
   f.flags = n > 0 && n <= idx::MAX_WINDOW_FLAGS ? region : nullptr;
   return f;
 }
 const uint32_t *launch_flag(const idx::WindowFlags &f, int32_t r0, int32_t kb) {
-  return f.flags ? f.flags + (int64_t)(r0 / f.Tc) * f.nlaunch + kb / f.LB : nullptr;
+  const int32_t l = kb < f.first ? 0 : 1 + (kb - f.first) / f.LB;
+  return f.flags ? f.flags + (int64_t)(r0 / f.Tc) * f.nlaunch + l : nullptr;
 }
 
 struct RefineWs {
@@ -262,7 +290,7 @@ idx_status idx_workspace_size(int32_t op, const idx_problem *p, int32_t K, int32
       if (K < 1 || K > MAX_K) return IDX_E_PARAM;
       const int32_t Bk = eff_block(p, block_k);
       if (check_block(Bk) != IDX_OK) return IDX_E_PARAM;
-      *bytes = fused_ws(Tc, launch_keys(p, Bk), K);
+      *bytes = fused_ws(p, Tc, Bk, K);
       return IDX_OK;
     }
     case IDX_OP_BLOCK_CANDIDATES: {
@@ -383,17 +411,16 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
   if (!aligned(out_idx, 4) || (out_val && !aligned(out_val, 4)) || (out_slot && !aligned(out_slot, 4)) ||
       (slot_of_key && !aligned(slot_of_key, 4)))
     return IDX_E_ALIGN;
-  const int32_t LB = launch_keys(p, Bk);
   int32_t bsh = 0;
   if (blocks) {
     if (mask) return IDX_E_PARAM;                        // one consumer at a time
     if (n_blocks < 0 || ld_blocks < n_blocks) return IDX_E_SHAPE;
     if (pool < 1 || (pool & (pool - 1))) return IDX_E_UNSUPPORTED;
     while ((1 << bsh) < pool) ++bsh;
-    if (((LB - 1) >> bsh) + 2 > idx::BMAP_BITS) return IDX_E_UNSUPPORTED;   // blocks of one launch
+    if (((Bk - 1) >> bsh) + 2 > idx::BMAP_BITS) return IDX_E_UNSUPPORTED;   // blocks of one launch
     if (!aligned(blocks, 4)) return IDX_E_ALIGN;
   }
-  const size_t need = fused_ws(Tc, LB, K);
+  const size_t need = fused_ws(p, Tc, Bk, K);
   if (p->T == 0) return IDX_OK;
   if (ws_bytes < need) return IDX_E_WORKSPACE;
   // a workspace the library provides is looked up only once every host check has passed
@@ -405,67 +432,32 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
   const int32_t Kc = cand_cap(K);
   Carve cv{(uint8_t *)ws};
   RefineWs rw = carve_refine(cv, Tc, Kc);
-  const int32_t sld = pitch(LB);
+  const int32_t sld = pitch(Bk);
   float *scratch = cv.take<float>((size_t)Tc * sld);
-  const int32_t nslab_max = block_slabs(LB);
+  const int32_t nslab_max = schedule_slabs(key_schedule(p, Bk, true), p->L);
   float *thr = cv.take<float>((size_t)Tc);
   uint32_t *ovf = cv.take<uint32_t>((size_t)Tc / 8 + 1);   // per scoring row block (>= 8 rows)
   uint32_t *ccnt = cv.take<uint32_t>((size_t)Tc * nslab_max * idx::CAND_PARTS);
   uint32_t *slab = cv.take<uint32_t>((size_t)Tc * nslab_max * CAPS * 2);
-  const idx::WindowFlags wf = window_flags(p, Tc, LB, cv.take<uint32_t>(idx::MAX_WINDOW_FLAGS));
+  uint32_t *col_rows = cv.take<uint32_t>((size_t)Tc);
+  // slabs for every launch after the first; two blocks per launch unless a consumer mask
+  // asks for scores and slabs in one pass
+  const bool slab_ok = slabs_fit(Tc, nslab_max);
+  const KeySchedule ksch = key_schedule(p, Bk, slab_ok && !mask && !blocks);
+  const idx::WindowFlags wf = window_flags(p, Tc, ksch, cv.take<uint32_t>(idx::MAX_WINDOW_FLAGS));
   if ((st = launched(idx::launch_key_bound((const uint8_t *)p->k, (const uint8_t *)p->k_scale, p->k_fmt, p->L,
                                            rw.kpart, rw.overflow, &wf, s))))
     return st;
   for (int32_t r0 = 0; r0 < p->T; r0 += Tc) {
     const int32_t nr = std::min(Tc, p->T - r0);
-    int32_t kb = 0;
-    do {
-      const int32_t nk = std::min(LB, p->L - kb);
-      // launches after the first write only the scores above each row's running threshold,
-      // to candidate slabs; the row blocks where a slab overflowed are then scored again into
-      // the scratch, which the top-K reads for those rows
-      bool slabs = false;
-      int32_t nslab = 0;
-      if (nk > 0) {
-        idx::LogitsArgs a = logits_args(p, r0, nr, kb, kb + nk, scratch, sld, nk);
-        a.by_row = launch_flag(wf, r0, kb);
-        slabs = kb >= slab_from(p) * LB && a.nsplit <= nslab_max && (int64_t)nr * a.nsplit * CAPS * 8 < INT32_MAX;
-        nslab = a.nsplit;
-        if (slabs && !mask && !blocks) {
-          idx::LogitsArgs c = a;
-          c.thr = thr;
-          c.cand = slab;
-          c.ccnt = ccnt;
-          c.caps = CAPS;
-          if ((st = launched(idx::launch_logits(c, p->k_fmt, p->H, idx::STORE_SLAB, s)))) return st;
-          const int32_t rpw = idx::logits_rows_per_workgroup(p->H);
-          if ((st = launched(idx::launch_slab_check(ccnt, a.nsplit * idx::CAND_PARTS, thr, nr, rpw, ovf, s))))
-            return st;
-          a.only_flagged = ovf;
-          if ((st = launched(idx::launch_logits(a, p->k_fmt, p->H, idx::STORE_BLOCK, s)))) return st;
-        } else if (slabs) {
-          // a consumer mask the scoring kernel does not see would fill the slabs with keys the
-          // top-K then drops: score the block and the slabs in one pass instead
-          a.thr = thr;
-          a.cand = slab;
-          a.ccnt = ccnt;
-          a.caps = CAPS;
-          if ((st = launched(idx::launch_logits(a, p->k_fmt, p->H, idx::STORE_CAND, s)))) return st;
-        } else if ((st = launched(idx::launch_logits(a, p->k_fmt, p->H, idx::STORE_BLOCK, s)))) {
-          return st;
-        }
-      }
+    for (int32_t l = 0; l < ksch.n; ++l) {
+      const int32_t kb = ksch.start(l);
+      const int32_t nk = std::max(0, std::min(l == 0 ? ksch.first : ksch.step, p->L - kb));
       idx::TopkArgs b{};
-      if (slabs) {
-        b.cand = slab;
-        b.ccnt = ccnt;
-        b.nslab = nslab;
-        b.caps = CAPS;
-      }
       b.thr_out = thr;
       b.vals = scratch;
       b.ld = sld;
-      b.ncols = nk > 0 ? nk : 0;
+      b.ncols = nk;
       b.block = Bk;
       b.ks = p->ks;
       b.ke = p->ke;
@@ -484,10 +476,64 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
       b.K = Kc;
       b.out_idx = rw.cidx;
       b.out_val = rw.cval;
-      b.first = kb == 0;
+      b.first = l == 0;
+      idx::LogitsArgs a = logits_args(p, r0, nr, kb, kb + nk, scratch, sld, nk);
+      a.by_row = launch_flag(wf, r0, kb);
+      const bool slabs = l > 0 && nk > 0 && slab_ok && a.nsplit <= nslab_max;
+      if (slabs && !mask && !blocks) {
+        // the launch writes the scores above each row's running threshold to its slabs; the
+        // row blocks where a slab overflowed are scored again into the scratch, one block of
+        // keys per pass, and the top-K reads those rows' columns there
+        idx::LogitsArgs c = a;
+        c.thr = thr;
+        c.cand = slab;
+        c.ccnt = ccnt;
+        c.caps = CAPS;
+        if ((st = launched(idx::launch_logits(c, p->k_fmt, p->H, idx::STORE_SLAB, s)))) return st;
+        const int32_t rpw = idx::logits_rows_per_workgroup(p->H);
+        if ((st = launched(idx::launch_slab_check(ccnt, a.nsplit * idx::CAND_PARTS, thr, nr, rpw, ovf, s))))
+          return st;
+        for (int32_t h0 = 0; h0 < nk; h0 += Bk) {
+          const int32_t hn = std::min(Bk, nk - h0);
+          idx::LogitsArgs f = logits_args(p, r0, nr, kb + h0, kb + h0 + hn, scratch, sld, hn);
+          f.by_row = a.by_row;
+          f.only_flagged = ovf;
+          if ((st = launched(idx::launch_logits(f, p->k_fmt, p->H, idx::STORE_BLOCK, s)))) return st;
+          idx::TopkArgs bh = b;
+          if (h0 == 0) {   // slab merges, and the first block's columns for the other rows
+            bh.cand = slab;
+            bh.ccnt = ccnt;
+            bh.nslab = a.nsplit;
+            bh.caps = CAPS;
+            bh.vcols = hn;
+            bh.col_rows = nk > Bk ? col_rows : nullptr;
+          } else {         // the next block's columns, for the rows that read columns
+            bh.key0 = kb + h0;
+            bh.ncols = hn;
+            bh.only_rows = col_rows;
+          }
+          if ((st = launched(idx::launch_topk(bh, s)))) return st;
+        }
+        continue;
+      }
+      if (nk > Bk) return IDX_E_UNSUPPORTED;   // the scratch holds one block (not reached: see key_schedule)
+      if (slabs) {
+        // a consumer mask the scoring kernel does not see would fill the slabs with keys the
+        // top-K then drops: score the block and the slabs in one pass instead
+        a.thr = thr;
+        a.cand = slab;
+        a.ccnt = ccnt;
+        a.caps = CAPS;
+        b.cand = slab;
+        b.ccnt = ccnt;
+        b.nslab = a.nsplit;
+        b.caps = CAPS;
+        if ((st = launched(idx::launch_logits(a, p->k_fmt, p->H, idx::STORE_CAND, s)))) return st;
+      } else if (nk > 0 && (st = launched(idx::launch_logits(a, p->k_fmt, p->H, idx::STORE_BLOCK, s)))) {
+        return st;
+      }
       if ((st = launched(idx::launch_topk(b, s)))) return st;
-      kb += LB;
-    } while (kb < p->L);
+    }
     idx::RefineArgs r = refine_args(p, rw, r0, nr, Kc, K, 1, out_idx + (int64_t)r0 * K,
                                     out_val ? out_val + (int64_t)r0 * K : nullptr);
     r.slot_of_key = slot_of_key;
@@ -580,7 +626,7 @@ idx_status idx_block_candidates(const idx_problem *p, const float *logits, int64
   int32_t *kept = cv.take<int32_t>((size_t)Tc * n_blocks);
   idx::WindowFlags wf{};
   if (!logits) {
-    wf = window_flags(p, Tc, Bk, cv.take<uint32_t>(idx::MAX_WINDOW_FLAGS));
+    wf = window_flags(p, Tc, key_schedule(p, Bk, false), cv.take<uint32_t>(idx::MAX_WINDOW_FLAGS));
     if ((st = launched(idx::launch_key_bound((const uint8_t *)p->k, (const uint8_t *)p->k_scale, p->k_fmt, p->L,
                                              rw.kpart, rw.overflow, &wf, s))))
       return st;

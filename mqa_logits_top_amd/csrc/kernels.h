@@ -111,6 +111,13 @@ struct TopkArgs {
   const uint32_t *ccnt;
   int32_t nslab, caps;
   float *thr_out;         // nullable: per launch row, the full list's smallest value, else NaN
+  // A launch's columns in two calls: vcols > 0 limits the columns read from vals to [0, vcols)
+  // (rows still merge slabs over all ncols); col_rows (nullable) receives 1 for a row that read
+  // columns instead of merging its slabs, 0 for one that merged; a call with only_rows set
+  // serves only the rows whose word there is nonzero.
+  int32_t vcols;
+  uint32_t *col_rows;
+  const uint32_t *only_rows;
 };
 constexpr int BMAP_BITS = 9216;   // block bitmap of a top-K launch (65536 keys in 8-key blocks, and slack)
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
@@ -150,7 +157,8 @@ int key_bound_parts(int L);
 // workgroups out by row block), else 0.
 struct WindowFlags {
   const int32_t *ks, *ke;
-  int32_t T, Tc, LB, nlaunch;
+  int32_t T, Tc;
+  int32_t first, LB, nlaunch;   // launch 0 takes keys [0, first), launch l > 0 [first + (l - 1) LB, + LB)
   uint32_t *flags;
 };
 constexpr int32_t MAX_WINDOW_FLAGS = 16384;

@@ -568,7 +568,7 @@ __device__ void window_flag(const WindowFlags wf, int L, int f) {
   __shared__ double wred[4];
   const int c = f / wf.nlaunch, l = f % wf.nlaunch;
   const int r0 = c * wf.Tc, r1 = min(wf.T, r0 + wf.Tc);
-  const int klo = l * wf.LB, khi = min(L, klo + wf.LB);
+  const int klo = l == 0 ? 0 : wf.first + (l - 1) * wf.LB, khi = min(L, l == 0 ? wf.first : klo + wf.LB);
   double sum = 0.0;
   for (int r = r0 + (int)threadIdx.x; r < r1; r += 256) {
     const int lo = max(max(wf.ks[r], 0), klo), hi = min(min(wf.ke[r], L), khi);

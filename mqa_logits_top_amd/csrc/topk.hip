@@ -240,6 +240,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   // newest rows first: the scoring launch before this one wrote them last, so they are the
   // ones still held in the memory-side cache
   const int r = a.nrows - 1 - (int)blockIdx.x;
+  if (a.only_rows && a.only_rows[r] == 0u) return;   // uniform
   const int t = a.row0 + r;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -258,6 +259,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   }
   const int c_lo = max(id_lo - off, 0);
   const int c_hi = min(id_hi - off, a.ncols);
+  const int c_rd = min(c_hi, a.vcols > 0 ? a.vcols : a.ncols);   // columns present in vals
   int32_t *oidx = a.out_idx + (int64_t)r * K;
   float *oval = a.out_val ? a.out_val + (int64_t)r * K : nullptr;
   if (!a.first && c_lo >= c_hi) return;  // nothing new for this row: running state stays as is
@@ -382,8 +384,9 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     }
   }
 
-  for (int S = sbase; S < c_hi && !merged; S += seg) {
-    const int s0 = max(S, c_lo), s1 = min(S + seg, c_hi);  // valid columns of this segment
+  if (a.col_rows && tid == 0) a.col_rows[r] = merged ? 0u : 1u;
+  for (int S = sbase; S < c_rd && !merged; S += seg) {
+    const int s0 = max(S, c_lo), s1 = min(S + seg, c_rd);  // valid columns of this segment
 
     auto run_key = [&](int p) __attribute__((always_inline)) -> uint32_t { return sm.ikey[p]; };
     uint32_t floor_key = 0;

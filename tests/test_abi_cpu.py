@@ -152,19 +152,24 @@ def test_workspace_sizes(lib):
     p = _problem(T=2048, L=65536)
     n = ctypes.c_size_t()
     assert lib.idx_workspace_size(2, ctypes.byref(p), 2048, 32768, 0, 0, 0, 0, ctypes.byref(n)) == 0
-    # key blocks are scored in pairs: 65536 keys per launch, split 16 ways
-    # thresholds, overflow flags, count words (16 splits x 4 parts), (value, id) pairs (16 slabs of 512)
-    slab = lambda Tc: _r(Tc * 4) + _r((Tc // 8 + 1) * 4) + _r(Tc * 16 * 4 * 4) + _r(Tc * 16 * 512 * 8)
+    # scores of one block of B_k keys ([Tc, B_k + 64] fp32), then the slabs of the later launches:
+    # thresholds, overflow flags, count words (ns splits x 4 parts), (value, id) pairs (ns slabs
+    # of 512), the two-call top-K's row words.  Here keys [32768, 65536) in one launch: 8 splits.
+    slab = lambda Tc, ns: (_r(Tc * 4) + _r((Tc // 8 + 1) * 4) + _r(Tc * ns * 4 * 4) + _r(Tc * ns * 512 * 8)
+                           + _r(Tc * 4))
     flags = 16384 * 4   # window flags of the scoring launches, a fixed region
-    assert n.value == head + 2 * _r(2048 * kc(2048) * 4) + 2048 * (65536 + 64) * 4 + slab(2048) + flags
-    # the row chunk bounds the workspace; the number of keys does not enter
+    assert n.value == head + 2 * _r(2048 * kc(2048) * 4) + 2048 * (32768 + 64) * 4 + slab(2048, 8) + flags
+    # the row chunk and B_k bound the workspace: later launches take at most two blocks (16 splits)
     p2 = _problem(T=16384, L=487936)
     assert lib.idx_workspace_size(2, ctypes.byref(p2), 512, 32768, 4096, 0, 0, 0, ctypes.byref(n)) == 0
-    assert n.value == head + 2 * _r(4096 * kc(512) * 4) + 4096 * (65536 + 64) * 4 + slab(4096) + flags
-    p3 = _problem(T=16384, L=65536)
+    assert n.value == head + 2 * _r(4096 * kc(512) * 4) + 4096 * (32768 + 64) * 4 + slab(4096, 16) + flags
     m = ctypes.c_size_t()
+    p3 = _problem(T=16384, L=262144)
     assert lib.idx_workspace_size(2, ctypes.byref(p3), 512, 32768, 4096, 0, 0, 0, ctypes.byref(m)) == 0
     assert m.value == n.value
+    p4 = _problem(T=16384, L=65536)
+    assert lib.idx_workspace_size(2, ctypes.byref(p4), 512, 32768, 4096, 0, 0, 0, ctypes.byref(m)) == 0
+    assert m.value < n.value
     assert lib.idx_workspace_size(3, ctypes.byref(p), 0, 32768, 0, 8, 2048, 0, ctypes.byref(n)) == 0
     assert n.value == head + 2 * _r(2048 * kc(2048) * 4) + 2048 * (4096 + 64) * 4 + 2048 * 2048 * 4 + flags
     assert lib.idx_workspace_size(4, ctypes.byref(p), 0, 0, 1024, 8, 2048, 65536, ctypes.byref(n)) == 0

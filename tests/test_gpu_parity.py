@@ -165,11 +165,11 @@ def test_fused_equals_dense_refined_bitwise(case, block_k, row_chunk):
 
 
 def test_fused_slab_overflow_and_fit():
-    """Key blocks after the first merge their scoring-kernel candidate slabs when every
-    slab fits and read the whole block otherwise.  Scores are sums of non-negative terms
-    here, so scaling a block's keys up makes nearly all of them beat the running list:
-    the second block (x64) overflows its 512-entry slabs (1024-key splits) and falls back,
-    the third (x128, 512-key splits) fills its slabs exactly and merges them."""
+    """Launches after the first merge their scoring-kernel candidate slabs when every slab
+    fits and read the launch's scores otherwise.  Scores are sums of non-negative terms here,
+    so scaling keys up makes nearly all of them beat the running list: the second launch
+    (keys 8192..20000, two blocks scaled x64 and x128) overflows its 512-entry slabs, and its
+    rows read its scores from the one-block scratch, block by block."""
     T, L, H, K, Bk = 16, 20000, 64, 64, 8192   # H = 64: slabs from the second block on
     p = synth.make_problem(T, L, H, k_fmt=synth.K_FP8, seed=3)
     p.k_scale[Bk:2 * Bk] *= 64.0
@@ -184,6 +184,35 @@ def test_fused_slab_overflow_and_fit():
     di, dv = idx.idx_refine_topk(d, ci, cv, K)
     assert torch.equal(di, fi)
     assert torch.equal(dv.view(torch.int32), fv.view(torch.int32))
+
+
+def test_fused_two_block_launch_mixed_fallback():
+    """A launch of two key blocks where one row block's slabs overflow and the other's fit:
+    the overflowing rows read the launch's scores from the one-block scratch in two passes,
+    the others merge their slabs once and are left alone by the second pass (their windows
+    reach into the second block, whose scores the scratch does not hold for them).  Keys
+    8192..12288 are made non-negative and scaled x64; rows 8..15 have non-negative q (those
+    keys beat their whole running list), rows 0..7 non-positive q (those keys score 0)."""
+    T, L, H, K, Bk = 16, 40000, 64, 64, 8192
+    p = synth.make_problem(T, L, H, k_fmt=synth.K_FP8, seed=12)
+    p.k[8192:12288] &= 0x7F
+    p.k_scale[8192:12288] *= 64.0
+    p.q[8:16] &= 0x7F
+    p.q[0:8] |= 0x80
+    dq = oracle.Dequantised(p)
+    o = oracle.rows_logits(dq, range(T))
+    d = dev(p)
+    fi, fv = idx.idx_logits_topk_fused(d, K, block_k=Bk)
+    topk_ok(fi.cpu().numpy(), fv.cpu().numpy(), o, dq.ks, K)
+    lg = idx.idx_mqa_logits(d, d.W)
+    ci, cv = idx.idx_topk(lg, d.ks, d.ke, idx.candidate_capacity(K))
+    di, dv = idx.idx_refine_topk(d, ci, cv, K)
+    assert torch.equal(di, fi)
+    assert torch.equal(dv.view(torch.int32), fv.view(torch.int32))
+    # the scaled keys fill the top of rows 8..15 and none of rows 0..7
+    sel = fi.cpu().numpy()
+    assert ((sel[8:] >= 8192) & (sel[8:] < 12288)).all()
+    assert not ((sel[:8] >= 8192) & (sel[:8] < 12288)).any()
 
 
 @pytest.mark.parametrize("row_chunk", [0, 16])
