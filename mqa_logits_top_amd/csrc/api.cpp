@@ -180,9 +180,12 @@ size_t gather_ws(int32_t R, int32_t H, int32_t D) {
 constexpr size_t FLAGS_WS = (size_t)idx::MAX_WINDOW_FLAGS * 4;
 // The fused path's workspace: refinement, the [Tc, B_k] score scratch, the slabs of the
 // two-block schedule (the widest the call can take) and the window flags.
+// The row chunks' first window keys (WindowFlags::kshift).
+size_t shift_ws(const idx_problem *p, int32_t Tc) { return round_up_sz((size_t)((p->T + Tc - 1) / Tc + 1) * 4, 256); }
 size_t fused_ws(const idx_problem *p, int32_t Tc, int32_t Bk, int32_t K) {
   const int32_t ns = schedule_slabs(key_schedule(p, Bk, true), p->L);
-  return refine_ws(Tc, cand_cap(K)) + round_up_sz((size_t)Tc * pitch(Bk) * 4, 256) + slab_ws(Tc, ns) + FLAGS_WS;
+  return refine_ws(Tc, cand_cap(K)) + round_up_sz((size_t)Tc * pitch(Bk) * 4, 256) + slab_ws(Tc, ns) + FLAGS_WS +
+         shift_ws(p, Tc);
 }
 size_t cand_ws(int32_t Tc, int32_t pooled_cols, int32_t n_blocks, bool fused) {
   return refine_ws(Tc, cand_cap(n_blocks)) + round_up_sz((size_t)Tc * pitch(pooled_cols) * 4, 256) +
@@ -444,12 +447,14 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
   // asks for scores and slabs in one pass
   const bool slab_ok = slabs_fit(Tc, nslab_max);
   const KeySchedule ksch = key_schedule(p, Bk, slab_ok && !mask && !blocks);
-  const idx::WindowFlags wf = window_flags(p, Tc, ksch, cv.take<uint32_t>(idx::MAX_WINDOW_FLAGS));
+  idx::WindowFlags wf = window_flags(p, Tc, ksch, cv.take<uint32_t>(idx::MAX_WINDOW_FLAGS));
+  wf.kshift = cv.take<int32_t>(shift_ws(p, Tc) / 4);
   if ((st = launched(idx::launch_key_bound((const uint8_t *)p->k, (const uint8_t *)p->k_scale, p->k_fmt, p->L,
                                            rw.kpart, rw.overflow, &wf, s))))
     return st;
   for (int32_t r0 = 0; r0 < p->T; r0 += Tc) {
     const int32_t nr = std::min(Tc, p->T - r0);
+    const int32_t *kshift = wf.kshift + r0 / Tc;
     for (int32_t l = 0; l < ksch.n; ++l) {
       const int32_t kb = ksch.start(l);
       const int32_t nk = std::max(0, std::min(l == 0 ? ksch.first : ksch.step, p->L - kb));
@@ -477,8 +482,10 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
       b.out_idx = rw.cidx;
       b.out_val = rw.cval;
       b.first = l == 0;
+      b.kshift = kshift;
       idx::LogitsArgs a = logits_args(p, r0, nr, kb, kb + nk, scratch, sld, nk);
       a.by_row = launch_flag(wf, r0, kb);
+      a.kshift = kshift;
       const bool slabs = l > 0 && nk > 0 && slab_ok && a.nsplit <= nslab_max;
       if (slabs && !mask && !blocks) {
         // the launch writes the scores above each row's running threshold to its slabs; the
@@ -497,6 +504,7 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
           const int32_t hn = std::min(Bk, nk - h0);
           idx::LogitsArgs f = logits_args(p, r0, nr, kb + h0, kb + h0 + hn, scratch, sld, hn);
           f.by_row = a.by_row;
+          f.kshift = kshift;
           f.only_flagged = ovf;
           if ((st = launched(idx::launch_logits(f, p->k_fmt, p->H, idx::STORE_BLOCK, s)))) return st;
           idx::TopkArgs bh = b;

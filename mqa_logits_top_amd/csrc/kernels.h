@@ -61,6 +61,9 @@ struct LogitsArgs {
   // do unless *neg_seq >= seq.  seq grows with every launch pair in the process.
   unsigned long long *neg_seq;
   unsigned long long seq;
+  // nullable: a device word added to key_lo and key_hi (the row chunk's first window key,
+  // see WindowFlags)
+  const int32_t *kshift;
 };
 
 hipError_t launch_logits(const LogitsArgs &a, int k_fmt, int H, int mode, hipStream_t s);
@@ -118,6 +121,7 @@ struct TopkArgs {
   int32_t vcols;
   uint32_t *col_rows;
   const uint32_t *only_rows;
+  const int32_t *kshift;  // nullable: a device word added to key0 (as LogitsArgs::kshift)
 };
 constexpr int BMAP_BITS = 9216;   // block bitmap of a top-K launch (65536 keys in 8-key blocks, and slack)
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
@@ -160,7 +164,12 @@ struct WindowFlags {
   int32_t T, Tc;
   int32_t first, LB, nlaunch;   // launch 0 takes keys [0, first), launch l > 0 [first + (l - 1) LB, + LB)
   uint32_t *flags;
+  // nullable: per row chunk, the smallest ks of its rows with a non-empty window, rounded
+  // down to 256 (0 when there is none); the chunk's launches are shifted by it, so that its
+  // first launch holds the first keys its rows see
+  int32_t *kshift;
 };
+constexpr int32_t KEY_SHIFT_ALIGN = 256;
 constexpr int32_t MAX_WINDOW_FLAGS = 16384;
 hipError_t launch_key_bound(const uint8_t *k, const uint8_t *k_scale, int k_fmt, int L, float *part,
                             uint32_t *overflow, const WindowFlags *wf, hipStream_t s);

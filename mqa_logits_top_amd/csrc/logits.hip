@@ -170,6 +170,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(!F16 &&
   // fp32 form: nothing to do unless an f16-form workgroup of this launch pair found rows
   // with a negative head weight (uniform)
   if (!F16 && *a.neg_seq < a.seq) return;
+  if (a.kshift) {   // the row chunk's launches start at its first window key
+    const int sh = *a.kshift;
+    a.key_lo = min(a.key_lo + sh, a.L);
+    a.key_hi = min(a.key_hi + sh, a.L);
+  }
   const int b = blockIdx.x;
   int item = b, part = 0, nparts = 1;
   if (b >= a.nfull) {

@@ -40,6 +40,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <climits>
+
 namespace idx {
 namespace {
 
@@ -562,13 +564,33 @@ __global__ __launch_bounds__(NTH) void refine_kernel(RefineArgs a) {
   }
 }
 
+// First key of row chunk c's launches (see WindowFlags::kshift).  Every thread of the
+// workgroup calls it.
+__device__ int chunk_key_start(const WindowFlags &wf, int L, int c) {
+  __shared__ int cred[4];
+  const int r0 = c * wf.Tc, r1 = min(wf.T, r0 + wf.Tc);
+  int m = INT_MAX;
+  for (int r = r0 + (int)threadIdx.x; r < r1; r += 256) {
+    const int lo = max(wf.ks[r], 0), hi = min(wf.ke[r], L);
+    if (hi > lo) m = min(m, lo);
+  }
+  for (int o = 32; o > 0; o >>= 1) m = min(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) cred[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = min(min(cred[0], cred[1]), min(cred[2], cred[3]));
+  __syncthreads();
+  return m == INT_MAX ? 0 : m / KEY_SHIFT_ALIGN * KEY_SHIFT_ALIGN;
+}
+
 // Window coverage of one (row chunk, key launch) rectangle: flag 1 when the rows' windows
 // cover less than half of it (see WindowFlags).
 __device__ void window_flag(const WindowFlags wf, int L, int f) {
   __shared__ double wred[4];
   const int c = f / wf.nlaunch, l = f % wf.nlaunch;
   const int r0 = c * wf.Tc, r1 = min(wf.T, r0 + wf.Tc);
-  const int klo = l == 0 ? 0 : wf.first + (l - 1) * wf.LB, khi = min(L, l == 0 ? wf.first : klo + wf.LB);
+  const int sh = wf.kshift ? chunk_key_start(wf, L, c) : 0;
+  const int klo = min(L, sh + (l == 0 ? 0 : wf.first + (l - 1) * wf.LB));
+  const int khi = min(L, l == 0 ? sh + wf.first : klo + wf.LB);
   double sum = 0.0;
   for (int r = r0 + (int)threadIdx.x; r < r1; r += 256) {
     const int lo = max(max(wf.ks[r], 0), klo), hi = min(min(wf.ke[r], L), khi);
@@ -584,10 +606,18 @@ __device__ void window_flag(const WindowFlags wf, int L, int f) {
 }
 
 // Largest |k| over all key rows: per-workgroup partial maxima (workgroups [0, np)); the
-// workgroups after them compute the window flags, one each.
+// nf workgroups after them compute the window flags, one each, and the ones after those
+// the row chunks' first keys, one each.
 __global__ __launch_bounds__(256) void key_bound_kernel(const uint8_t *k, const uint8_t *k_scale, int k_fmt, int L,
-                                                        float *part, uint32_t *overflow, int np, WindowFlags wf) {
+                                                        float *part, uint32_t *overflow, int np, int nf,
+                                                        WindowFlags wf) {
   __shared__ float red[4], redf[4];
+  if ((int)blockIdx.x >= np + nf) {   // uniform
+    const int c = (int)blockIdx.x - np - nf;
+    const int sh = chunk_key_start(wf, L, c);
+    if (threadIdx.x == 0) wf.kshift[c] = sh;
+    return;
+  }
   if ((int)blockIdx.x >= np) {   // uniform
     window_flag(wf, L, (int)blockIdx.x - np);
     return;
@@ -651,13 +681,17 @@ hipError_t launch_key_bound(const uint8_t *k, const uint8_t *k_scale, int k_fmt,
                             uint32_t *overflow, const WindowFlags *wf, hipStream_t s) {
   const int np = key_bound_parts(L);
   WindowFlags w{};
-  int nf = 0;
-  if (wf && wf->flags && wf->Tc > 0 && wf->LB > 0 && wf->nlaunch > 0) {
-    nf = ((wf->T + wf->Tc - 1) / wf->Tc) * wf->nlaunch;
-    if (nf > MAX_WINDOW_FLAGS) nf = 0;   // callers pass no flags to their launches then
-    else w = *wf;
+  int nf = 0, nc = 0;
+  if (wf && wf->Tc > 0) {
+    w = *wf;
+    if (wf->flags && wf->LB > 0 && wf->nlaunch > 0) {
+      nf = ((wf->T + wf->Tc - 1) / wf->Tc) * wf->nlaunch;
+      if (nf > MAX_WINDOW_FLAGS) nf = 0;   // callers pass no flags to their launches then
+    }
+    if (wf->kshift) nc = (wf->T + wf->Tc - 1) / wf->Tc;
   }
-  hipLaunchKernelGGL(key_bound_kernel, dim3(np + nf), dim3(256), 0, s, k, k_scale, k_fmt, L, part, overflow, np, w);
+  hipLaunchKernelGGL(key_bound_kernel, dim3(np + nf + nc), dim3(256), 0, s, k, k_scale, k_fmt, L, part, overflow, np,
+                     nf, w);
   return hipGetLastError();
 }
 

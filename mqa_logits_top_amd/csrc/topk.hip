@@ -241,6 +241,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   // ones still held in the memory-side cache
   const int r = a.nrows - 1 - (int)blockIdx.x;
   if (a.only_rows && a.only_rows[r] == 0u) return;   // uniform
+  if (a.kshift) a.key0 += *a.kshift;                  // (as the scoring launch's key range)
   const int t = a.row0 + r;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -615,3 +615,29 @@ def test_rows_of_both_scoring_forms_in_one_launch(H, fmt):
     assert torch.equal(fi, fi2) and torch.equal(fv.view(torch.int32), fv2.view(torch.int32))
     lg2 = idx.idx_mqa_logits(dm, dm.W).cpu().numpy()
     assert np.array_equal(lg.view(np.int32), lg2.view(np.int32))
+
+
+def test_fused_chunks_start_at_their_first_window_key():
+    """Each row chunk's key launches start at the smallest ks of its rows (rounded down to
+    256): chunks of rows whose windows start late fill their running lists in their first
+    launch.  Results equal the oracle's, the dense + refine pipeline's, and those of other row
+    chunkings, bitwise."""
+    T, L, H, K, Bk = 64, 24000, 64, 96, 2048
+    rng = np.random.default_rng(5)
+    c = np.arange(T) // 16
+    ks = (c * 5000 + rng.integers(0, 3000, T)).astype(np.int32)
+    ke = np.minimum(ks + rng.integers(500, 14000, T), L).astype(np.int32)
+    ks[37] = ke[37] = 0                # an empty window: its chunk still starts near key 10000
+    p = synth.make_problem(T, L, H, k_fmt=synth.K_FP8, seed=8, ks=ks, ke=ke)
+    dq = oracle.Dequantised(p)
+    o = oracle.rows_logits(dq, range(T))
+    d = dev(p)
+    fi, fv = idx.idx_logits_topk_fused(d, K, block_k=Bk, row_chunk=16)
+    topk_ok(fi.cpu().numpy(), fv.cpu().numpy(), o, dq.ks, K)
+    lg = idx.idx_mqa_logits(d, d.W)
+    ci, cv = idx.idx_topk(lg, d.ks, d.ke, idx.candidate_capacity(K))
+    di, dv = idx.idx_refine_topk(d, ci, cv, K)
+    assert torch.equal(di, fi) and torch.equal(dv.view(torch.int32), fv.view(torch.int32))
+    for rc in (0, 8, 32):
+        gi, gv = idx.idx_logits_topk_fused(d, K, block_k=Bk, row_chunk=rc)
+        assert torch.equal(gi, fi) and torch.equal(gv.view(torch.int32), fv.view(torch.int32)), rc
