@@ -60,10 +60,15 @@
  *     to sum_h |w'[t, h]| * ReLU(...), not to a score that those terms cancel
  *     down to.  Paths that select from q/k (idx_logits_topk_fused,
  *     idx_block_candidates without logits, idx_refine_topk) keep K + 512
- *     candidates and re-score every candidate near the K-th score exactly
- *     (fp64 over the exact fp8 products), so their selection is that of the
- *     exact scores rounded to fp32.  idx_topk selects exactly on the values
- *     it is given.  The first 4 bytes of the workspace receive the number of
+ *     candidates and re-score exactly (fp64 over the exact fp8 products) every
+ *     candidate within +-2D of the K-th score, D a per-row error scale: twice
+ *     the truncation unit 2^-13 Kmax Mq_h of each head (4.5 to 36 standard
+ *     deviations of the error measured on N(0,1) data), plus the f16 rounding
+ *     bound.  Their selection is that of the exact scores rounded to fp32
+ *     whenever no key's scoring error exceeds D.  D is not a worst-case bound:
+ *     keys can be built whose products cancel but for small terms the MFMA
+ *     drops, so that their error exceeds it; such keys can be misplaced.
+ *     idx_topk selects exactly on the values it is given.  The first 4 bytes of the workspace receive the number of
  *     rows whose candidate list was too short to settle the boundary (0 on
  *     every workload this library was measured on).
  *   - Preconditions the host cannot check without reading device memory
