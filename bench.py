@@ -104,11 +104,11 @@ def time_events(fn, n, stream):
 
 def key_launches(L, block_k):
     """(key0, keys) of the fused path's scoring launches over one row chunk: B_k keys first,
-    then up to two blocks per launch, spread evenly over the keys left."""
+    then up to four blocks per launch, spread evenly over the keys left."""
     if L <= block_k:
         return [(0, L)]
     rest = L - block_k
-    n2 = -(-rest // (2 * block_k))
+    n2 = -(-rest // (4 * block_k))
     step = -(-(-(-rest // n2)) // 256) * 256
     return [(0, block_k)] + [(kb, min(step, L - kb)) for kb in range(block_k, L, step)]
 

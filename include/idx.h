@@ -167,12 +167,12 @@ idx_status idx_topk(const float *logits, int64_t ld, int32_t W, const int32_t *k
 /* Fused key-blocked indexer (P1 section 2.3): for each chunk of row_chunk rows,
  * score its first key block of block_k keys into a [row_chunk, block_k] fp32
  * scratch and take each row's top-(K + 512) from it; every later launch (up to
- * two blocks of keys) writes only the scores above each row's running
+ * four blocks of keys) writes only the scores above each row's running
  * (K + 512)-th to per-row candidate slabs, which are merged into the running
  * lists (rows whose slabs overflow are scored again into the scratch, one block
  * at a time); then settle the boundary exactly (idx_refine_topk).  [T, L] logits
- * are never materialised: the workspace is O(row_chunk * (block_k + K)) and
- * stops growing with L once L exceeds 3 block_k.  The result
+ * are never materialised: the workspace is O(row_chunk * (block_k + K)), with
+ * a bound that holds whatever L.  The result
  * equals idx_mqa_logits + idx_topk (K + 512 columns) + idx_refine_topk
  * bitwise.  mask (nullable):
  * [T, ld_mask] bytes, column j <-> key ks[t] + j (the candidate mask of
@@ -218,8 +218,9 @@ idx_status idx_logits_topk_fused_paged(const idx_problem *p, int32_t K, int32_t 
  * (s - ks[t]) / pool is among blocks[t * ld_blocks + i], i < n_blocks (the
  * out_blocks layout of idx_block_candidates; ids -1 are ignored).  The result equals
  * idx_logits_topk_fused with the byte mask those blocks expand to.  No [T, L] byte
- * mask is read or written.  pool: a power of two, at least 8 for the default
- * two-block launches of 32768 keys (IDX_E_UNSUPPORTED otherwise). */
+ * mask is read or written.  pool: a power of two with block_k / pool + 2 <= 9216
+ * (pool >= 4 at block_k = 32768; IDX_E_UNSUPPORTED otherwise): each launch takes
+ * one key block. */
 idx_status idx_logits_topk_fused_blocks(const idx_problem *p, int32_t K, int32_t block_k, int32_t row_chunk,
                                         const int32_t *blocks, int64_t ld_blocks, int32_t n_blocks, int32_t pool,
                                         int32_t *out_idx, float *out_val, void *ws, size_t ws_bytes, void *stream);

@@ -143,23 +143,25 @@ size_t slab_ws(int32_t Tc, int32_t ns) {
 // row's running top-K merged across them; memory c * T * B_k).  The first launch of a row
 // chunk scores B_k keys into the [Tc, B_k] score scratch, from which the top-K builds each
 // row's running list and threshold.  Every later launch writes only the scores above that
-// threshold, to candidate slabs, and takes up to two blocks' keys (spread evenly over the
-// keys left), so that it holds more work items: its last wave of workgroups, which drains
-// with fewer workgroups per CU, is then a smaller share of it.  Rows whose slabs overflow
-// are scored again into the scratch, one block at a time.  Without slabs (a consumer mask,
-// or too many rows for the slab index range) every launch takes one block.
+// threshold, to candidate slabs, and takes up to SLAB_BLOCKS blocks' keys (spread evenly
+// over the keys left): fewer launches, each with more work items, so fewer slab merges per
+// row and fewer last waves of workgroups that drain with fewer workgroups per CU.  Rows
+// whose slabs overflow are scored again into the scratch, one block at a time.  Without
+// slabs (a consumer mask, or too many rows for the slab index range) every launch takes one
+// block.
 struct KeySchedule {
   int32_t first, step, n;   // keys of launch 0, of every later launch; launches
   int32_t start(int32_t l) const { return l == 0 ? 0 : first + (l - 1) * step; }
 };
-KeySchedule key_schedule(const idx_problem *p, int32_t Bk, bool pairs) {
+constexpr int32_t SLAB_BLOCKS = 4;
+KeySchedule key_schedule(const idx_problem *p, int32_t Bk, bool slabs) {
   KeySchedule k{Bk, Bk, 1};
   const int64_t L = p->L > 0 ? p->L : 0;
   if (L <= Bk) return k;
   const int64_t rest = L - Bk;
-  if (pairs) {
-    const int64_t n2 = (rest + 2 * (int64_t)Bk - 1) / (2 * (int64_t)Bk);
-    k.step = (int32_t)(((rest + n2 - 1) / n2 + KEY_ALIGN - 1) / KEY_ALIGN * KEY_ALIGN);   // <= 2 B_k
+  if (slabs) {
+    const int64_t n2 = (rest + SLAB_BLOCKS * (int64_t)Bk - 1) / (SLAB_BLOCKS * (int64_t)Bk);
+    k.step = (int32_t)(((rest + n2 - 1) / n2 + KEY_ALIGN - 1) / KEY_ALIGN * KEY_ALIGN);   // <= SLAB_BLOCKS B_k
   }
   k.n = (int32_t)(1 + (rest + k.step - 1) / k.step);
   return k;
@@ -179,7 +181,7 @@ size_t gather_ws(int32_t R, int32_t H, int32_t D) {
 // Window flags of the scoring launches (idx::WindowFlags), a fixed region.
 constexpr size_t FLAGS_WS = (size_t)idx::MAX_WINDOW_FLAGS * 4;
 // The fused path's workspace: refinement, the [Tc, B_k] score scratch, the slabs of the
-// two-block schedule (the widest the call can take) and the window flags.
+// slab schedule (the widest the call can take) and the window flags.
 // The row chunks' first window keys (WindowFlags::kshift).
 size_t shift_ws(const idx_problem *p, int32_t Tc) { return round_up_sz((size_t)((p->T + Tc - 1) / Tc + 1) * 4, 256); }
 size_t fused_ws(const idx_problem *p, int32_t Tc, int32_t Bk, int32_t K) {
@@ -443,8 +445,8 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
   uint32_t *ccnt = cv.take<uint32_t>((size_t)Tc * nslab_max * idx::CAND_PARTS);
   uint32_t *slab = cv.take<uint32_t>((size_t)Tc * nslab_max * CAPS * 2);
   uint32_t *col_rows = cv.take<uint32_t>((size_t)Tc);
-  // slabs for every launch after the first; two blocks per launch unless a consumer mask
-  // asks for scores and slabs in one pass
+  // slabs for every launch after the first; up to SLAB_BLOCKS blocks per launch unless a
+  // consumer mask asks for scores and slabs in one pass
   const bool slab_ok = slabs_fit(Tc, nslab_max);
   const KeySchedule ksch = key_schedule(p, Bk, slab_ok && !mask && !blocks);
   idx::WindowFlags wf = window_flags(p, Tc, ksch, cv.take<uint32_t>(idx::MAX_WINDOW_FLAGS));
