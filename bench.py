@@ -60,9 +60,9 @@ def log(*a):
 
 
 def kernel_source_hash():
-    """Hash of the scoring kernel's code (logits.hip and the LogitsArgs struct; comments and
-    blank lines excluded), to tell whether committed counter figures were taken on the kernel
-    as it stands."""
+    """Hash of the scoring kernel's code (logits.hip, the LogitsArgs struct and the key-split
+    planning; comments and blank lines excluded), to tell whether committed counter figures
+    were taken on the kernel and launch layout as they stand."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mqa_logits_top_amd", "csrc")
     with open(os.path.join(csrc, "logits.hip")) as fh:
@@ -71,6 +71,10 @@ def kernel_source_hash():
         hdr = fh.read()
     a = hdr.index("struct LogitsArgs {")
     text += hdr[a:hdr.index("};", a)]
+    with open(os.path.join(csrc, "api.cpp")) as fh:
+        api = fh.read()
+    a = api.index("void plan_splits(")
+    text += api[a:api.index("\n}\n", a)]
     for line in text.splitlines():
         code = line.split("//", 1)[0].rstrip()
         if code:

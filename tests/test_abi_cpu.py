@@ -161,10 +161,10 @@ def test_workspace_sizes(lib):
     shift = lambda T, Tc: _r((-(-T // Tc) + 1) * 4)   # each row chunk's first window key
     assert n.value == (head + 2 * _r(2048 * kc(2048) * 4) + 2048 * (32768 + 64) * 4 + slab(2048, 8) + flags
                        + shift(2048, 2048))
-    # the row chunk and B_k bound the workspace: later launches take at most four blocks (32 splits)
+    # the row chunk and B_k bound the workspace: later launches take at most four blocks (16 splits)
     p2 = _problem(T=16384, L=487936)
     assert lib.idx_workspace_size(2, ctypes.byref(p2), 512, 32768, 4096, 0, 0, 0, ctypes.byref(n)) == 0
-    assert n.value == (head + 2 * _r(4096 * kc(512) * 4) + 4096 * (32768 + 64) * 4 + slab(4096, 32) + flags
+    assert n.value == (head + 2 * _r(4096 * kc(512) * 4) + 4096 * (32768 + 64) * 4 + slab(4096, 16) + flags
                        + shift(16384, 4096))
     m = ctypes.c_size_t()
     p3 = _problem(T=16384, L=262144)

@@ -187,10 +187,11 @@ def test_fused_slab_overflow_and_fit():
 
 
 def test_fused_two_block_launch_mixed_fallback():
-    """A launch of two key blocks where one row block's slabs overflow and the other's fit:
-    the overflowing rows read the launch's scores from the one-block scratch in two passes,
-    the others merge their slabs once and are left alone by the second pass (their windows
-    reach into the second block, whose scores the scratch does not hold for them).  Keys
+    """A launch of several key blocks (here keys 8192..40000, four blocks) where one row
+    block's slabs overflow and the other's fit: the overflowing rows read the launch's scores
+    from the one-block scratch one block per pass, the others merge their slabs once and are
+    left alone by the later passes (their windows reach into the later blocks, whose scores
+    the scratch does not hold for them).  Keys
     8192..12288 are made non-negative and scaled x64; rows 8..15 have non-negative q (those
     keys beat their whole running list), rows 0..7 non-positive q (those keys score 0)."""
     T, L, H, K, Bk = 16, 40000, 64, 64, 8192
