@@ -469,9 +469,12 @@ def trace_summary(trace_dir, scoring="logits_kernel<0, 64, 1, 4, "):
         k = i
         while k + 1 < len(ev) and ev[k + 1][0].startswith(ours):
             k += 1
-        steps.append(ev[i:k + 1])
+        if any(n.startswith("refine_kernel") for n, _, _ in ev[i:k + 1]):   # a whole fused step
+            steps.append(ev[i:k + 1])
         i = k + 1
-    print(f"{len(steps)} fused steps (each from its window kernel to its last refinement)\n")
+    if len(steps) > 1:
+        steps = steps[1:]   # the warm-up step
+    print(f"{len(steps)} fused steps after the warm-up (each from its window kernel to its last refinement)\n")
     if steps:
         names = []
         for st in steps:
