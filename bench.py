@@ -106,21 +106,29 @@ def time_events(fn, n, stream):
     return [a.elapsed_time(b) for a, b in evs]
 
 
-def key_launches(L, block_k):
-    """(key0, keys) of the fused path's scoring launches over one row chunk: B_k keys first,
-    then up to four blocks per launch, spread evenly over the keys left."""
+def key_launches(L, block_k, K):
+    """(key0, keys) of the fused path's scoring launches over one row chunk: one block of B_k
+    keys per launch while the keys seen stay below 20 (K + 512), then up to four blocks per
+    launch, spread evenly over the keys left."""
+    kc = min(K + 512, 2560)
     if L <= block_k:
         return [(0, L)]
-    rest = L - block_k
+    nb = 1
+    while nb * block_k < L and kc * 20 > nb * block_k:
+        nb += 1
+    out = [(i * block_k, min(block_k, L - i * block_k)) for i in range(nb) if i * block_k < L]
+    rest = L - nb * block_k
+    if rest <= 0:
+        return out
     n2 = -(-rest // (4 * block_k))
     step = -(-(-(-rest // n2)) // 256) * 256
-    return [(0, block_k)] + [(kb, min(step, L - kb)) for kb in range(block_k, L, step)]
+    return out + [(kb, min(step, L - kb)) for kb in range(nb * block_k, L, step)]
 
 
-def launch_rects(d, block_k, row_chunk):
+def launch_rects(d, block_k, row_chunk, K):
     """The (row0, rows, key0, keys) rectangles the fused path scores, one per launch."""
     Tc = d.T if row_chunk <= 0 else min(row_chunk, d.T)
-    return [(r0, min(Tc, d.T - r0), kb, nk) for r0 in range(0, d.T, Tc) for kb, nk in key_launches(d.L, block_k)]
+    return [(r0, min(Tc, d.T - r0), kb, nk) for r0 in range(0, d.T, Tc) for kb, nk in key_launches(d.L, block_k, K)]
 
 
 def rect_pairs(d, r0, nr, kb, nk):
@@ -129,11 +137,11 @@ def rect_pairs(d, r0, nr, kb, nk):
     return int(torch.clamp(hi - lo, min=0).sum().item())
 
 
-def scoring_roofline(d, block_k, row_chunk, reps, stream, workload):
+def scoring_roofline(d, block_k, row_chunk, K, reps, stream, workload):
     """The scoring kernel over the fused path's launch rectangles (key-block store, as
     idx_mqa_logits_block launches it), reps passes back to back between one pair of events on
     `stream`; achieved = algorithmic fp8 FLOPs per launch / average launch duration."""
-    rects = launch_rects(d, block_k, row_chunk)
+    rects = launch_rects(d, block_k, row_chunk, K)
     rmax = max(r[1] for r in rects)
     kmax = max(r[3] for r in rects)
     scratch = torch.empty((rmax, kmax + 64), dtype=torch.float32, device=d.q.device)[:, :kmax]
@@ -227,7 +235,7 @@ def workload(name, dev, stream, steps, warmup, roof_reps):
     log(f"[bench] {name}: fused step {ms:.4f} ms -> {line['pairs_per_s']:.4e} pairs/s, {line['tflops']:.0f} TFLOP/s "
         f"({100 * line['fp8_peak_frac_step']:.1f}% of fp8 peak at step level), workspace {ws.numel() / 2**20:.0f} MiB")
     if roof_reps:
-        line["roofline"] = scoring_roofline(d, Bk, rc, roof_reps, stream, name)
+        line["roofline"] = scoring_roofline(d, Bk, rc, K, roof_reps, stream, name)
         r = line["roofline"]
         log(f"[bench] {name}: scoring kernel {r['avg_launch_ms']:.4f} ms/launch -> {r['achieved']:.1f} TFLOP/s "
             f"({100 * r['frac']:.1f}% of fp8 peak)")
@@ -331,7 +339,8 @@ def traffic_probe(dev):
     for name in PROBE:
         pw = p if name == "glm_chunk" else synth.make_config(name)
         dw = d if name == "glm_chunk" else idx.Inputs.from_host(pw, device=dev)
-        r0, nr, kb, nk = max(launch_rects(dw, pw.meta["block_k"], ROW_CHUNK[name]), key=lambda r: r[1] * r[3])
+        r0, nr, kb, nk = max(launch_rects(dw, pw.meta["block_k"], ROW_CHUNK[name], pw.meta["K"]),
+                             key=lambda r: r[1] * r[3])
         scratch = torch.empty((nr, nk + 64), dtype=torch.float32, device=dev)[:, :nk]
         for rep in range(2):
             idx.idx_mqa_logits_block(dw, r0, nr, kb, nk, out=scratch)
@@ -381,7 +390,7 @@ def traffic_summary(fetch_dir, write_dir):
         w = launch_pairs([v * factor["WRITE_SIZE"] for n, v, _, _ in rows["WRITE_SIZE"] if kname in n])[-2:]
         p = synth.make_config(name)
         Tc = p.T if ROW_CHUNK[name] <= 0 else min(ROW_CHUNK[name], p.T)
-        rect = [Tc, max(nk for _, nk in key_launches(p.L, p.meta["block_k"]))]
+        rect = [Tc, max(nk for _, nk in key_launches(p.L, p.meta["block_k"], p.meta["K"]))]
         rec = {"kernel_source_hash": kernel_source_hash(), "rect": rect,
                "bytes_per_launch": float(np.mean(f) + np.mean(w)), "fetch_bytes_per_launch": float(np.mean(f)),
                "write_bytes_per_launch": float(np.mean(w)), "fetch_factor": factor["FETCH_SIZE"],
@@ -531,7 +540,7 @@ def extras(dev, stream, glm, dsv4):
     # the same shape with fp8 keys
     p4 = synth.make_problem(2048, 102400, 64, k_fmt=synth.K_FP8)
     d4 = idx.Inputs.from_host(p4, device=dev)
-    ex["c3_shape_fp8_logits_stage"] = scoring_roofline(d4, 32768, 0, 3, stream, "c3_shape_fp8")
+    ex["c3_shape_fp8_logits_stage"] = scoring_roofline(d4, 32768, 0, 512, 3, stream, "c3_shape_fp8")
     log(f"[bench] T=2048 L=102400 H=64 fp8 scoring {ex['c3_shape_fp8_logits_stage']['achieved']:.1f} TFLOP/s")
     del d4
     # workspace of the fused path at the long-context shape, against L: flat

@@ -144,36 +144,48 @@ size_t slab_ws(int32_t Tc, int32_t ns) {
          round_up_sz((size_t)Tc * ns * CAPS * 8, 256) + round_up_sz((size_t)Tc * 4, 256);
 }
 // Key launches of the fused path (P1 section 2.3: key blocks scored one after another, each
-// row's running top-K merged across them; memory c * T * B_k).  The first launch of a row
-// chunk scores B_k keys into the [Tc, B_k] score scratch, from which the top-K builds each
-// row's running list and threshold.  Every later launch writes only the scores above that
-// threshold, to candidate slabs, and takes up to SLAB_BLOCKS blocks' keys (spread evenly
-// over the keys left): fewer launches, each with more work items, so fewer slab merges per
-// row and fewer last waves of workgroups that drain with fewer workgroups per CU.  Rows
-// whose slabs overflow are scored again into the scratch, one block at a time.  Without
-// slabs (a consumer mask, or too many rows for the slab index range) every launch takes one
-// block.
+// row's running top-K merged across them; memory c * T * B_k).  The first launches of a row
+// chunk score one block of B_k keys each into the [Tc, B_k] score scratch, from which the
+// top-K builds and updates each row's running list of Kc = K + 512 entries and its threshold
+// (the list's smallest entry).  Once the keys seen reach SLAB_DENSITY x Kc, so that at most one
+// in SLAB_DENSITY of the next scores can still enter a list, every later launch writes only
+// the scores above the threshold, to candidate slabs, and takes up to SLAB_BLOCKS blocks'
+// keys (spread evenly over the keys left): fewer launches, each with more work items, so
+// fewer merges per row and fewer last waves of workgroups that drain with the CU partly
+// empty.  Rows whose slabs overflow are scored again into the scratch, one block at a time.
+// At higher candidate densities a slab launch costs more than a block launch with its top-K
+// (glm_chunk's second block, 8% of its scores above the threshold: 298 + 93 us against
+// 243 + 108 us).  Without slabs (a consumer mask, or too many rows for the slab index range)
+// every launch takes one block.
 struct KeySchedule {
-  int32_t first, step, n;   // keys of launch 0, of every later launch; launches
-  int32_t start(int32_t l) const { return l == 0 ? 0 : first + (l - 1) * step; }
+  int32_t bk, nb, step, n;   // block keys, block launches, keys of each slab launch, launches
+  int32_t start(int32_t l) const { return l < nb ? l * bk : nb * bk + (l - nb) * step; }
+  int32_t keys(int32_t l) const { return l < nb ? bk : step; }
+  bool slab(int32_t l) const { return l >= nb; }
 };
 constexpr int32_t SLAB_BLOCKS = 4;
-KeySchedule key_schedule(const idx_problem *p, int32_t Bk, bool slabs) {
-  KeySchedule k{Bk, Bk, 1};
+constexpr int32_t SLAB_DENSITY = 20;
+KeySchedule key_schedule(const idx_problem *p, int32_t Bk, int32_t Kc, bool slabs) {
+  KeySchedule k{Bk, 1, Bk, 1};
   const int64_t L = p->L > 0 ? p->L : 0;
   if (L <= Bk) return k;
-  const int64_t rest = L - Bk;
-  if (slabs) {
-    const int64_t n2 = (rest + SLAB_BLOCKS * (int64_t)Bk - 1) / (SLAB_BLOCKS * (int64_t)Bk);
-    k.step = (int32_t)(((rest + n2 - 1) / n2 + KEY_ALIGN - 1) / KEY_ALIGN * KEY_ALIGN);   // <= SLAB_BLOCKS B_k
-  }
-  k.n = (int32_t)(1 + (rest + k.step - 1) / k.step);
+  int64_t nb = 1;
+  if (!slabs) nb = (L + Bk - 1) / Bk;
+  else
+    while (nb * Bk < L && (int64_t)Kc * SLAB_DENSITY > nb * Bk) ++nb;
+  k.nb = (int32_t)nb;
+  k.n = k.nb;
+  const int64_t rest = L - nb * Bk;
+  if (rest <= 0) return k;
+  const int64_t n2 = (rest + SLAB_BLOCKS * (int64_t)Bk - 1) / (SLAB_BLOCKS * (int64_t)Bk);
+  k.step = (int32_t)(((rest + n2 - 1) / n2 + KEY_ALIGN - 1) / KEY_ALIGN * KEY_ALIGN);   // <= SLAB_BLOCKS B_k
+  k.n = (int32_t)(nb + (rest + k.step - 1) / k.step);
   return k;
 }
-// Slabs per row of the widest later launch.
+// Slabs per row of the widest slab launch.
 int32_t schedule_slabs(const KeySchedule &k, int32_t L) {
-  if (k.n <= 1) return 0;
-  return std::max(block_slabs(std::min(k.step, L - k.start(1))), block_slabs(L - k.start(k.n - 1)));
+  if (k.n <= k.nb) return 0;
+  return std::max(block_slabs(std::min(k.step, L - k.start(k.nb))), block_slabs(L - k.start(k.n - 1)));
 }
 // Slab pair indices of a launch stay within int32 for row chunks below this.
 bool slabs_fit(int32_t Tc, int32_t ns) { return (int64_t)Tc * ns * CAPS * 8 < INT32_MAX; }
@@ -184,12 +196,12 @@ size_t gather_ws(int32_t R, int32_t H, int32_t D) {
 }
 // Window flags of the scoring launches (idx::WindowFlags), a fixed region.
 constexpr size_t FLAGS_WS = (size_t)idx::MAX_WINDOW_FLAGS * 4;
-// The fused path's workspace: refinement, the [Tc, B_k] score scratch, the slabs of the
-// slab schedule (the widest the call can take) and the window flags.
 // The row chunks' first window keys (WindowFlags::kshift).
 size_t shift_ws(const idx_problem *p, int32_t Tc) { return round_up_sz((size_t)((p->T + Tc - 1) / Tc + 1) * 4, 256); }
+// The fused path's workspace: refinement, the [Tc, B_k] score scratch, the slabs of the
+// slab schedule (the widest the call can take), the window flags and the key shifts.
 size_t fused_ws(const idx_problem *p, int32_t Tc, int32_t Bk, int32_t K) {
-  const int32_t ns = schedule_slabs(key_schedule(p, Bk, true), p->L);
+  const int32_t ns = schedule_slabs(key_schedule(p, Bk, cand_cap(K), true), p->L);
   return refine_ws(Tc, cand_cap(K)) + round_up_sz((size_t)Tc * pitch(Bk) * 4, 256) + slab_ws(Tc, ns) + FLAGS_WS +
          shift_ws(p, Tc);
 }
@@ -205,7 +217,8 @@ idx::WindowFlags window_flags(const idx_problem *p, int32_t Tc, const KeySchedul
   f.ke = p->ke;
   f.T = p->T;
   f.Tc = Tc;
-  f.first = k.first;
+  f.B0 = k.bk;
+  f.nb = k.nb;
   f.LB = k.step;
   f.nlaunch = p->L > 0 ? k.n : 0;
   const int64_t n = (int64_t)((p->T + Tc - 1) / Tc) * f.nlaunch;
@@ -213,7 +226,7 @@ idx::WindowFlags window_flags(const idx_problem *p, int32_t Tc, const KeySchedul
   return f;
 }
 const uint32_t *launch_flag(const idx::WindowFlags &f, int32_t r0, int32_t kb) {
-  const int32_t l = kb < f.first ? 0 : 1 + (kb - f.first) / f.LB;
+  const int32_t l = kb < f.nb * f.B0 ? kb / f.B0 : f.nb + (kb - f.nb * f.B0) / f.LB;
   return f.flags ? f.flags + (int64_t)(r0 / f.Tc) * f.nlaunch + l : nullptr;
 }
 
@@ -443,7 +456,7 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
   RefineWs rw = carve_refine(cv, Tc, Kc);
   const int32_t sld = pitch(Bk);
   float *scratch = cv.take<float>((size_t)Tc * sld);
-  const int32_t nslab_max = schedule_slabs(key_schedule(p, Bk, true), p->L);
+  const int32_t nslab_max = schedule_slabs(key_schedule(p, Bk, cand_cap(K), true), p->L);
   float *thr = cv.take<float>((size_t)Tc);
   uint32_t *ovf = cv.take<uint32_t>((size_t)Tc / 8 + 1);   // per scoring row block (>= 8 rows)
   uint32_t *ccnt = cv.take<uint32_t>((size_t)Tc * nslab_max * idx::CAND_PARTS);
@@ -452,7 +465,7 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
   // slabs for every launch after the first; up to SLAB_BLOCKS blocks per launch unless a
   // consumer mask asks for scores and slabs in one pass
   const bool slab_ok = slabs_fit(Tc, nslab_max);
-  const KeySchedule ksch = key_schedule(p, Bk, slab_ok && !mask && !blocks);
+  const KeySchedule ksch = key_schedule(p, Bk, Kc, slab_ok && !mask && !blocks);
   idx::WindowFlags wf = window_flags(p, Tc, ksch, cv.take<uint32_t>(idx::MAX_WINDOW_FLAGS));
   wf.kshift = cv.take<int32_t>(shift_ws(p, Tc) / 4);
   if ((st = launched(idx::launch_key_bound((const uint8_t *)p->k, (const uint8_t *)p->k_scale, p->k_fmt, p->L,
@@ -463,7 +476,7 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
     const int32_t *kshift = wf.kshift + r0 / Tc;
     for (int32_t l = 0; l < ksch.n; ++l) {
       const int32_t kb = ksch.start(l);
-      const int32_t nk = std::max(0, std::min(l == 0 ? ksch.first : ksch.step, p->L - kb));
+      const int32_t nk = std::max(0, std::min(ksch.keys(l), p->L - kb));
       idx::TopkArgs b{};
       b.thr_out = thr;
       b.vals = scratch;
@@ -492,7 +505,7 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
       idx::LogitsArgs a = logits_args(p, r0, nr, kb, kb + nk, scratch, sld, nk);
       a.by_row = launch_flag(wf, r0, kb);
       a.kshift = kshift;
-      const bool slabs = l > 0 && nk > 0 && slab_ok && a.nsplit <= nslab_max;
+      const bool slabs = ksch.slab(l) && nk > 0 && slab_ok && a.nsplit <= nslab_max;
       if (slabs && !mask && !blocks) {
         // the launch writes the scores above each row's running threshold to its slabs; the
         // row blocks where a slab overflowed are scored again into the scratch, one block of
@@ -640,7 +653,7 @@ idx_status idx_block_candidates(const idx_problem *p, const float *logits, int64
   int32_t *kept = cv.take<int32_t>((size_t)Tc * n_blocks);
   idx::WindowFlags wf{};
   if (!logits) {
-    wf = window_flags(p, Tc, key_schedule(p, Bk, false), cv.take<uint32_t>(idx::MAX_WINDOW_FLAGS));
+    wf = window_flags(p, Tc, key_schedule(p, Bk, 0, false), cv.take<uint32_t>(idx::MAX_WINDOW_FLAGS));
     if ((st = launched(idx::launch_key_bound((const uint8_t *)p->k, (const uint8_t *)p->k_scale, p->k_fmt, p->L,
                                              rw.kpart, rw.overflow, &wf, s))))
       return st;

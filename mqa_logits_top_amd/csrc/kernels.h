@@ -162,7 +162,8 @@ int key_bound_parts(int L);
 struct WindowFlags {
   const int32_t *ks, *ke;
   int32_t T, Tc;
-  int32_t first, LB, nlaunch;   // launch 0 takes keys [0, first), launch l > 0 [first + (l - 1) LB, + LB)
+  // launch l < nb takes keys [l B0, (l + 1) B0), launch l >= nb [nb B0 + (l - nb) LB, + LB)
+  int32_t B0, nb, LB, nlaunch;
   uint32_t *flags;
   // nullable: per row chunk, the smallest ks of its rows with a non-empty window, rounded
   // down to 256 (0 when there is none); the chunk's launches are shifted by it, so that its

@@ -589,8 +589,8 @@ __device__ void window_flag(const WindowFlags wf, int L, int f) {
   const int c = f / wf.nlaunch, l = f % wf.nlaunch;
   const int r0 = c * wf.Tc, r1 = min(wf.T, r0 + wf.Tc);
   const int sh = wf.kshift ? chunk_key_start(wf, L, c) : 0;
-  const int klo = min(L, sh + (l == 0 ? 0 : wf.first + (l - 1) * wf.LB));
-  const int khi = min(L, l == 0 ? sh + wf.first : klo + wf.LB);
+  const int klo = min(L, sh + (l < wf.nb ? l * wf.B0 : wf.nb * wf.B0 + (l - wf.nb) * wf.LB));
+  const int khi = min(L, klo + (l < wf.nb ? wf.B0 : wf.LB));
   double sum = 0.0;
   for (int r = r0 + (int)threadIdx.x; r < r1; r += 256) {
     const int lo = max(max(wf.ks[r], 0), klo), hi = min(min(wf.ke[r], L), khi);

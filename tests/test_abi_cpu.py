@@ -154,12 +154,13 @@ def test_workspace_sizes(lib):
     assert lib.idx_workspace_size(2, ctypes.byref(p), 2048, 32768, 0, 0, 0, 0, ctypes.byref(n)) == 0
     # scores of one block of B_k keys ([Tc, B_k + 64] fp32), then the slabs of the later launches:
     # thresholds, overflow flags, count words (ns splits x 4 parts), (value, id) pairs (ns slabs
-    # of 512), the two-call top-K's row words.  Here keys [32768, 65536) in one launch: 8 splits.
+    # of 512), the two-call top-K's row words.  Here K + 512 = 2560 > 65536 / 20: both blocks are
+    # block launches and there are no slabs.
     slab = lambda Tc, ns: (_r(Tc * 4) + _r((Tc // 8 + 1) * 4) + _r(Tc * ns * 4 * 4) + _r(Tc * ns * 512 * 8)
                            + _r(Tc * 4))
     flags = 16384 * 4   # window flags of the scoring launches, a fixed region
     shift = lambda T, Tc: _r((-(-T // Tc) + 1) * 4)   # each row chunk's first window key
-    assert n.value == (head + 2 * _r(2048 * kc(2048) * 4) + 2048 * (32768 + 64) * 4 + slab(2048, 8) + flags
+    assert n.value == (head + 2 * _r(2048 * kc(2048) * 4) + 2048 * (32768 + 64) * 4 + slab(2048, 0) + flags
                        + shift(2048, 2048))
     # the row chunk and B_k bound the workspace: later launches take at most four blocks (16 splits)
     p2 = _problem(T=16384, L=487936)

@@ -165,11 +165,12 @@ def test_fused_equals_dense_refined_bitwise(case, block_k, row_chunk):
 
 
 def test_fused_slab_overflow_and_fit():
-    """Launches after the first merge their scoring-kernel candidate slabs when every slab
-    fits and read the launch's scores otherwise.  Scores are sums of non-negative terms here,
-    so scaling keys up makes nearly all of them beat the running list: the second launch
-    (keys 8192..20000, two blocks scaled x64 and x128) overflows its 512-entry slabs, and its
-    rows read its scores from the one-block scratch, block by block."""
+    """Slab launches merge their scoring-kernel candidate slabs when every slab fits and read
+    the launch's scores otherwise.  Scores are sums of non-negative terms here, so scaling keys
+    up makes nearly all of them beat the running list.  With K + 512 = 576 the first two blocks
+    (keys 0..16384, the second scaled x64) are block launches; the slab launch (keys
+    16384..20000, scaled x128) overflows its 512-entry slabs, and its rows read its scores from
+    the one-block scratch."""
     T, L, H, K, Bk = 16, 20000, 64, 64, 8192   # H = 64: slabs from the second block on
     p = synth.make_problem(T, L, H, k_fmt=synth.K_FP8, seed=3)
     p.k_scale[Bk:2 * Bk] *= 64.0
@@ -186,18 +187,20 @@ def test_fused_slab_overflow_and_fit():
     assert torch.equal(dv.view(torch.int32), fv.view(torch.int32))
 
 
-def test_fused_two_block_launch_mixed_fallback():
-    """A launch of several key blocks (here keys 8192..40000, four blocks) where one row
-    block's slabs overflow and the other's fit: the overflowing rows read the launch's scores
+def test_fused_slab_launch_mixed_fallback():
+    """A slab launch of several key blocks (with K + 512 = 576 and B_k = 8192: keys 0..16384
+    in two block launches, then keys 16384..40000, three blocks, in one slab launch) where one
+    row block's slabs overflow and the other's fit: the overflowing rows read the launch's scores
     from the one-block scratch one block per pass, the others merge their slabs once and are
     left alone by the later passes (their windows reach into the later blocks, whose scores
-    the scratch does not hold for them).  Keys
-    8192..12288 are made non-negative and scaled x64; rows 8..15 have non-negative q (those
-    keys beat their whole running list), rows 0..7 non-positive q (those keys score 0)."""
+    the scratch does not hold for them).  Keys 16384..20480 are made non-negative and scaled
+    x64; rows 8..15 have non-negative q (those keys beat their whole running list), rows 0..7
+    non-positive q (those keys score 0)."""
     T, L, H, K, Bk = 16, 40000, 64, 64, 8192
+    lo, hi = 16384, 20480
     p = synth.make_problem(T, L, H, k_fmt=synth.K_FP8, seed=12)
-    p.k[8192:12288] &= 0x7F
-    p.k_scale[8192:12288] *= 64.0
+    p.k[lo:hi] &= 0x7F
+    p.k_scale[lo:hi] *= 64.0
     p.q[8:16] &= 0x7F
     p.q[0:8] |= 0x80
     dq = oracle.Dequantised(p)
@@ -212,8 +215,8 @@ def test_fused_two_block_launch_mixed_fallback():
     assert torch.equal(dv.view(torch.int32), fv.view(torch.int32))
     # the scaled keys fill the top of rows 8..15 and none of rows 0..7
     sel = fi.cpu().numpy()
-    assert ((sel[8:] >= 8192) & (sel[8:] < 12288)).all()
-    assert not ((sel[:8] >= 8192) & (sel[:8] < 12288)).any()
+    assert ((sel[8:] >= lo) & (sel[8:] < hi)).all()
+    assert not ((sel[:8] >= lo) & (sel[:8] < hi)).any()
 
 
 @pytest.mark.parametrize("row_chunk", [0, 16])
