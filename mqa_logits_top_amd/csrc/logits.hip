@@ -648,12 +648,22 @@ hipError_t launch4(const LogitsArgs &a0, hipStream_t s) {
   const int64_t items = (int64_t)((nrb + 7) / 8) * 8 * a0.nsplit;   // row blocks padded to whole groups of 8
   if (items <= 0) return hipSuccess;
   // Whole items fill as many complete waves of resident workgroups as they can; the
-  // remainder is cut into parts so that the last wave spans the machine as well.
+  // remainder is cut into parts so that the last waves span the machine as well: into the
+  // part count p <= CAND_PARTS whose ceil(rem p / slots) / p item-lengths of tail is
+  // shortest (rem = 512 on 768 slots: 3 parts, 2/3 of an item instead of a whole one).
   LogitsArgs a = a0;
   const int64_t slots = resident_workgroups(kern, NW * 64);
   const int64_t full_waves = slots > 0 ? items / slots : items;
   const int64_t rem = items - full_waves * slots;
-  a.parts = rem > 0 ? (int)std::min<int64_t>(CAND_PARTS, std::max<int64_t>(1, slots / rem)) : 1;
+  a.parts = 1;
+  if (rem > 0 && slots > 0) {
+    int64_t bw = (rem + slots - 1) / slots, bp = 1;   // tail = bw / bp item-lengths
+    for (int64_t p = 2; p <= CAND_PARTS; ++p) {
+      const int64_t w = (rem * p + slots - 1) / slots;
+      if (w * bp < bw * p) { bw = w; bp = p; }
+    }
+    a.parts = (int)bp;
+  }
   a.nfull = (int)(items - rem);
   const int64_t grid = a.nfull + rem * a.parts;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), 0, s, a);
