@@ -505,6 +505,7 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
       idx::LogitsArgs a = logits_args(p, r0, nr, kb, kb + nk, scratch, sld, nk);
       a.by_row = launch_flag(wf, r0, kb);
       a.kshift = kshift;
+      b.launch_flag = a.by_row;
       const bool slabs = ksch.slab(l) && nk > 0 && slab_ok && a.nsplit <= nslab_max;
       if (slabs && !mask && !blocks) {
         // the launch writes the scores above each row's running threshold to its slabs; the
@@ -517,7 +518,8 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
         c.caps = CAPS;
         if ((st = launched(idx::launch_logits(c, p->k_fmt, p->H, idx::STORE_SLAB, s)))) return st;
         const int32_t rpw = idx::logits_rows_per_workgroup(p->H);
-        if ((st = launched(idx::launch_slab_check(ccnt, a.nsplit * idx::CAND_PARTS, thr, nr, rpw, ovf, s))))
+        if ((st = launched(
+                 idx::launch_slab_check(ccnt, a.nsplit * idx::CAND_PARTS, thr, nr, rpw, ovf, a.by_row, s))))
           return st;
         for (int32_t h0 = 0; h0 < nk; h0 += Bk) {
           const int32_t hn = std::min(Bk, nk - h0);
@@ -693,6 +695,7 @@ idx_status idx_block_candidates(const idx_problem *p, const float *logits, int64
         if (nk > 0) {
           idx::LogitsArgs a = logits_args(p, r0, nr, kb, kb + nk, pooled, pld, (nk + pool - 1) / pool);
           a.by_row = launch_flag(wf, r0, kb);
+          b.launch_flag = a.by_row;
           if ((st = launched(idx::launch_logits(a, p->k_fmt, p->H, idx::STORE_POOL8, s)))) return st;
         }
         b.vals = pooled;

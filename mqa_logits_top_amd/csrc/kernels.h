@@ -49,11 +49,13 @@ struct LogitsArgs {
   // nonzero (nullable: all)
   const uint32_t *only_flagged;
   int32_t caps;
-  // Workgroup -> XCD layout (nullable: by key split).  By key split, each split's workgroups
-  // share an XCD, so its keys stay in one L2 (rows whose windows span the keys).  By row block
-  // (nonzero word here), each row block's workgroups share an XCD; a launch whose rows each see
-  // only a small part of the keys (a ragged batch of short requests) then spreads its active
-  // workgroups over every XCD instead of the few that own the splits those windows touch.
+  // The launch's window flag word (nullable; see WindowFlags).  Bit 1 set: no row of the launch
+  // has a window key in its key range, and the launch does nothing.  Bit 0 picks the workgroup
+  // -> XCD layout.  By key split (bit clear), each split's workgroups share an XCD, so its keys
+  // stay in one L2 (rows whose windows span the keys).  By row block (bit set), each row block's
+  // workgroups share an XCD; a launch whose rows each see only a small part of the keys (a
+  // ragged batch of short requests) then spreads its active workgroups over every XCD instead
+  // of the few that own the splits those windows touch.
   const uint32_t *by_row;
   // Launch pair marker (filled by launch_logits): a scoring launch is an f16 form and an fp32
   // form over the same grid.  An f16-form workgroup whose rows hold a head weight below zero
@@ -70,9 +72,10 @@ hipError_t launch_logits(const LogitsArgs &a, int k_fmt, int H, int mode, hipStr
 int logits_rows_per_workgroup(int H);   // RPW of the scoring launches
 // Row blocks of a candidate-slab launch whose rows the top-K cannot serve from the slabs
 // alone (a share overflowed, the shares together exceed the merge capacity, or the row's
-// list is not full yet: thr NaN): flags[b] = 1 for them, 0 for the others.
+// list is not full yet: thr NaN): flags[b] = 1 for them, 0 for the others (all 0 when
+// launch_flag, nullable, marks the launch as holding no window key).
 hipError_t launch_slab_check(const uint32_t *ccnt, int32_t nshares, const float *thr, int32_t nrows, int32_t rpw,
-                             uint32_t *flags, hipStream_t s);
+                             uint32_t *flags, const uint32_t *launch_flag, hipStream_t s);
 
 // Top-K over row-major fp32 values (one workgroup per row, running top-K kept
 // across passes).  Row r of the launch is problem row t = row0 + r.  Column c
@@ -122,6 +125,9 @@ struct TopkArgs {
   uint32_t *col_rows;
   const uint32_t *only_rows;
   const int32_t *kshift;  // nullable: a device word added to key0 (as LogitsArgs::kshift)
+  // nullable: the scoring launch's window flag word (LogitsArgs::by_row); with its bit 1 set a
+  // call other than the first has nothing new for any row and returns at once
+  const uint32_t *launch_flag;
 };
 constexpr int BMAP_BITS = 9216;   // block bitmap of a top-K launch (65536 keys in 8-key blocks, and slack)
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
@@ -164,6 +170,8 @@ struct WindowFlags {
   int32_t T, Tc;
   // launch l < nb takes keys [l B0, (l + 1) B0), launch l >= nb [nb B0 + (l - nb) LB, + LB)
   int32_t B0, nb, LB, nlaunch;
+  // one word per (row chunk, launch): bit 0 when the rows' windows cover less than half of the
+  // rectangle, bit 1 when they cover none of it
   uint32_t *flags;
   // nullable: per row chunk, the smallest ks of its rows with a non-empty window, rounded
   // down to 256 (0 when there is none); the chunk's launches are shifted by it, so that its

@@ -170,6 +170,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(!F16 &&
   // fp32 form: nothing to do unless an f16-form workgroup of this launch pair found rows
   // with a negative head weight (uniform)
   if (!F16 && *a.neg_seq < a.seq) return;
+  if (a.by_row && (*a.by_row & 2u) != 0u) return;   // no window key in the launch (uniform)
   if (a.kshift) {   // the row chunk's launches start at its first window key
     const int sh = *a.kshift;
     a.key_lo = min(a.key_lo + sh, a.L);
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(!F16 &&
   // fastest within groups of 8, item = (group * nsplit + split) * 8 + rb % 8, so workgroup b
   // takes row blocks == b (mod 8).  Row blocks are padded to whole groups of 8.
   int split_i, rb;
-  const bool by_row = a.by_row && *a.by_row != 0u;   // uniform
+  const bool by_row = a.by_row && (*a.by_row & 1u) != 0u;   // uniform
   if (by_row) {
     const int grp = item / (8 * a.nsplit), rem8 = item % (8 * a.nsplit);
     split_i = rem8 >> 3;

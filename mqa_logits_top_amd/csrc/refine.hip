@@ -585,8 +585,8 @@ __device__ int chunk_key_start(const WindowFlags &wf, int L, int c) {
   return m == INT_MAX ? 0 : m / KEY_SHIFT_ALIGN * KEY_SHIFT_ALIGN;
 }
 
-// Window coverage of one (row chunk, key launch) rectangle: flag 1 when the rows' windows
-// cover less than half of it (see WindowFlags).
+// Window coverage of one (row chunk, key launch) rectangle: bit 0 when the rows' windows
+// cover less than half of it, bit 1 when they cover none of it (see WindowFlags).
 __device__ void window_flag(const WindowFlags wf, int L, int f) {
   __shared__ double wred[4];
   const int c = f / wf.nlaunch, l = f % wf.nlaunch;
@@ -604,7 +604,7 @@ __device__ void window_flag(const WindowFlags wf, int L, int f) {
   __syncthreads();
   if (threadIdx.x == 0) {
     const double tot = (wred[0] + wred[1]) + (wred[2] + wred[3]);
-    wf.flags[f] = 2.0 * tot < (double)(r1 - r0) * (double)(khi - klo) ? 1u : 0u;
+    wf.flags[f] = (2.0 * tot < (double)(r1 - r0) * (double)(khi - klo) ? 1u : 0u) | (tot == 0.0 ? 2u : 0u);
   }
 }
 

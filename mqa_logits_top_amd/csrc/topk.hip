@@ -241,6 +241,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   // ones still held in the memory-side cache
   const int r = a.nrows - 1 - (int)blockIdx.x;
   if (a.only_rows && a.only_rows[r] == 0u) return;   // uniform
+  if (!a.first && a.launch_flag && (*a.launch_flag & 2u) != 0u) return;   // an empty launch (uniform)
   if (a.kshift) a.key0 += *a.kshift;                  // (as the scoring launch's key range)
   const int t = a.row0 + r;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -662,8 +663,13 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 // are those under which topk_kernel<true, *> leaves the slab merge for the column pass.
 // Lanes take the row's count words (nshares <= NTH); the wave sums them.
 __global__ __launch_bounds__(64) void slab_check_kernel(const uint32_t *ccnt, int32_t nshares, const float *thr,
-                                                        int32_t nrows, int32_t rpw, uint32_t *flags) {
+                                                        int32_t nrows, int32_t rpw, uint32_t *flags,
+                                                        const uint32_t *launch_flag) {
   const int b = blockIdx.x, lane = threadIdx.x;
+  if (launch_flag && (*launch_flag & 2u) != 0u) {   // the launch scored nothing: no row needs the scores
+    if (lane == 0) flags[b] = 0u;
+    return;
+  }
   bool need = nshares > NTH;
   for (int r = b * rpw; r < min((b + 1) * rpw, nrows); ++r) {
     uint32_t tot = 0, over = 0;
@@ -682,10 +688,11 @@ __global__ __launch_bounds__(64) void slab_check_kernel(const uint32_t *ccnt, in
 }  // namespace
 
 hipError_t launch_slab_check(const uint32_t *ccnt, int32_t nshares, const float *thr, int32_t nrows, int32_t rpw,
-                             uint32_t *flags, hipStream_t s) {
+                             uint32_t *flags, const uint32_t *launch_flag, hipStream_t s) {
   const int nb = (nrows + rpw - 1) / rpw;
   if (nb <= 0) return hipSuccess;
-  hipLaunchKernelGGL(slab_check_kernel, dim3(nb), dim3(64), 0, s, ccnt, nshares, thr, nrows, rpw, flags);
+  hipLaunchKernelGGL(slab_check_kernel, dim3(nb), dim3(64), 0, s, ccnt, nshares, thr, nrows, rpw, flags,
+                     launch_flag);
   return hipGetLastError();
 }
 
