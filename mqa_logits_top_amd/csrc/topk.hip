@@ -324,46 +324,64 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   if (SLABS && !a.first && run_n == K) {
     // one count word per (slab, part): candidates in the low half, share offset above
     const int ne = a.nslab * CAND_PARTS;
-    uint32_t cs = 0, over = 0, d0 = 0xFFFFFFFFu, cw = 0;
+    uint32_t cs = 0, over = 0, cw = 0;
     if (tid < ne) {
       cw = a.ccnt[(int64_t)r * ne + tid];
       cs = cw & 0xFFFFu;
       over = cs == CAND_OVER;
       if (over) cs = 0;
     }
-    uint32_t ex, d1, tot_c, d2;
-    block_scan2(sm, cs, 0u, ex, d1, tot_c, d2, lane, wave);
-    uint32_t osum = over;
-    block_sum_minmax(sm, osum, d0, over, lane, wave);
+    uint32_t ex, d1, tot_c, osum;   // share offsets, total candidates, overflowed shares
+    block_scan2(sm, cs, over, ex, d1, tot_c, osum, lane, wave);
     if (osum == 0 && tot_c <= (uint32_t)CAPK && a.caps <= CAPS_MAX && ne <= NTH) {  // uniform
       // the shares hold their candidates in id order and cover consecutive key ranges,
       // so appending them after the running list keeps the items in id order
       if (tid < ne) { sm.hist[tid] = ex; sm.hist[NTH + tid] = (cw & 0xFFFF0000u) | cs; }
       __syncthreads();
-      // wave w gathers shares w, w + 8, ..., all of a share's loads in flight at once
+      auto share_src = [&](int e) __attribute__((always_inline)) -> const uint2 * {
+        return (const uint2 *)a.cand + ((int64_t)r * a.nslab + e / CAND_PARTS) * a.caps + (sm.hist[NTH + e] >> 16);
+      };
+      auto put = [&](uint2 ev, uint32_t at) __attribute__((always_inline)) {
+        const int id = (int)ev.y;
+        uint32_t k = fkey(__uint_as_float(ev.x));
+        if (mrow) {
+          const int64_t mj = (int64_t)id - ks;
+          if (!(mj >= 0 && mj < a.mask_w && mrow[mj])) k = 0;
+        }
+        if (BLOCKS && !block_ok((int64_t)id - ks)) k = 0;
+        sm.ikey[at] = k;
+        sm.iid[at] = id;
+      };
+      // Wave w gathers shares w, w + 8, ...: entry `lane` of up to GS of its shares is loaded
+      // at once (one memory round trip when the shares hold at most 64 entries, as they mostly
+      // do), then the rest of the longer shares.
+      constexpr int GS = 8;
+      for (int e0 = wave; e0 < ne; e0 += NWV * GS) {
+        uint2 ev[GS];
+        static_for<GS>([&](auto j) __attribute__((always_inline)) {
+          const int e = e0 + NWV * j;
+          const uint32_t n = e < ne ? sm.hist[NTH + e] & 0xFFFFu : 0u;
+          ev[j] = (uint32_t)lane < n ? share_src(e)[lane] : make_uint2(0u, 0u);
+        });
+        static_for<GS>([&](auto j) __attribute__((always_inline)) {
+          const int e = e0 + NWV * j;
+          const uint32_t n = e < ne ? sm.hist[NTH + e] & 0xFFFFu : 0u;
+          if ((uint32_t)lane < n) put(ev[j], run_n + sm.hist[e] + lane);
+        });
+      }
       for (int e = wave; e < ne; e += NWV) {
-        const uint32_t base = run_n + sm.hist[e], n = sm.hist[NTH + e] & 0xFFFFu;
-        if (n == 0) continue;  // uniform over the wave
-        const uint2 *src = (const uint2 *)a.cand + ((int64_t)r * a.nslab + e / CAND_PARTS) * a.caps +
-                           (sm.hist[NTH + e] >> 16);
-        uint2 ev[CAPS_MAX / 64];
-        static_for<CAPS_MAX / 64>([&](auto m) __attribute__((always_inline)) {
-          const uint32_t i = lane + 64 * m;
+        const uint32_t n = sm.hist[NTH + e] & 0xFFFFu;
+        if (n <= 64) continue;  // uniform over the wave
+        const uint2 *src = share_src(e);
+        const uint32_t base = run_n + sm.hist[e];
+        uint2 ev[CAPS_MAX / 64 - 1];
+        static_for<CAPS_MAX / 64 - 1>([&](auto m) __attribute__((always_inline)) {
+          const uint32_t i = lane + 64 * (m + 1);
           ev[m] = i < n ? src[i] : make_uint2(0u, 0u);
         });
-        static_for<CAPS_MAX / 64>([&](auto m) __attribute__((always_inline)) {
-          const uint32_t i = lane + 64 * m;
-          if (i < n) {
-            const int id = (int)ev[m].y;
-            uint32_t k = fkey(__uint_as_float(ev[m].x));
-            if (mrow) {
-              const int64_t mj = (int64_t)id - ks;
-              if (!(mj >= 0 && mj < a.mask_w && mrow[mj])) k = 0;
-            }
-            if (BLOCKS && !block_ok((int64_t)id - ks)) k = 0;
-            sm.ikey[base + i] = k;
-            sm.iid[base + i] = id;
-          }
+        static_for<CAPS_MAX / 64 - 1>([&](auto m) __attribute__((always_inline)) {
+          const uint32_t i = lane + 64 * (m + 1);
+          if (i < n) put(ev[m], base + i);
         });
       }
       __syncthreads();
