@@ -529,9 +529,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(!F16 &&
         if (cand) {
           // values above the row's running threshold also go to its slab, in key order
           uint32_t pm = 0;
+          if constexpr (KF == 0) {
+            // the lane's keys s0 .. s0 + 3 inside its row's window and range as one mask per batch
+            // (with fp8 keys 0.7% faster on long_ctx than testing each key; with MXFP4 keys 2% slower)
+            const int wlo = min(max(v_lo - s0, 0), 4), whi = min(max(v_hi - s0, 0), 4);
+            const uint32_t wm = writer && whi > wlo ? (0xFu >> (4 - whi)) & (0xFu << wlo) : 0u;
   #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            pm |= (uint32_t)(writer && s0 + j >= v_lo && s0 + j < v_hi && val[j] > thr_row) << j;
+            for (int j = 0; j < 4; ++j) pm |= (uint32_t)(val[j] > thr_row) << j;
+            pm &= wm;
+          } else {
+  #pragma unroll
+            for (int j = 0; j < 4; ++j)
+              pm |= (uint32_t)(writer && s0 + j >= v_lo && s0 + j < v_hi && val[j] > thr_row) << j;
+          }
           // wave-uniform tests: at high thresholds most batches have no candidate at all, and
           // a store is issued only for a j that some lane of the wave needs (lanes without a
           // candidate there, or past the slab, are dropped)
