@@ -69,9 +69,20 @@
  *     whenever no key's scoring error exceeds D.  D is not a worst-case bound:
  *     keys can be built whose products cancel but for small terms the MFMA
  *     drops, so that their error exceeds it; such keys can be misplaced.
- *     idx_topk selects exactly on the values it is given.  The first 4 bytes of the workspace receive the number of
- *     rows whose candidate list was too short to settle the boundary (0 on
- *     every workload this library was measured on).
+ *     idx_topk selects exactly on the values it is given.  The first 4 bytes
+ *     of the workspace receive the number of rows whose candidate list was
+ *     too short to settle the boundary (0 on every workload this library was
+ *     measured on).
+ *   - Exact mode.  With the environment variable IDX_EXACT set (to anything
+ *     but "0", read on every call) every score is computed exactly from the
+ *     stored codes instead: fp8 x fp8 and fp8 x e2m1 products are exact, their
+ *     128-term sums are exact in fp64, scales, ReLU, weights and the head sum
+ *     follow in fp64, and each score rounds to fp32 once.  Logits are then
+ *     within one fp32 ulp of the exact values, for head weights of any sign,
+ *     and the selection is that of the exact scores for any keys.  The fused
+ *     path then scores key blocks into its scratch only (no candidate slabs).
+ *     This runs on the fp64 VALU, some 50 times slower than the default mode;
+ *     workspace sizes and every other contract are unchanged.
  *   - Preconditions the host cannot check without reading device memory
  *     (0 <= ks[t] <= ke[t] <= L, finite inputs, q_scale/k_scale >= 0, window
  *     length <= W where a W is given) are the caller's; violating them gives

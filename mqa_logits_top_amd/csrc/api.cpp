@@ -98,6 +98,11 @@ idx::LogitsArgs logits_args(const idx_problem *p, int32_t row0, int32_t nrows, i
   return a;
 }
 
+// A scoring launch on the fp8 MFMA, or the exact fp64 kernel when `exact` (IDX_EXACT).
+hipError_t score(const idx::LogitsArgs &a, const idx_problem *p, int mode, bool exact, hipStream_t s) {
+  return exact ? idx::launch_logits_exact(a, p->k_fmt, p->H, mode, s) : idx::launch_logits(a, p->k_fmt, p->H, mode, s);
+}
+
 idx_status launched(hipError_t e) { return e == hipSuccess ? IDX_OK : IDX_E_LAUNCH; }
 
 struct Carve {
@@ -345,7 +350,7 @@ idx_status idx_mqa_logits(const idx_problem *p, float *logits, int64_t ld, int32
   hipStream_t s = (hipStream_t)stream;
   if (p->L > 0) {
     idx::LogitsArgs a = logits_args(p, 0, p->T, 0, p->L, logits, ld, W);
-    st = launched(idx::launch_logits(a, p->k_fmt, p->H, idx::STORE_DENSE, s));
+    st = launched(score(a, p, idx::STORE_DENSE, idx::exact_enabled(), s));
     if (st) return st;
   }
   return launched(idx::launch_fill_tail(logits, ld, W, p->ks, p->ke, 0, p->T, s));
@@ -364,7 +369,7 @@ idx_status idx_mqa_logits_block(const idx_problem *p, int32_t row0, int32_t nrow
   if (nrows == 0 || key_hi <= key0) return IDX_OK;
   if ((st = idx::debug_check(p->ks, p->ke, p->T, p->L, -1, p, stream))) return st;
   idx::LogitsArgs a = logits_args(p, row0, nrows, key0, key_hi, out, ld, nkeys);
-  return launched(idx::launch_logits(a, p->k_fmt, p->H, idx::STORE_BLOCK, (hipStream_t)stream));
+  return launched(score(a, p, idx::STORE_BLOCK, idx::exact_enabled(), (hipStream_t)stream));
 }
 
 idx_status idx_topk(const float *logits, int64_t ld, int32_t W, const int32_t *ks, const int32_t *ke,
@@ -465,7 +470,9 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
   // slabs for every launch after the first; up to SLAB_BLOCKS blocks per launch unless a
   // consumer mask asks for scores and slabs in one pass
   const bool slab_ok = slabs_fit(Tc, nslab_max);
-  const KeySchedule ksch = key_schedule(p, Bk, Kc, slab_ok && !mask && !blocks);
+  // exact scores (IDX_EXACT) come from the fp64 kernel, which writes no candidate slabs
+  const bool exact = exact_enabled();
+  const KeySchedule ksch = key_schedule(p, Bk, Kc, slab_ok && !mask && !blocks && !exact);
   idx::WindowFlags wf = window_flags(p, Tc, ksch, cv.take<uint32_t>(idx::MAX_WINDOW_FLAGS));
   wf.kshift = cv.take<int32_t>(shift_ws(p, Tc) / 4);
   if ((st = launched(idx::launch_key_bound((const uint8_t *)p->k, (const uint8_t *)p->k_scale, p->k_fmt, p->L,
@@ -506,7 +513,7 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
       a.by_row = launch_flag(wf, r0, kb);
       a.kshift = kshift;
       b.launch_flag = a.by_row;
-      const bool slabs = ksch.slab(l) && nk > 0 && slab_ok && a.nsplit <= nslab_max;
+      const bool slabs = ksch.slab(l) && nk > 0 && slab_ok && a.nsplit <= nslab_max && !exact;
       if (slabs && !mask && !blocks) {
         // the launch writes the scores above each row's running threshold to its slabs; the
         // row blocks where a slab overflowed are scored again into the scratch, one block of
@@ -558,7 +565,7 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
         b.nslab = a.nsplit;
         b.caps = CAPS;
         if ((st = launched(idx::launch_logits(a, p->k_fmt, p->H, idx::STORE_CAND, s)))) return st;
-      } else if (nk > 0 && (st = launched(idx::launch_logits(a, p->k_fmt, p->H, idx::STORE_BLOCK, s)))) {
+      } else if (nk > 0 && (st = launched(score(a, p, idx::STORE_BLOCK, exact, s)))) {
         return st;
       }
       if ((st = launched(idx::launch_topk(b, s)))) return st;
@@ -647,6 +654,7 @@ idx_status idx_block_candidates(const idx_problem *p, const float *logits, int64
   if ((st = idx::debug_check(p->ks, p->ke, p->T, logits ? INT32_MAX : p->L, W, logits ? nullptr : p, stream)))
     return st;
   hipStream_t s = (hipStream_t)stream;
+  const bool exact = idx::exact_enabled();
   Carve cv{(uint8_t *)ws};
   const int32_t Kc = logits ? n_blocks : cand_cap(n_blocks);
   RefineWs rw = carve_refine(cv, Tc, cand_cap(n_blocks));
@@ -696,7 +704,7 @@ idx_status idx_block_candidates(const idx_problem *p, const float *logits, int64
           idx::LogitsArgs a = logits_args(p, r0, nr, kb, kb + nk, pooled, pld, (nk + pool - 1) / pool);
           a.by_row = launch_flag(wf, r0, kb);
           b.launch_flag = a.by_row;
-          if ((st = launched(idx::launch_logits(a, p->k_fmt, p->H, idx::STORE_POOL8, s)))) return st;
+          if ((st = launched(score(a, p, idx::STORE_POOL8, exact, s)))) return st;
         }
         b.vals = pooled;
         b.ld = pld;

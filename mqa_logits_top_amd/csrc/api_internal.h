@@ -21,6 +21,9 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
 
 // IDX_DEBUG set (and not "0") in the environment, read on every call.
 bool debug_enabled();
+// IDX_EXACT set (and not "0") in the environment, read on every call: scores are computed
+// exactly (fp64 over the codes) instead of on the fp8 MFMA, and no candidate slabs are used.
+bool exact_enabled();
 // In debug mode: check on the device that 0 <= ks[t] <= ke[t] <= L and ke[t] - ks[t] <= W (W >= 0)
 // for t < T, and, with a problem p, that its q_scale are >= 0, its w finite and its key scales
 // valid; synchronises `stream` and returns IDX_E_DEVICE_CHECK on a failure.  IDX_OK otherwise,

@@ -93,6 +93,11 @@ bool debug_enabled() {
   return v && *v && std::strcmp(v, "0") != 0;
 }
 
+bool exact_enabled() {
+  const char *v = std::getenv("IDX_EXACT");
+  return v && *v && std::strcmp(v, "0") != 0;
+}
+
 idx_status debug_check(const int32_t *ks, const int32_t *ke, int32_t T, int32_t L, int64_t W, const idx_problem *p,
                        void *stream) {
   if (!debug_enabled()) return IDX_OK;

@@ -69,6 +69,9 @@ struct LogitsArgs {
 };
 
 hipError_t launch_logits(const LogitsArgs &a, int k_fmt, int H, int mode, hipStream_t s);
+// The same scores computed exactly from the codes in fp64 (STORE_DENSE, STORE_BLOCK and
+// STORE_POOL8 layouts; split and nsplit unused); rounded to fp32 once.
+hipError_t launch_logits_exact(const LogitsArgs &a, int k_fmt, int H, int mode, hipStream_t s);
 int logits_rows_per_workgroup(int H);   // RPW of the scoring launches
 // Row blocks of a candidate-slab launch whose rows the top-K cannot serve from the slabs
 // alone (a share overflowed, the shares together exceed the merge capacity, or the row's

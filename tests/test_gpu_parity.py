@@ -88,7 +88,8 @@ def test_dense_logits(case):
 
 
 @pytest.mark.xfail(strict=True, reason="head weights of both signs: the fp8 MFMA's truncation error is ~2e-5 of "
-                                       "sum_h |w_h| ReLU(x_h), which exceeds 1e-3 of a score that cancels down")
+                                       "sum_h |w_h| ReLU(x_h), which exceeds 1e-3 of a score that cancels down "
+                                       "(exact scores with IDX_EXACT=1: test_gpu_exact_mode.py)")
 @pytest.mark.parametrize("param", MIXED, ids=_case_id)
 def test_mixed_sign_logits_plain_bar(param):
     c = _make_case(param)
@@ -702,7 +703,8 @@ def _aligned_truncation_problem():
 @pytest.mark.xfail(strict=True, reason="the refinement band D = 2 * 2^-13 * Kmax * sum_h |w'_h| Mq_h is a safety "
                                        "factor on the fp8 MFMA's truncation error, not a worst-case bound: keys "
                                        "built so that their truncation errors align (here 337.5 per head against "
-                                       "a band of 98) fall outside it and are not re-scored")
+                                       "a band of 98) fall outside it and are not re-scored (exact scores with "
+                                       "IDX_EXACT=1: test_gpu_exact_mode.py)")
 def test_refine_band_against_aligned_truncation():
     p, a_rows = _aligned_truncation_problem()
     K = len(a_rows)
