@@ -129,13 +129,10 @@ constexpr size_t HEAD = 256 + 2048;
 // instead of all sitting a power of two apart.
 int32_t pitch(int32_t cols) { return cols + 64; }
 size_t refine_ws(int32_t Tc, int32_t Kc) { return HEAD + 2 * round_up_sz((size_t)Tc * Kc * 4, 256); }
-// Candidate slabs of the fused path: for launches from slab_from() on, the scoring
-// kernel appends each row's values above its running list's smallest entry to one
-// slab of CAPS entries per key split; the top-K merges them instead of the keys.
+// Candidate slabs of the fused path: in a slab launch the scoring kernel appends each row's
+// values above its running list's smallest entry to one slab of CAPS entries per key split;
+// the top-K merges them instead of the keys.
 constexpr int32_t CAPS = 512;
-// Launches from the second on write slabs: the first leaves each row's running list full
-// and its threshold known.
-int32_t slab_from(const idx_problem *) { return 1; }
 int32_t block_slabs(int32_t Bk) {
   int32_t split, nsplit;
   plan_splits(Bk, split, nsplit);
