@@ -98,6 +98,17 @@ def test_dsv4_row_count_invariance():
         assert torch.equal(ci, gi) and torch.equal(cv.view(torch.int32), gv.view(torch.int32)), rc
 
 
+def test_long_ctx_row_count_invariance():
+    """P2 Accuracy/equivalence at its own shape: the 16384-row long-context chunk scored in one
+    call and in row chunks of 128 .. 4096 gives identical output, bitwise."""
+    p, d, dq = prob("long_ctx")
+    K, Bk = p.meta["K"], p.meta["block_k"]
+    gi, gv = fused(d, K, Bk, row_chunk=0)
+    for rc in (128, 256, 512, 1024, 2048, 4096):
+        ci, cv = fused(d, K, Bk, row_chunk=rc)
+        assert torch.equal(ci, gi) and torch.equal(cv.view(torch.int32), gv.view(torch.int32)), rc
+
+
 def test_dsv4_duplicate_keys_tie_by_index():
     p, d, dq = prob("dsv4_mxfp4")
     K = p.meta["K"]
