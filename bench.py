@@ -665,6 +665,9 @@ def main():
               f"query rows with no exchange, see the design notes)", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    for var in ("IDX_EXACT", "IDX_DEBUG"):   # the benchmark times the default path
+        if os.environ.pop(var, None) not in (None, "", "0"):
+            log(f"[bench] {var} ignored: the benchmark times the default path")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
