@@ -179,9 +179,10 @@ idx_status idx_topk(const float *logits, int64_t ld, int32_t W, const int32_t *k
  * score its first key block of block_k keys into a [row_chunk, block_k] fp32
  * scratch and take each row's top-(K + 512) from it; every later launch (up to
  * four blocks of keys) writes only the scores above each row's running
- * (K + 512)-th to per-row candidate slabs, which are merged into the running
- * lists (rows whose slabs overflow are scored again into the scratch, one block
- * at a time); then settle the boundary exactly (idx_refine_topk).  [T, L] logits
+ * (K + 512)-th to per-row candidate slabs in the scratch rows, which are merged
+ * into the running lists (the rows of a row block where a slab overflowed are
+ * scored again into the scratch, one block at a time); then settle the boundary
+ * exactly (idx_refine_topk).  [T, L] logits
  * are never materialised: the workspace is O(row_chunk * (block_k + K)), with
  * a bound that holds whatever L.  The result
  * equals idx_mqa_logits + idx_topk (K + 512 columns) + idx_refine_topk

@@ -131,20 +131,24 @@ int32_t pitch(int32_t cols) { return cols + 64; }
 size_t refine_ws(int32_t Tc, int32_t Kc) { return HEAD + 2 * round_up_sz((size_t)Tc * Kc * 4, 256); }
 // Candidate slabs of the fused path: in a slab launch the scoring kernel appends each row's
 // values above its running list's smallest entry to one slab of CAPS entries per key split;
-// the top-K merges them instead of the keys.
+// the top-K merges them instead of the keys.  A row's slabs lie in its row of the score
+// scratch, which slab launches leave unused: a row block that the slab check flags is scored
+// again into the scratch, over its slabs, and its rows then read columns instead.
 constexpr int32_t CAPS = 512;
 int32_t block_slabs(int32_t Bk) {
   int32_t split, nsplit;
   plan_splits(Bk, split, nsplit);
   return nsplit;
 }
-// Thresholds, slab-check flags, count words and (value, id) pairs of ns slabs per row;
-// then the per-row words of the two-call top-K of a launch wider than B_k.
+// Thresholds, slab-check flags and count words of ns slabs per row; then the per-row words of
+// the two-call top-K of a launch wider than B_k.
 size_t slab_ws(int32_t Tc, int32_t ns) {
   return round_up_sz((size_t)Tc * 4, 256) + round_up_sz((size_t)(Tc / 8 + 1) * 4, 256) +
-         round_up_sz((size_t)Tc * ns * idx::CAND_PARTS * 4, 256) +
-         round_up_sz((size_t)Tc * ns * CAPS * 8, 256) + round_up_sz((size_t)Tc * 4, 256);
+         round_up_sz((size_t)Tc * ns * idx::CAND_PARTS * 4, 256) + round_up_sz((size_t)Tc * 4, 256);
 }
+// Floats per score scratch row: B_k scores (plus pitch), or the row's ns slabs of CAPS
+// (value, id) pairs if they take more.
+int32_t scratch_pitch(int32_t Bk, int32_t ns) { return std::max(pitch(Bk), ns * CAPS * 2); }
 // Key launches of the fused path (P1 section 2.3: key blocks scored one after another, each
 // row's running top-K merged across them; memory c * T * B_k).  The first launches of a row
 // chunk score one block of B_k keys each into the [Tc, B_k] score scratch, from which the
@@ -154,11 +158,11 @@ size_t slab_ws(int32_t Tc, int32_t ns) {
 // the scores above the threshold, to candidate slabs, and takes up to SLAB_BLOCKS blocks'
 // keys (spread evenly over the keys left): fewer launches, each with more work items, so
 // fewer merges per row and fewer last waves of workgroups that drain with the CU partly
-// empty.  Rows whose slabs overflow are scored again into the scratch, one block at a time.
-// At higher candidate densities a slab launch costs more than a block launch with its top-K
-// (glm_chunk's second block, 8% of its scores above the threshold: 298 + 93 us against
-// 243 + 108 us).  Without slabs (a consumer mask, or too many rows for the slab index range)
-// every launch takes one block.
+// empty.  Row blocks with a slab that overflowed are scored again into the scratch, one block
+// at a time.  At higher candidate densities a slab launch costs more than a block launch with
+// its top-K (glm_chunk's second block, 8% of its scores above the threshold: 298 + 93 us
+// against 243 + 108 us).  Without slabs (a consumer mask or block list, or exact scores) every
+// launch takes one block.
 struct KeySchedule {
   int32_t bk, nb, step, n;   // block keys, block launches, keys of each slab launch, launches
   int32_t start(int32_t l) const { return l < nb ? l * bk : nb * bk + (l - nb) * step; }
@@ -189,8 +193,6 @@ int32_t schedule_slabs(const KeySchedule &k, int32_t L) {
   if (k.n <= k.nb) return 0;
   return std::max(block_slabs(std::min(k.step, L - k.start(k.nb))), block_slabs(L - k.start(k.n - 1)));
 }
-// Slab pair indices of a launch stay within int32 for row chunks below this.
-bool slabs_fit(int32_t Tc, int32_t ns) { return (int64_t)Tc * ns * CAPS * 8 < INT32_MAX; }
 // Row gather: q [R, H, D] bytes, q_scale and w [R, H] floats, ks and ke [R].
 size_t gather_ws(int32_t R, int32_t H, int32_t D) {
   return round_up_sz((size_t)R * H * D, 256) + 2 * round_up_sz((size_t)R * H * 4, 256) +
@@ -200,12 +202,13 @@ size_t gather_ws(int32_t R, int32_t H, int32_t D) {
 constexpr size_t FLAGS_WS = (size_t)idx::MAX_WINDOW_FLAGS * 4;
 // The row chunks' first window keys (WindowFlags::kshift).
 size_t shift_ws(const idx_problem *p, int32_t Tc) { return round_up_sz((size_t)((p->T + Tc - 1) / Tc + 1) * 4, 256); }
-// The fused path's workspace: refinement, the [Tc, B_k] score scratch, the slabs of the
-// slab schedule (the widest the call can take), the window flags and the key shifts.
+// The fused path's workspace: refinement, the score scratch (which also holds the slabs of the
+// slab schedule, the widest the call can take), the slabs' bookkeeping, the window flags and
+// the key shifts.
 size_t fused_ws(const idx_problem *p, int32_t Tc, int32_t Bk, int32_t K) {
   const int32_t ns = schedule_slabs(key_schedule(p, Bk, cand_cap(K), true), p->L);
-  return refine_ws(Tc, cand_cap(K)) + round_up_sz((size_t)Tc * pitch(Bk) * 4, 256) + slab_ws(Tc, ns) + FLAGS_WS +
-         shift_ws(p, Tc);
+  return refine_ws(Tc, cand_cap(K)) + round_up_sz((size_t)Tc * scratch_pitch(Bk, ns) * 4, 256) + slab_ws(Tc, ns) +
+         FLAGS_WS + shift_ws(p, Tc);
 }
 size_t cand_ws(int32_t Tc, int32_t pooled_cols, int32_t n_blocks, bool fused) {
   return refine_ws(Tc, cand_cap(n_blocks)) + round_up_sz((size_t)Tc * pitch(pooled_cols) * 4, 256) +
@@ -456,20 +459,20 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
   const int32_t Kc = cand_cap(K);
   Carve cv{(uint8_t *)ws};
   RefineWs rw = carve_refine(cv, Tc, Kc);
-  const int32_t sld = pitch(Bk);
-  float *scratch = cv.take<float>((size_t)Tc * sld);
   const int32_t nslab_max = schedule_slabs(key_schedule(p, Bk, cand_cap(K), true), p->L);
+  const int32_t sld = scratch_pitch(Bk, nslab_max);
+  float *scratch = cv.take<float>((size_t)Tc * sld);
+  uint32_t *slab = (uint32_t *)scratch;                     // row r's slabs in its scratch row
   float *thr = cv.take<float>((size_t)Tc);
   uint32_t *ovf = cv.take<uint32_t>((size_t)Tc / 8 + 1);   // per scoring row block (>= 8 rows)
   uint32_t *ccnt = cv.take<uint32_t>((size_t)Tc * nslab_max * idx::CAND_PARTS);
-  uint32_t *slab = cv.take<uint32_t>((size_t)Tc * nslab_max * CAPS * 2);
   uint32_t *col_rows = cv.take<uint32_t>((size_t)Tc);
-  // slabs for every launch after the first; up to SLAB_BLOCKS blocks per launch unless a
-  // consumer mask asks for scores and slabs in one pass
-  const bool slab_ok = slabs_fit(Tc, nslab_max);
-  // exact scores (IDX_EXACT) come from the fp64 kernel, which writes no candidate slabs
+  // Slab launches after the first block launches, unless a consumer mask or block list
+  // restricts the keys (the scoring kernel cannot drop the keys they exclude, which would
+  // fill the slabs), or exact scores (IDX_EXACT) come from the fp64 kernel, which writes no
+  // slabs: then every launch takes one block.
   const bool exact = exact_enabled();
-  const KeySchedule ksch = key_schedule(p, Bk, Kc, slab_ok && !mask && !blocks && !exact);
+  const KeySchedule ksch = key_schedule(p, Bk, Kc, !mask && !blocks && !exact);
   idx::WindowFlags wf = window_flags(p, Tc, ksch, cv.take<uint32_t>(idx::MAX_WINDOW_FLAGS));
   wf.kshift = cv.take<int32_t>(shift_ws(p, Tc) / 4);
   if ((st = launched(idx::launch_key_bound((const uint8_t *)p->k, (const uint8_t *)p->k_scale, p->k_fmt, p->L,
@@ -510,14 +513,15 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
       a.by_row = launch_flag(wf, r0, kb);
       a.kshift = kshift;
       b.launch_flag = a.by_row;
-      const bool slabs = ksch.slab(l) && nk > 0 && slab_ok && a.nsplit <= nslab_max && !exact;
-      if (slabs && !mask && !blocks) {
+      if (ksch.slab(l) && nk > 0) {
+        if (a.nsplit > nslab_max) return IDX_E_LAUNCH;   // (not reached: the schedule sized the slabs)
         // the launch writes the scores above each row's running threshold to its slabs; the
         // row blocks where a slab overflowed are scored again into the scratch, one block of
         // keys per pass, and the top-K reads those rows' columns there
         idx::LogitsArgs c = a;
         c.thr = thr;
         c.cand = slab;
+        c.cand_ld = sld / 2;
         c.ccnt = ccnt;
         c.caps = CAPS;
         if ((st = launched(idx::launch_logits(c, p->k_fmt, p->H, idx::STORE_SLAB, s)))) return st;
@@ -535,9 +539,12 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
           idx::TopkArgs bh = b;
           if (h0 == 0) {   // slab merges, and the first block's columns for the other rows
             bh.cand = slab;
+            bh.cand_ld = sld / 2;
             bh.ccnt = ccnt;
             bh.nslab = a.nsplit;
             bh.caps = CAPS;
+            bh.slab_flags = ovf;
+            bh.slab_rpw = rpw;
             bh.vcols = hn;
             bh.col_rows = nk > Bk ? col_rows : nullptr;
           } else {         // the next block's columns, for the rows that read columns
@@ -550,21 +557,7 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
         continue;
       }
       if (nk > Bk) return IDX_E_UNSUPPORTED;   // the scratch holds one block (not reached: see key_schedule)
-      if (slabs) {
-        // a consumer mask the scoring kernel does not see would fill the slabs with keys the
-        // top-K then drops: score the block and the slabs in one pass instead
-        a.thr = thr;
-        a.cand = slab;
-        a.ccnt = ccnt;
-        a.caps = CAPS;
-        b.cand = slab;
-        b.ccnt = ccnt;
-        b.nslab = a.nsplit;
-        b.caps = CAPS;
-        if ((st = launched(idx::launch_logits(a, p->k_fmt, p->H, idx::STORE_CAND, s)))) return st;
-      } else if (nk > 0 && (st = launched(score(a, p, idx::STORE_BLOCK, exact, s)))) {
-        return st;
-      }
+      if (nk > 0 && (st = launched(score(a, p, idx::STORE_BLOCK, exact, s)))) return st;
       if ((st = launched(idx::launch_topk(b, s)))) return st;
     }
     idx::RefineArgs r = refine_args(p, rw, r0, nr, Kc, K, 1, out_idx + (int64_t)r0 * K,

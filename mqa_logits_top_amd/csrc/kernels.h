@@ -5,8 +5,8 @@
 
 namespace idx {
 
-// STORE_SLAB: the candidate output of STORE_CAND alone, no block scores.
-enum LogitsMode { STORE_DENSE = 0, STORE_BLOCK = 1, STORE_POOL8 = 2, STORE_CAND = 3, STORE_SLAB = 4 };
+// STORE_SLAB: no scores, only the candidate output (LogitsArgs::cand).
+enum LogitsMode { STORE_DENSE = 0, STORE_BLOCK = 1, STORE_POOL8 = 2, STORE_SLAB = 4 };
 
 // Largest number of parts a scoring work item (row block x key split) is cut into.
 constexpr int CAND_PARTS = 4;
@@ -37,13 +37,14 @@ struct LogitsArgs {
   int64_t ld;
   int32_t wcols;  // columns available in an output row (dense W, block nkeys, pool ceil(nkeys/8))
   int32_t nfull, parts;  // launch layout (filled by launch_logits)
-  // Candidate output (STORE_CAND = STORE_BLOCK plus this): launch row r's in-window values above
-  // thr[r] (NaN: none) also go, as (value bits, key id) word pairs in key order, to slab
-  // r * nsplit + split of caps pairs, part p of an item to its p-th share; the count word
-  // ccnt[(r * nsplit + split) * CAND_PARTS + p] describes that share (parts that do not
+  // Candidate output (STORE_SLAB): launch row r's in-window values above thr[r] (NaN: none)
+  // go, as (value bits, key id) word pairs in key order, to its slab for the split: caps pairs
+  // at pair r * cand_ld + split * caps of cand, part p of an item to its p-th share; the count
+  // word ccnt[(r * nsplit + split) * CAND_PARTS + p] describes that share (parts that do not
   // exist: count 0).
   const float *thr;
   uint32_t *cand;
+  int64_t cand_ld;   // pairs from one row's slabs to the next row's (>= nsplit * caps)
   uint32_t *ccnt;
   // STORE_BLOCK: score only the row blocks (RPW rows of the launch) whose word here is
   // nonzero (nullable: all)
@@ -115,10 +116,14 @@ struct TopkArgs {
   int32_t first;          // 1: no running state yet (out_* contents are ignored)
   // TOPK_BLOCK with the scoring launch's candidate slabs (nullable cand; layout as in
   // LogitsArgs): a row whose list is full and whose nslab slabs all fit merges the slabs
-  // instead of reading vals
+  // instead of reading vals, unless its row block (slab_rpw rows of the launch) is flagged in
+  // slab_flags (nullable), whose rows were scored again into vals
   const uint32_t *cand;
+  int64_t cand_ld;
   const uint32_t *ccnt;
   int32_t nslab, caps;
+  const uint32_t *slab_flags;
+  int32_t slab_rpw;
   float *thr_out;         // nullable: per launch row, the full list's smallest value, else NaN
   // A launch's columns in two calls: vcols > 0 limits the columns read from vals to [0, vcols)
   // (rows still merge slabs over all ncols); col_rows (nullable) receives 1 for a row that read

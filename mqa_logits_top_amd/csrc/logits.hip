@@ -268,7 +268,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(!F16 &&
   const int ntiles = pt1 - pt0 + (extend ? 1 : 0);
   // candidate share of this part in each of its rows' slabs
   const int share0 = part * a.caps / nparts, share = (part + 1) * a.caps / nparts - share0;
-  constexpr bool cand = MODE == STORE_CAND || MODE == STORE_SLAB;
+  constexpr bool cand = MODE == STORE_SLAB;
   if (cand && part == 0) {  // count words of the parts an item does not have
     for (int i = tid; i < RPW * (CAND_PARTS - nparts); i += NW * 64) {
       const int rr = r_begin + i / (CAND_PARTS - nparts);
@@ -332,20 +332,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(!F16 &&
   }
   // keys this lane may store: inside its row's window and inside the workgroup range
   const int v_lo = max(kst, s_lo), v_hi = min(ket, s_hi);
-  // candidate slab of this lane's row (STORE_BLOCK with candidate output)
+  // the wave's first output row (of the launch): buffer resources cover its QR rows
+  const int wrow = min(wr, a.row0 + a.nrows - 1) - a.row0;
   float thr_row = __builtin_nanf("");
-  int slab = 0;  // pair offset of the slab (slabs span < 2^31 bytes)
+  int slab = 0;  // pair offset of the lane's slab for this split, from the wave's first row's slabs
   __amdgpu_buffer_rsrc_t crsrc;
   if (cand) {
     const int rr = min(t_out, r_end - 1) - a.row0;
     thr_row = a.thr[rr];
-    slab = (rr * a.nsplit + split_i) * a.caps + share0;
-    crsrc = __builtin_amdgcn_make_buffer_rsrc(a.cand, 0, a.nrows * a.nsplit * a.caps * 8, RSRC3);
+    slab = (int)((rr - wrow) * a.cand_ld) + split_i * a.caps + share0;
+    crsrc = __builtin_amdgcn_make_buffer_rsrc(a.cand + (int64_t)wrow * a.cand_ld * 2, 0, (int)(QR * a.cand_ld * 8),
+                                              RSRC3);
   }
   uint32_t crow = 0;  // candidates of this lane's row so far (uniform over its 16 lanes)
   const bool writer = row_ok && (QR == 4 || (g & 1) == 0);
-  // one buffer resource per wave over its QR output rows
-  const int wrow = min(wr, a.row0 + a.nrows - 1) - a.row0;
   const int64_t ld = a.ld;
   __amdgpu_buffer_rsrc_t orsrc =
       __builtin_amdgcn_make_buffer_rsrc(a.out + (int64_t)wrow * ld, 0, (int)(QR * ld * 4), RSRC3);
@@ -563,7 +563,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(!F16 &&
             crow += tot;
           }
         }
-        if (MODE != STORE_POOL8 && MODE != STORE_SLAB) {
+        if constexpr (MODE == STORE_DENSE || MODE == STORE_BLOCK) {
           const int col = MODE == STORE_DENSE ? s0 - kst : s0 - a.key_lo;   // column of key s0
           if (writer && row_al && s0 >= v_lo && s0 + 4 <= lim) {
             const v4u d = {__float_as_uint(val[0]), __float_as_uint(val[1]), __float_as_uint(val[2]),
@@ -577,7 +577,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(!F16 &&
                                                     0, 0);
             }
           }
-        } else {
+        } else if constexpr (MODE == STORE_POOL8) {
           // 8-key blocks of the row start at ks: the block starting in octet o (keys 8 o .. 8 o + 7,
           // held by lanes 2 m, 2 m + 1) is keys 8 o + r .. 8 o + r + 7, r = ks & 7.  hi: the octet's
           // in-window keys at positions >= r (the head of its block); lo: those at positions < r
@@ -724,7 +724,6 @@ hipError_t launch2(const LogitsArgs &a, int mode, hipStream_t s) {
   switch (mode) {
     case STORE_DENSE: return launch3<KF, H, STORE_DENSE>(a, s);
     case STORE_BLOCK: return launch3<KF, H, STORE_BLOCK>(a, s);
-    case STORE_CAND: return launch3<KF, H, STORE_CAND>(a, s);
     case STORE_SLAB: return launch3<KF, H, STORE_SLAB>(a, s);
     default: return launch3<KF, H, STORE_POOL8>(a, s);
   }

@@ -321,7 +321,8 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   // fit the scoring kernel's slabs merges those instead of reading the block's columns
   bool merged = false;
   uint32_t list_min = 0;  // smallest key of the list after the last merge (once it is full)
-  if (SLABS && !a.first && run_n == K) {
+  // (a row block flagged by the slab check was scored again into vals, over its slabs)
+  if (SLABS && !a.first && run_n == K && !(a.slab_flags && a.slab_flags[r / a.slab_rpw] != 0u)) {
     // one count word per (slab, part): candidates in the low half, share offset above
     const int ne = a.nslab * CAND_PARTS;
     uint32_t cs = 0, over = 0, cw = 0;
@@ -339,7 +340,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       if (tid < ne) { sm.hist[tid] = ex; sm.hist[NTH + tid] = (cw & 0xFFFF0000u) | cs; }
       __syncthreads();
       auto share_src = [&](int e) __attribute__((always_inline)) -> const uint2 * {
-        return (const uint2 *)a.cand + ((int64_t)r * a.nslab + e / CAND_PARTS) * a.caps + (sm.hist[NTH + e] >> 16);
+        return (const uint2 *)a.cand + (int64_t)r * a.cand_ld + (e / CAND_PARTS) * a.caps + (sm.hist[NTH + e] >> 16);
       };
       auto put = [&](uint2 ev, uint32_t at) __attribute__((always_inline)) {
         const int id = (int)ev.y;

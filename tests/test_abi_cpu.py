@@ -152,12 +152,12 @@ def test_workspace_sizes(lib):
     p = _problem(T=2048, L=65536)
     n = ctypes.c_size_t()
     assert lib.idx_workspace_size(2, ctypes.byref(p), 2048, 32768, 0, 0, 0, 0, ctypes.byref(n)) == 0
-    # scores of one block of B_k keys ([Tc, B_k + 64] fp32), then the slabs of the later launches:
-    # thresholds, overflow flags, count words (ns splits x 4 parts), (value, id) pairs (ns slabs
-    # of 512), the two-call top-K's row words.  Here K + 512 = 2560 > 65536 / 20: both blocks are
-    # block launches and there are no slabs.
-    slab = lambda Tc, ns: (_r(Tc * 4) + _r((Tc // 8 + 1) * 4) + _r(Tc * ns * 4 * 4) + _r(Tc * ns * 512 * 8)
-                           + _r(Tc * 4))
+    # scores of one block of B_k keys ([Tc, B_k + 64] fp32; a row's (value, id) slabs of the later
+    # launches, ns slabs of 512 pairs, lie in its scratch row), then the slabs' bookkeeping:
+    # thresholds, overflow flags, count words (ns splits x 4 parts), the two-call top-K's row
+    # words.  Here K + 512 = 2560 > 65536 / 20: both blocks are block launches and there are no
+    # slabs.
+    slab = lambda Tc, ns: _r(Tc * 4) + _r((Tc // 8 + 1) * 4) + _r(Tc * ns * 4 * 4) + _r(Tc * 4)
     flags = 16384 * 4   # window flags of the scoring launches, a fixed region
     shift = lambda T, Tc: _r((-(-T // Tc) + 1) * 4)   # each row chunk's first window key
     assert n.value == (head + 2 * _r(2048 * kc(2048) * 4) + 2048 * (32768 + 64) * 4 + slab(2048, 0) + flags
@@ -174,6 +174,14 @@ def test_workspace_sizes(lib):
     p4 = _problem(T=16384, L=65536)
     assert lib.idx_workspace_size(2, ctypes.byref(p4), 512, 32768, 4096, 0, 0, 0, ctypes.byref(m)) == 0
     assert m.value < n.value
+    # a small B_k: a row's slabs (1024 floats per split) take more than B_k + 64 floats, and the
+    # scratch rows widen to hold them (exactly one slab count fits the size)
+    p5 = _problem(T=4096, L=200000)
+    assert lib.idx_workspace_size(2, ctypes.byref(p5), 64, 2048, 512, 0, 0, 0, ctypes.byref(m)) == 0
+    fits = [ns for ns in range(1, 65)
+            if m.value == (head + 2 * _r(512 * kc(64) * 4) + _r(512 * max(2048 + 64, 1024 * ns) * 4)
+                           + slab(512, ns) + flags + shift(4096, 512))]
+    assert len(fits) == 1 and 1024 * fits[0] > 2048 + 64, fits
     assert lib.idx_workspace_size(3, ctypes.byref(p), 0, 32768, 0, 8, 2048, 0, ctypes.byref(n)) == 0
     assert n.value == head + 2 * _r(2048 * kc(2048) * 4) + 2048 * (4096 + 64) * 4 + 2048 * 2048 * 4 + flags
     assert lib.idx_workspace_size(4, ctypes.byref(p), 0, 0, 1024, 8, 2048, 65536, ctypes.byref(n)) == 0

@@ -188,16 +188,19 @@ def test_fused_slab_overflow_and_fit():
     assert torch.equal(dv.view(torch.int32), fv.view(torch.int32))
 
 
-def test_fused_slab_launch_mixed_fallback():
-    """A slab launch of several key blocks (with K + 512 = 576 and B_k = 8192: keys 0..16384
-    in two block launches, then keys 16384..40000, three blocks, in one slab launch) where one
-    row block's slabs overflow and the other's fit: the overflowing rows read the launch's scores
-    from the one-block scratch one block per pass, the others merge their slabs once and are
-    left alone by the later passes (their windows reach into the later blocks, whose scores
-    the scratch does not hold for them).  Keys 16384..20480 are made non-negative and scaled
-    x64; rows 8..15 have non-negative q (those keys beat their whole running list), rows 0..7
-    non-positive q (those keys score 0)."""
-    T, L, H, K, Bk = 16, 40000, 64, 64, 8192
+@pytest.mark.parametrize("Bk", [8192, 1024])
+def test_fused_slab_launch_mixed_fallback(Bk):
+    """A slab launch of several key blocks where one row block's slabs overflow and the other's
+    fit: the overflowing row block is scored again into the scratch, over its slabs, one block
+    per pass, and its rows read the scores; the other rows merge their slabs once and are left
+    alone by the later passes (their windows reach into the later blocks, whose scores the
+    scratch does not hold for them).  With K + 512 = 576 and B_k = 8192, keys 0..16384 go in two
+    block launches and keys 16384..40000, three blocks, in one slab launch.  With B_k = 1024 the
+    slab launches take four blocks of 1024 keys and 8 splits, whose slabs (8 x 512 pairs) are
+    wider than a row of B_k scores: the scratch rows widen to hold them.  Keys 16384..20480 are
+    made non-negative and scaled x64; rows 8..15 have non-negative q (those keys beat their
+    whole running list), rows 0..7 non-positive q (those keys score 0)."""
+    T, L, H, K = 16, 40000, 64, 64
     lo, hi = 16384, 20480
     p = synth.make_problem(T, L, H, k_fmt=synth.K_FP8, seed=12)
     p.k[lo:hi] &= 0x7F
