@@ -82,13 +82,14 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload, rect):
-    """HBM bytes per scoring launch from the committed rocprofv3 counter summary, if it was taken
-    on the current kernel source and the same launch rectangle (rows, keys)."""
+def load_traffic(workload, mode, rect):
+    """HBM bytes per scoring launch of one mode ("block", "slab") from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source and the same launch rectangle
+    (rows, keys)."""
     path = os.path.join(ROOT, "profiles", "logits_hbm_traffic.json")
     try:
         with open(path) as f:
-            e = json.load(f).get(workload)
+            e = json.load(f).get(f"{workload}/{mode}")
         if e and e.get("kernel_source_hash") == kernel_source_hash() and e.get("rect") == list(rect):
             return e["bytes_per_launch"]
     except (OSError, ValueError, KeyError):
@@ -106,16 +107,24 @@ def time_events(fn, n, stream):
     return [a.elapsed_time(b) for a, b in evs]
 
 
-def key_launches(L, block_k, K):
-    """(key0, keys) of the fused path's scoring launches over one row chunk: one block of B_k
-    keys per launch while the keys seen stay below 20 (K + 512), then up to four blocks per
-    launch, spread evenly over the keys left."""
+def block_launches(L, block_k, K):
+    """Number of one-block launches at the start of a row chunk's key schedule."""
     kc = min(K + 512, 2560)
     if L <= block_k:
-        return [(0, L)]
+        return 1
     nb = 1
     while nb * block_k < L and kc * 20 > nb * block_k:
         nb += 1
+    return nb
+
+
+def key_launches(L, block_k, K):
+    """(key0, keys) of the fused path's scoring launches over one row chunk: one block of B_k
+    keys per launch while the keys seen stay below 20 (K + 512), then up to four blocks per
+    launch, spread evenly over the keys left (the slab launches)."""
+    if L <= block_k:
+        return [(0, L)]
+    nb = block_launches(L, block_k, K)
     out = [(i * block_k, min(block_k, L - i * block_k)) for i in range(nb) if i * block_k < L]
     rest = L - nb * block_k
     if rest <= 0:
@@ -160,10 +169,73 @@ def scoring_roofline(d, block_k, row_chunk, K, reps, stream, workload):
     achieved = per_launch / (avg_ms * 1e-3)
     main = max(rects, key=lambda r: r[1] * r[3])
     return {"bound": "mfma", "achieved": achieved / 1e12, "peak": FP8_PEAK / 1e12, "unit": "TFLOP/s",
-            "frac": achieved / FP8_PEAK, "traffic": load_traffic(workload, (main[1], main[3])),
+            "frac": achieved / FP8_PEAK, "traffic": load_traffic(workload, "block", (main[1], main[3])),
             "kernel": f"logits_kernel (scoring, {'MXFP4' if d.k_fmt else 'fp8'} keys, H={d.H}, key-block store)",
             "avg_launch_ms": avg_ms, "launches_per_pass": len(rects), "flop_per_launch": per_launch,
             "rect_rows_keys": [main[1], main[3]]}
+
+
+KEY_SHIFT_ALIGN = 256   # a row chunk's launches start at its first window key, rounded down to this
+
+
+def chunk_shifts(d, Tc):
+    """First window key of each row chunk, rounded down to KEY_SHIFT_ALIGN (the fused path shifts
+    the chunk's key launches by it on the device)."""
+    ks = torch.clamp(d.ks.to(torch.int64), min=0).cpu()
+    ke = torch.clamp(d.ke.to(torch.int64), max=d.L).cpu()
+    out = []
+    for r0 in range(0, d.T, Tc):
+        lo, hi = ks[r0:r0 + Tc], ke[r0:r0 + Tc]
+        live = lo[hi > lo]
+        out.append(int(live.min()) // KEY_SHIFT_ALIGN * KEY_SHIFT_ALIGN if live.numel() else 0)
+    return out
+
+
+def fused_launch_roofline(step, d, row_chunk, n_steps, stream, workload):
+    """The fused step's scoring launches, timed by the library's launch-timing record (two HIP
+    events on the step's stream around each launch, both dispatches of its pair) over n_steps
+    steps.  The launch kind that takes the most time gives the roofline: algorithmic fp8 FLOPs
+    per launch (2 H D per in-window (row, key) pair of its rectangle) / its mean duration."""
+    torch.cuda.synchronize()
+    idx.idx_launch_timing(True)
+    try:
+        for _ in range(n_steps):
+            step()
+        torch.cuda.synchronize()
+        rec = idx.idx_launch_timing_read()
+    finally:
+        idx.idx_launch_timing(False)
+    Tc = d.T if row_chunk <= 0 else min(row_chunk, d.T)
+    shift = chunk_shifts(d, Tc)
+    groups = {}
+    for e in rec:
+        assert e["ms"] > 0, e
+        kind = e["mode"] + (" (flagged rows)" if e["flagged"] else "")
+        sh = shift[e["row0"] // Tc]
+        lo, hi = min(d.L, e["key0"] + sh), min(d.L, e["key0"] + e["nkeys"] + sh)
+        g = groups.setdefault(kind, {"n": 0, "ms": 0.0, "flop": 0, "keys": 0, "rows": 0})
+        g["n"] += 1
+        g["ms"] += e["ms"]
+        if not e["flagged"]:   # a flagged-rows pass scores only the row blocks the slab check flagged
+            g["flop"] += 2 * d.H * 128 * rect_pairs(d, e["row0"], e["nrows"], lo, hi - lo)
+        g["keys"] = max(g["keys"], e["nkeys"])
+        g["rows"] = max(g["rows"], e["nrows"])
+    main = max((k for k in groups if "flagged" not in k), key=lambda k: groups[k]["ms"])
+    g = groups[main]
+    avg_ms = g["ms"] / g["n"]
+    per_launch = g["flop"] / g["n"]
+    achieved = per_launch / (avg_ms * 1e-3)
+    what = {"slab": "candidate-slab launches", "block": "key-block launches"}.get(main, main + " launches")
+    others = {k: {"launches_per_step": v["n"] / n_steps, "mean_ms": v["ms"] / v["n"],
+                  "tflops": v["flop"] / (v["ms"] * 1e-3) / 1e12 if "flagged" not in k else None}
+              for k, v in groups.items() if k != main}
+    return {"bound": "mfma", "achieved": achieved / 1e12, "peak": FP8_PEAK / 1e12, "unit": "TFLOP/s",
+            "frac": achieved / FP8_PEAK, "traffic": load_traffic(workload, main, (g["rows"], g["keys"])),
+            "kernel": f"logits_kernel (scoring, {'MXFP4' if d.k_fmt else 'fp8'} keys, H={d.H}, {what} of the fused step)",
+            "launch_mode": main, "avg_launch_ms": avg_ms, "launches_per_step": g["n"] / n_steps,
+            "flop_per_launch": per_launch, "rect_rows_keys": [g["rows"], g["keys"]],
+            "timing": f"library launch-timing record over {n_steps} fused steps after the timed ones",
+            "other_launches": others}
 
 
 def fused_step(d, K, block_k, row_chunk, cu_q, cu_k, stream):
@@ -235,10 +307,14 @@ def workload(name, dev, stream, steps, warmup, roof_reps):
     log(f"[bench] {name}: fused step {ms:.4f} ms -> {line['pairs_per_s']:.4e} pairs/s, {line['tflops']:.0f} TFLOP/s "
         f"({100 * line['fp8_peak_frac_step']:.1f}% of fp8 peak at step level), workspace {ws.numel() / 2**20:.0f} MiB")
     if roof_reps:
-        line["roofline"] = scoring_roofline(d, Bk, rc, K, roof_reps, stream, name)
+        line["roofline"] = fused_launch_roofline(step, d, rc, 3, stream, name)
         r = line["roofline"]
-        log(f"[bench] {name}: scoring kernel {r['avg_launch_ms']:.4f} ms/launch -> {r['achieved']:.1f} TFLOP/s "
-            f"({100 * r['frac']:.1f}% of fp8 peak)")
+        log(f"[bench] {name}: scoring kernel, {r['launch_mode']} launches of the fused step, {r['avg_launch_ms']:.4f} "
+            f"ms/launch -> {r['achieved']:.1f} TFLOP/s ({100 * r['frac']:.1f}% of fp8 peak)")
+        line["scoring_block_store"] = scoring_roofline(d, Bk, rc, K, roof_reps, stream, name)
+        r = line["scoring_block_store"]
+        log(f"[bench] {name}: scoring kernel, key-block store over the step's rectangles, {r['avg_launch_ms']:.4f} "
+            f"ms/launch -> {r['achieved']:.1f} TFLOP/s ({100 * r['frac']:.1f}% of fp8 peak)")
     return p, d, line, (oi, ov, ws)
 
 
@@ -309,6 +385,9 @@ COPY_BYTES = 256 << 20   # calibration copy of the traffic probe
 # (each workgroup works in one of them); these prefixes name both.
 PROBE = {"glm_chunk": "logits_kernel<0, 32, 1, 4, ", "long_ctx": "logits_kernel<0, 64, 1, 4, ",
          "dsv4_mxfp4": "logits_kernel<1, 64, 1, 4, "}
+# the candidate-slab launches of the fused calls the probe makes (every slab launch of the call)
+SLAB_PROBE = {"long_ctx": "logits_kernel<0, 64, 4, 4, ", "dsv4_mxfp4": "logits_kernel<1, 64, 4, 4, "}
+PROBE_CALLS = ("glm_chunk fused", "ragged_cand candidates", "long_ctx fused", "dsv4_mxfp4 fused")
 MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_MFMA",
                  "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "GRBM_COUNT")
 
@@ -319,11 +398,12 @@ def launch_pairs(values):
 
 
 def traffic_probe(dev):
-    """Launches for a rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE run: one fused glm_chunk call and the
-    ragged workload's candidate source (the selection, refinement, pooling and mask kernels), then
-    the scoring kernel on the glm_chunk and long_ctx launch rectangles (as the fused path launches
-    them) twice each, then two device-to-device copies of COPY_BYTES that calibrate what those
-    counters read for a known number of bytes."""
+    """Launches for a rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE run: one fused glm_chunk call, the
+    ragged workload's candidate source (the selection, refinement, pooling and mask kernels), one
+    fused long_ctx call and one fused dsv4_mxfp4 call (their candidate-slab launches), then the
+    scoring kernel on the glm_chunk, long_ctx and dsv4_mxfp4 key-block rectangles (as the fused
+    path launches them) twice each, then two device-to-device copies of COPY_BYTES that calibrate
+    what those counters read for a known number of bytes."""
     p = synth.make_config("glm_chunk")
     d = idx.Inputs.from_host(p, device=dev)
     idx.idx_logits_topk_fused(d, p.meta["K"], block_k=p.meta["block_k"])
@@ -336,6 +416,14 @@ def traffic_probe(dev):
     torch.cuda.synchronize()
     del d5, blocks5
     torch.cuda.empty_cache()
+    for name in SLAB_PROBE:
+        pw = synth.make_config(name)
+        dw = idx.Inputs.from_host(pw, device=dev)
+        idx.idx_logits_topk_fused(dw, pw.meta["K"], block_k=pw.meta["block_k"], row_chunk=ROW_CHUNK[name])
+        torch.cuda.synchronize()
+        del dw
+        torch.cuda.empty_cache()
+        log(f"[bench] traffic probe: {name} fused call")
     for name in PROBE:
         pw = p if name == "glm_chunk" else synth.make_config(name)
         dw = d if name == "glm_chunk" else idx.Inputs.from_host(pw, device=dev)
@@ -382,39 +470,50 @@ def traffic_summary(fetch_dir, write_dir):
             allrec = json.load(f)
     except (OSError, ValueError):
         allrec = {}
-    print("| workload | launch (rows x keys) | FETCH_SIZE factor | WRITE_SIZE factor | fetched MiB per launch | "
-          "written MiB per launch | HBM MiB per launch |")
-    print("|---|---|---|---|---|---|---|")
-    for name, kname in PROBE.items():
-        f = launch_pairs([v * factor["FETCH_SIZE"] for n, v, _, _ in rows["FETCH_SIZE"] if kname in n])[-2:]
-        w = launch_pairs([v * factor["WRITE_SIZE"] for n, v, _, _ in rows["WRITE_SIZE"] if kname in n])[-2:]
+    print("| workload | launches | rows x keys | FETCH_SIZE factor | WRITE_SIZE factor | fetched MiB per launch | "
+          "written MiB per launch | HBM MiB per launch (mean) |")
+    print("|---|---|---|---|---|---|---|---|")
+    allrec = {k: v for k, v in allrec.items() if "/" in k}   # entries keyed workload/mode only
+    cases = [(name, "block", kname, 2) for name, kname in PROBE.items()] + \
+            [(name, "slab", kname, None) for name, kname in SLAB_PROBE.items()]
+    for name, mode, kname, last in cases:
+        f = launch_pairs([v * factor["FETCH_SIZE"] for n, v, _, _ in rows["FETCH_SIZE"] if kname in n])
+        w = launch_pairs([v * factor["WRITE_SIZE"] for n, v, _, _ in rows["WRITE_SIZE"] if kname in n])
+        if last:
+            f, w = f[-last:], w[-last:]
         p = synth.make_config(name)
         Tc = p.T if ROW_CHUNK[name] <= 0 else min(ROW_CHUNK[name], p.T)
-        rect = [Tc, max(nk for _, nk in key_launches(p.L, p.meta["block_k"], p.meta["K"]))]
+        kl = key_launches(p.L, p.meta["block_k"], p.meta["K"])
+        nb = block_launches(p.L, p.meta["block_k"], p.meta["K"])
+        rect = [Tc, max(nk for _, nk in (kl if mode == "block" else kl[nb:]))]
         rec = {"kernel_source_hash": kernel_source_hash(), "rect": rect,
                "bytes_per_launch": float(np.mean(f) + np.mean(w)), "fetch_bytes_per_launch": float(np.mean(f)),
                "write_bytes_per_launch": float(np.mean(w)), "fetch_factor": factor["FETCH_SIZE"],
                "write_factor": factor["WRITE_SIZE"], "launches": len(f)}
-        allrec[name] = rec
-        print(f"| {name} | {rect[0]} x {rect[1]} | {factor['FETCH_SIZE']:.4f} | {factor['WRITE_SIZE']:.4f} | "
-              + ", ".join(f"{x / 2**20:.1f}" for x in f) + " | " + ", ".join(f"{x / 2**20:.1f}" for x in w)
-              + f" | {rec['bytes_per_launch'] / 2**20:.1f} |")
+        allrec[f"{name}/{mode}"] = rec
+        fs = ", ".join(f"{x / 2**20:.1f}" for x in f) if len(f) <= 4 else \
+            f"{min(f) / 2**20:.1f}-{max(f) / 2**20:.1f} ({len(f)} launches)"
+        ws_ = ", ".join(f"{x / 2**20:.1f}" for x in w) if len(w) <= 4 else \
+            f"{min(w) / 2**20:.1f}-{max(w) / 2**20:.1f} ({len(w)} launches)"
+        print(f"| {name} | {mode} | {rect[0]} x {rect[1]} | {factor['FETCH_SIZE']:.4f} | {factor['WRITE_SIZE']:.4f} | "
+              f"{fs} | {ws_} | {rec['bytes_per_launch'] / 2**20:.1f} |")
     with open(path, "w") as fo:
         json.dump(allrec, fo, indent=1)
     print(f"\nKernel source hash {kernel_source_hash()}.")
     # the other kernels of the probe: bytes per dispatch and the rate over its (profiled) duration
     groups = {}
-    wl = "glm_chunk fused"
     nkb = 0
-    for (n, fv, t0, t1), (_, wv, _, _) in zip(rows["FETCH_SIZE"], rows["WRITE_SIZE"]):
+    # the fused calls and the candidate source end with their last refinement; the key-block
+    # rectangles and the copies follow
+    last_ref = max(i for i, (n, _, _, _) in enumerate(rows["FETCH_SIZE"]) if "refine_kernel" in n)
+    for i, ((n, fv, t0, t1), (_, wv, _, _)) in enumerate(zip(rows["FETCH_SIZE"], rows["WRITE_SIZE"])):
+        if i > last_ref:
+            break
         m = re.search(r"namespace\)::(\w+(?:<[^>]*>)?)", n)
         name = m.group(1) if m else n.split("(")[0]
         if name.startswith("key_bound_kernel"):
             nkb += 1
-            if nkb == 2:
-                wl = "ragged_cand candidates"
-        if "copyBuffer" in n or any(k in n for k in PROBE.values()) and wl != "glm_chunk fused":
-            continue
+        wl = PROBE_CALLS[min(max(nkb, 1), len(PROBE_CALLS)) - 1]
         if not (n.startswith("void idx") or n.startswith("idx::")):
             continue
         g = groups.setdefault((wl, name), [0, 0.0, 0.0, 0.0])
@@ -431,7 +530,8 @@ def traffic_summary(fetch_dir, write_dir):
 
 def mfma_summary(pmc_dir):
     """Markdown summary of a traffic-probe run under rocprofv3 --pmc with MFMA_COUNTERS: for the
-    last two scoring launches of each probed workload, the issued MFMA work, MFMA-busy cycles,
+    last two key-block and candidate-slab scoring launches of each probed workload, the issued
+    MFMA work, MFMA-busy cycles,
     VALU instructions and the shader clock (GRBM_COUNT over the dispatch's duration, 8 XCDs)."""
     import csv
     acc = {}
@@ -442,15 +542,17 @@ def mfma_summary(pmc_dir):
     disp = [acc[k] for k in sorted(acc)]
     cols = ("SQ_INSTS_MFMA", "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_VALU_MFMA_BUSY_CYCLES",
             "SQ_INSTS_VALU", "GRBM_COUNT")
-    print("| workload | form | duration us | " + " | ".join(cols) + " | clock GHz | MFMA busy | VALU per MFMA |")
-    print("|---|---|---|" + "---|" * (len(cols) + 3))
-    for name, kname in PROBE.items():
+    print("| workload | launches | form | duration us | " + " | ".join(cols) + " | clock GHz | MFMA busy | VALU per MFMA |")
+    print("|---|---|---|---|" + "---|" * (len(cols) + 3))
+    cases = [(name, "block", kname) for name, kname in PROBE.items()] + \
+            [(name, "slab", kname) for name, kname in SLAB_PROBE.items()]
+    for name, mode, kname in cases:
         ds = [e for e in disp if kname in e["name"]][-4:]
         for e in ds:
             cyc = e.get("GRBM_COUNT", 0.0) / 8.0                      # per XCD
             busy = e.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / 1024.0    # per SIMD
             form = "f16" if "true>" in e["name"] else "fp32"
-            print(f"| {name} | {form} | {e['t'] * 1e6:.1f} | " + " | ".join(f"{e.get(c, 0.0):.4g}" for c in cols)
+            print(f"| {name} | {mode} | {form} | {e['t'] * 1e6:.1f} | " + " | ".join(f"{e.get(c, 0.0):.4g}" for c in cols)
                   + f" | {cyc / e['t'] / 1e9 if e['t'] > 0 else 0:.2f} | {busy / cyc if cyc else 0:.3f} | "
                   f"{e.get('SQ_INSTS_VALU', 0.0) / max(1.0, e.get('SQ_INSTS_MFMA', 0.0)):.2f} |")
 
@@ -461,10 +563,11 @@ def _short_kernel(n):
     return m.group(1) if m else n.split("(")[0][:48]
 
 
-def trace_summary(trace_dir, scoring="logits_kernel<0, 64, 1, 4, "):
+def trace_summary(trace_dir, slab="logits_kernel<0, 64, 4, 4, ", scoring="logits_kernel<0, 64, 1, 4, "):
     """Markdown summary of a rocprofv3 --kernel-trace run of the default headline bench: each
-    fused step (from its window kernel to its last refinement) by kernel, then the roofline's
-    block-store scoring launches, each the pair (f16 form, fp32 form) of dispatches."""
+    fused step (from its window kernel to its last refinement) by kernel, the fused steps'
+    candidate-slab launches (the roofline's launches), then the block-store scoring launches
+    over the step's rectangles; a launch is the pair (f16 form, fp32 form) of dispatches."""
     import csv
     rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
@@ -500,6 +603,13 @@ def trace_summary(trace_dir, scoring="logits_kernel<0, 64, 1, 4, "):
         busy = [sum(b - a for _, a, b in st) / 1e3 for st in steps]
         print("\nstep spans (us): " + ", ".join(f"{x:.0f}" for x in spans)
               + "; kernel time per step (us): " + ", ".join(f"{x:.0f}" for x in busy))
+        sp = [(st[j + 1][2] - st[j][1]) / 1e3 for st in steps for j in range(len(st) - 1)
+              if st[j][0] == slab + "true>" and st[j + 1][0] == slab + "false>"]
+        f16 = [(b - a) / 1e3 for st in steps for n, a, b in st if n == slab + "true>"]
+        if sp:
+            print(f"\nslab launches of the fused steps: {len(sp)} launches of `{slab}...>`: f16 form mean "
+                  f"{np.mean(f16):.1f} us, launch (first start to second end) mean {np.mean(sp):.1f} us, "
+                  f"median {np.median(sp):.1f} us")
     # roofline: runs of consecutive block-store scoring dispatches
     runs, cur = [], []
     for n, a, b in ev:
@@ -516,7 +626,7 @@ def trace_summary(trace_dir, scoring="logits_kernel<0, 64, 1, 4, "):
         f32 = [(b - a) / 1e3 for n, a, b in r if n.endswith("false>")]
         pairs = [(r[j + 1][2] - r[j][1]) / 1e3 for j in range(0, len(r) - 1, 2)
                  if r[j][0].endswith("true>") and r[j + 1][0].endswith("false>")]
-        print(f"\nroofline run: {len(pairs)} launches of `{scoring}...>`: f16 form mean {np.mean(f16):.1f} us "
+        print(f"\nblock-store run: {len(pairs)} launches of `{scoring}...>`: f16 form mean {np.mean(f16):.1f} us "
               f"(median {np.median(f16):.1f}), fp32 form mean {np.mean(f32):.1f} us, launch (first start to "
               f"second end) mean {np.mean(pairs):.1f} us, median {np.median(pairs):.1f} us")
 

@@ -313,6 +313,39 @@ idx_status idx_gather_rows(const idx_problem *p, const int32_t *rows, int32_t R,
  * fewer than n rows.  cu_q: device int32 [B + 1]; rows: device int32 [B * n]. */
 idx_status idx_tail_rows(const int32_t *cu_q, int32_t B, int32_t n, int32_t *rows, void *stream);
 
+/* Launch timing, for benchmarks and profilers (P3: the chunk-budget and CPU-gap
+ * commits attribute the indexer's time to its kernels).  idx_launch_timing(1) clears
+ * the record and starts recording on the current device: from then on each scoring
+ * launch of idx_mqa_logits, idx_mqa_logits_block, the fused entries and
+ * idx_block_candidates (both dispatches of a launch pair, or the exact kernel under
+ * IDX_EXACT) is bracketed by two HIP events on its call's stream.  At most
+ * IDX_TIMING_MAX launches are recorded; launches on another device or on a stream under
+ * capture are not.  idx_launch_timing(0) stops recording and keeps the record.
+ * idx_launch_timing_read waits for the recorded events, writes the first min(cap, *n)
+ * entries to out (host memory) in launch order, sets *n to the number recorded, and
+ * clears the record.  An entry whose launch failed has ms < 0.  Events are created at
+ * the first idx_launch_timing(1) on a device (IDX_E_LAUNCH if that fails) and kept until
+ * the process ends or another device starts a record.  One record per process, guarded
+ * by a lock: launches of calls that overlap on several host threads interleave in it. */
+#define IDX_TIMING_MAX 1024
+enum {
+  IDX_LAUNCH_DENSE = 0, /* dense row-relative logits (idx_mqa_logits)                  */
+  IDX_LAUNCH_BLOCK = 1, /* scores of a key rectangle (block launches of the fused path) */
+  IDX_LAUNCH_POOL8 = 2, /* pooled 8-key blocks (the fused candidate source)             */
+  IDX_LAUNCH_SLAB = 4   /* only the scores above each row's running threshold, to its
+                           candidate slabs (the fused path's later launches)           */
+};
+typedef struct idx_launch_time {
+  float ms;        /* first event to second event; < 0: the launch failed             */
+  int32_t mode;    /* IDX_LAUNCH_*                                                    */
+  int32_t flagged; /* 1: a pass over the row blocks whose slabs overflowed only       */
+  int32_t row0, nrows; /* the launch's rows                                           */
+  int32_t key0, nkeys; /* its keys; in the fused entries before the row chunk's shift
+                          to its first window key                                     */
+} idx_launch_time;
+idx_status idx_launch_timing(int32_t enable);
+idx_status idx_launch_timing_read(idx_launch_time *out, int32_t cap, int32_t *n);
+
 /* Static description of a status code. */
 const char *idx_status_str(idx_status s);
 

@@ -37,13 +37,22 @@ EXPORTS = ("idx_mqa_logits", "idx_mqa_logits_block", "idx_topk", "idx_logits_top
            "idx_logits_topk_fused_paged", "idx_logits_topk_fused_blocks", "idx_logits_topk_fused_static",
            "idx_refine_topk",
            "idx_block_candidates", "idx_workspace_size", "idx_ragged_windows", "idx_ragged_windows_ratio",
-           "idx_gather_rows", "idx_tail_rows", "idx_status_str")
+           "idx_gather_rows", "idx_tail_rows", "idx_launch_timing", "idx_launch_timing_read", "idx_status_str")
+
+IDX_TIMING_MAX = 1024
+LAUNCH_MODES = {0: "dense", 1: "block", 2: "pool8", 4: "slab"}
 
 
 class IdxError(RuntimeError):
     def __init__(self, fn: str, status: int):
         self.status = status
         super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({status_str(status)})")
+
+
+class idx_launch_time(ctypes.Structure):
+    _fields_ = [("ms", ctypes.c_float), ("mode", ctypes.c_int32), ("flagged", ctypes.c_int32),
+                ("row0", ctypes.c_int32), ("nrows", ctypes.c_int32), ("key0", ctypes.c_int32),
+                ("nkeys", ctypes.c_int32)]
 
 
 class idx_problem(ctypes.Structure):
@@ -80,6 +89,8 @@ def load_library():
     lib.idx_ragged_windows_ratio.argtypes = [VP, VP, VP, i32, i32, i32, VP, VP, VP]
     lib.idx_gather_rows.argtypes = [P, VP, i32, P, VP, sz, VP]
     lib.idx_tail_rows.argtypes = [VP, i32, i32, VP, VP]
+    lib.idx_launch_timing.argtypes = [i32]
+    lib.idx_launch_timing_read.argtypes = [ctypes.POINTER(idx_launch_time), i32, ctypes.POINTER(i32)]
     lib.idx_status_str.argtypes = [i32]
     lib.idx_status_str.restype = ctypes.c_char_p
     for name in EXPORTS:
@@ -405,6 +416,21 @@ def idx_tail_rows(cu_q: torch.Tensor, n: int, stream=None) -> torch.Tensor:
     rows = torch.empty(B * n, dtype=torch.int32, device=cu_q.device)
     _check("idx_tail_rows", load_library().idx_tail_rows(_ptr(cu_q), B, n, _ptr(rows), _stream(stream)))
     return rows
+
+
+def idx_launch_timing(enable: bool) -> None:
+    """Start (clearing the record) or stop recording the scoring launches' HIP event times."""
+    _check("idx_launch_timing", load_library().idx_launch_timing(1 if enable else 0))
+
+
+def idx_launch_timing_read() -> list:
+    """The recorded launches, in launch order, as dicts (ms < 0: the launch failed); clears the
+    record."""
+    buf = (idx_launch_time * IDX_TIMING_MAX)()
+    n = ctypes.c_int32()
+    _check("idx_launch_timing_read", load_library().idx_launch_timing_read(buf, IDX_TIMING_MAX, ctypes.byref(n)))
+    return [{"ms": e.ms, "mode": LAUNCH_MODES.get(e.mode, e.mode), "flagged": bool(e.flagged), "row0": e.row0,
+             "nrows": e.nrows, "key0": e.key0, "nkeys": e.nkeys} for e in buf[:min(n.value, IDX_TIMING_MAX)]]
 
 
 def idx_status_str(status: int) -> str:

@@ -99,8 +99,18 @@ idx::LogitsArgs logits_args(const idx_problem *p, int32_t row0, int32_t nrows, i
 }
 
 // A scoring launch on the fp8 MFMA, or the exact fp64 kernel when `exact` (IDX_EXACT).
-hipError_t score(const idx::LogitsArgs &a, const idx_problem *p, int mode, bool exact, hipStream_t s) {
-  return exact ? idx::launch_logits_exact(a, p->k_fmt, p->H, mode, s) : idx::launch_logits(a, p->k_fmt, p->H, mode, s);
+// One scoring launch (exact: the fp64 kernel), timed when a launch-timing record is on.
+// flagged: a pass over the row blocks the slab check flagged.
+hipError_t score(const idx::LogitsArgs &a, const idx_problem *p, int mode, bool exact, hipStream_t s,
+                 bool flagged = false) {
+  static_assert(IDX_LAUNCH_DENSE == idx::STORE_DENSE && IDX_LAUNCH_BLOCK == idx::STORE_BLOCK &&
+                    IDX_LAUNCH_POOL8 == idx::STORE_POOL8 && IDX_LAUNCH_SLAB == idx::STORE_SLAB,
+                "launch-timing modes name the scoring modes");
+  const int slot = idx::timing_begin(s);
+  const hipError_t e =
+      exact ? idx::launch_logits_exact(a, p->k_fmt, p->H, mode, s) : idx::launch_logits(a, p->k_fmt, p->H, mode, s);
+  idx::timing_end(slot, s, e == hipSuccess, mode, flagged ? 1 : 0, a.row0, a.nrows, a.key_lo, a.key_hi - a.key_lo);
+  return e;
 }
 
 idx_status launched(hipError_t e) { return e == hipSuccess ? IDX_OK : IDX_E_LAUNCH; }
@@ -524,7 +534,7 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
         c.cand_ld = sld / 2;
         c.ccnt = ccnt;
         c.caps = CAPS;
-        if ((st = launched(idx::launch_logits(c, p->k_fmt, p->H, idx::STORE_SLAB, s)))) return st;
+        if ((st = launched(score(c, p, idx::STORE_SLAB, false, s)))) return st;
         const int32_t rpw = idx::logits_rows_per_workgroup(p->H);
         if ((st = launched(
                  idx::launch_slab_check(ccnt, a.nsplit * idx::CAND_PARTS, thr, nr, rpw, ovf, a.by_row, s))))
@@ -535,7 +545,7 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
           f.by_row = a.by_row;
           f.kshift = kshift;
           f.only_flagged = ovf;
-          if ((st = launched(idx::launch_logits(f, p->k_fmt, p->H, idx::STORE_BLOCK, s)))) return st;
+          if ((st = launched(score(f, p, idx::STORE_BLOCK, false, s, true)))) return st;
           idx::TopkArgs bh = b;
           if (h0 == 0) {   // slab merges, and the first block's columns for the other rows
             bh.cand = slab;

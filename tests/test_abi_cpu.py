@@ -226,3 +226,15 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         idx.load_library()
     with pytest.raises(ImportError, match="not built"):
         idx.idx_status_str(0)
+
+
+def test_launch_timing_host_checks(lib):
+    """The timing read-out checks its arguments on the host; an empty record reads as 0
+    launches, and stopping a record that never started is a no-op (no device is touched)."""
+    n = ctypes.c_int32(-5)
+    assert lib.idx_launch_timing_read(None, 0, None) == 1          # NULL count
+    assert lib.idx_launch_timing_read(None, 4, ctypes.byref(n)) == 1   # NULL output with cap > 0
+    assert lib.idx_launch_timing_read(None, -1, ctypes.byref(n)) == 3  # PARAM
+    assert lib.idx_launch_timing(0) == 0
+    assert lib.idx_launch_timing_read(None, 0, ctypes.byref(n)) == 0 and n.value == 0
+    assert ctypes.sizeof(idx.idx_launch_time) == 28
