@@ -443,10 +443,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(!F16 &&
     if (ntiles > 1) vm_wait_barrier<LPT>();
     else vm_wait_barrier<0>();
 
+    // B operand of key group q = 4 b + j of a stage: LDS row p = 16 q + n16 holds key 64 b + 4 n16 + j
+    auto load_bk = [&](int buf, int q) __attribute__((always_inline)) -> v8i {
+      const int p = q * 16 + n16;
+      if (KF == 0) {
+        const int sw = swz8(p);
+        const v4i lo = *(const v4i *)&kbuf[buf][p * 128 + ((g ^ sw) << 4)];
+        const v4i hi = *(const v4i *)&kbuf[buf][p * 128 + (((4 + g) ^ sw) << 4)];
+        return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      } else {
+        const v4i v = *(const v4i *)&kbuf[buf][p * 64 + ((g ^ swz4(p)) << 4)];
+        return (v8i){v.x, v.y, v.z, v.w, 0, 0, 0, 0};
+      }
+    };
     for (int it = 0; it < ntiles; ++it) {
       const int buf = it % 3;
       if (it + 2 < ntiles) request(it + 2, (it + 2) % 3);  // its buffer was last read in iteration it - 1
       const int ts = tile0 + it * TK;
+      // f16 form: each key group's B operand is read from LDS while the group before it is
+      // multiplied (the fp32 form, short of registers, reads it just before use)
+      v8i bk_next = {};
+      if constexpr (F16) bk_next = load_bk(buf, 0);
   #pragma unroll
       for (int b = 0; b < TK / 64; ++b) {
         const int s0 = ts + 64 * b + 4 * n16;                       // this lane's first key
@@ -456,19 +473,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(!F16 &&
         (void)ebk;
   #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int p = (4 * b + j) * 16 + n16;   // LDS row of key s0 + j
           v8i bk;
-          int bscale = 0;
-          if (KF == 0) {
-            const int sw = swz8(p);
-            const v4i lo = *(const v4i *)&kbuf[buf][p * 128 + ((g ^ sw) << 4)];
-            const v4i hi = *(const v4i *)&kbuf[buf][p * 128 + (((4 + g) ^ sw) << 4)];
-            bk = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          if constexpr (F16) {
+            bk = bk_next;
+            if (4 * b + j + 1 < TK / 16) bk_next = load_bk(buf, 4 * b + j + 1);
           } else {
-            const v4i v = *(const v4i *)&kbuf[buf][p * 64 + ((g ^ swz4(p)) << 4)];
-            bk = (v8i){v.x, v.y, v.z, v.w, 0, 0, 0, 0};
-            bscale = (sc[j] >> (8 * g)) & 0xFF;
+            bk = load_bk(buf, 4 * b + j);
           }
+          int bscale = KF == 0 ? 0 : (sc[j] >> (8 * g)) & 0xFF;
           v4f c[NT];
           if constexpr (F16) {
             // every term scaled by 2^-SA into [-1, 1]; an MXFP4 key's block scales relative to its
