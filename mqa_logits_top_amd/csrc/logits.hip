@@ -456,12 +456,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(!F16 &&
         return (v8i){v.x, v.y, v.z, v.w, 0, 0, 0, 0};
       }
     };
+    // f16 form: each key group's B operand is read from LDS while the group before it is
+    // multiplied (the fp32 form, short of registers, reads it just before use)
     for (int it = 0; it < ntiles; ++it) {
       const int buf = it % 3;
       if (it + 2 < ntiles) request(it + 2, (it + 2) % 3);  // its buffer was last read in iteration it - 1
       const int ts = tile0 + it * TK;
-      // f16 form: each key group's B operand is read from LDS while the group before it is
-      // multiplied (the fp32 form, short of registers, reads it just before use)
       v8i bk_next = {};
       if constexpr (F16) bk_next = load_bk(buf, 0);
   #pragma unroll
@@ -539,7 +539,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(!F16 &&
           for (int j = 0; j < 4; ++j) val[j] *= __int_as_float(sc[j]);
         }
         if (cand) {
-          // values above the row's running threshold also go to its slab, in key order
+          // values above the row's running threshold go to its slab, in key order
           uint32_t pm = 0;
           if constexpr (KF == 0) {
             // the lane's keys s0 .. s0 + 3 inside its row's window and range as one mask per batch
