@@ -223,6 +223,44 @@ def test_fused_slab_launch_mixed_fallback(Bk):
     assert not ((sel[:8] >= lo) & (sel[:8] < hi)).any()
 
 
+@pytest.mark.parametrize("H,k_fmt", [(64, synth.K_FP8), (32, synth.K_MXFP4)])
+def test_fused_slab_launch_negative_weights(H, k_fmt):
+    """Slab launches served by the fp32 scoring form: rows 0..31 have head weights of both signs
+    (U(-0.5, 1)), rows 32..47 non-negative ones (the f16 form).  With K + 512 = 576 and B_k =
+    8192, keys 0..16384 go in two block launches and keys 16384..40000 in one slab launch.  Keys
+    16384..20480 are made non-negative and scaled x64 and rows 0..15 get non-negative q, so
+    those rows' slabs overflow and their row blocks are scored again, in the fp32 form, one
+    block per pass; rows 16..31 fit their slabs.  Selected sets equal the oracle's, and the
+    fused call equals dense logits + top-(K + 512) + refinement bitwise (both paths give a row
+    the same scoring form)."""
+    T, L, K, Bk = 48, 40000, 64, 8192
+    lo, hi = 16384, 20480
+    p = synth.make_problem(T, L, H, k_fmt=k_fmt, seed=23, w_lo=-0.5)
+    p.w[32:] = np.abs(p.w[32:])
+    if k_fmt == synth.K_FP8:
+        p.k[lo:hi] &= 0x7F
+        p.k_scale[lo:hi] *= 64.0
+    else:
+        p.k[lo:hi] &= 0x77                       # both nibbles' sign bits
+        p.k_scale[lo:hi] = np.minimum(p.k_scale[lo:hi].astype(np.int32) + 6, 254).astype(np.uint8)
+    p.q[0:16] &= 0x7F
+    assert (p.w[:32] < 0).any(axis=1).all(), "every mixed row has a negative weight"
+    dq = oracle.Dequantised(p)
+    o = oracle.rows_logits(dq, range(T))
+    d = dev(p)
+    fi, fv = idx.idx_logits_topk_fused(d, K, block_k=Bk)
+    topk_ok(fi.cpu().numpy(), None, o, dq.ks, K)
+    topk_ok(fi[32:].cpu().numpy(), fv[32:].cpu().numpy(), o[32:], dq.ks[32:], K)   # f16-form rows: values too
+    lg = idx.idx_mqa_logits(d, d.W)
+    ci, cv = idx.idx_topk(lg, d.ks, d.ke, idx.candidate_capacity(K))
+    di, dv = idx.idx_refine_topk(d, ci, cv, K)
+    assert torch.equal(di, fi)
+    assert torch.equal(dv.view(torch.int32), fv.view(torch.int32))
+    # the scaled keys reach the lists of rows 0..15 (their slabs overflowed)
+    sel = fi[:16].cpu().numpy()
+    assert ((sel >= lo) & (sel < hi)).sum() > 16 * K // 2
+
+
 @pytest.mark.parametrize("row_chunk", [0, 16])
 def test_fused_paged_transform(case, row_chunk):
     """Index -> KV-slot transform in the final write: out_slot = slot_of_key[out_idx], -1 pads;
