@@ -1,0 +1,63 @@
+"""A seeded sweep of fused-indexer configurations against the oracle.  Each case draws T, L,
+H, the key format, K (up to the largest, 2048), B_k, the row chunk, the window layout (causal,
+random with empty windows, or a ragged batch of requests on prefixes) and the range of the
+head weights (non-negative, or of both signs).  The selected sets must equal the oracle's,
+and the selected values too where every head weight is >= 0.  Depending on K and B_k a case
+runs block launches only or block and slab launches, one row chunk or several.  Sizes keep
+the oracle to a few seconds per case."""
+import numpy as np
+import pytest
+
+import mqa_logits_top_amd as idx
+import oracle
+import synth
+from checks import topk_ok
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 96
+
+
+def _draw(seed):
+    rng = np.random.default_rng(7000 + seed)
+    H = int(rng.choice([32, 64]))
+    fmt = int(rng.choice([synth.K_FP8, synth.K_MXFP4]))
+    L = int(rng.integers(1, 60001))
+    T = int(rng.integers(1, min(96, max(1, 3_000_000 // L)) + 1))   # T * L <= 3e6: the oracle stays quick
+    K = int(rng.choice([1, 7, 64, 200, 512, 700, 2048]))
+    Bk = int(rng.choice([256, 512, 1024, 2048, 8192, 32768]))
+    rc = int(rng.choice([0, 8, 16, 64]))
+    layout = str(rng.choice(["causal", "random", "ragged"]))
+    w_lo = float(rng.choice([0.0, 0.0, -0.5]))
+    kw = {}
+    if layout == "random":
+        ks = rng.integers(0, L, T).astype(np.int32)
+        ke = np.minimum(ks + rng.integers(0, L + 1, T), L).astype(np.int32)
+        ke[::5] = ks[::5]   # some empty windows
+        kw = dict(ks=ks, ke=ke)
+    elif layout == "ragged":
+        B = int(rng.integers(1, 5))
+        q_len = rng.multinomial(T, np.ones(B) / B)
+        prefix = rng.integers(0, max(1, L // B) + 1, B)
+        cu_q = np.concatenate([[0], np.cumsum(q_len)]).astype(np.int32)
+        cu_k = np.concatenate([[0], np.cumsum(q_len + prefix)]).astype(np.int32)
+        L = int(cu_k[-1]) if cu_k[-1] > 0 else 1
+        kw = dict(cu_q=cu_q, cu_k=cu_k)
+    return dict(T=T, L=L, H=H, fmt=fmt, K=K, Bk=Bk, rc=rc, layout=layout, w_lo=w_lo, seed=seed, kw=kw)
+
+
+def _id(seed):
+    c = _draw(seed)
+    return (f"s{seed}-T{c['T']}-L{c['L']}-H{c['H']}-f{c['fmt']}-K{c['K']}-B{c['Bk']}-rc{c['rc']}-"
+            f"{c['layout']}-w{c['w_lo']}")
+
+
+@pytest.mark.parametrize("seed", range(N_CASES), ids=_id)
+def test_random_fused_config_against_oracle(seed):
+    c = _draw(seed)
+    p = synth.make_problem(c["T"], c["L"], c["H"], k_fmt=c["fmt"], seed=100 + seed, w_lo=c["w_lo"], **c["kw"])
+    d = idx.Inputs.from_host(p)
+    dq = oracle.Dequantised(p)
+    o = oracle.rows_logits(dq, range(c["T"]))
+    gi, gv = idx.idx_logits_topk_fused(d, c["K"], block_k=c["Bk"], row_chunk=c["rc"])
+    topk_ok(gi.cpu().numpy(), None if c["w_lo"] < 0 else gv.cpu().numpy(), o, dq.ks, c["K"])
