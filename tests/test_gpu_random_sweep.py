@@ -1,4 +1,4 @@
-"""A seeded sweep of fused-indexer configurations against the oracle.  Each case draws T, L,
+"""Seeded sweeps of fused-indexer configurations against the oracle.  Each case draws T, L,
 H, the key format, K (up to the largest, 2048), B_k, the row chunk, the window layout (causal,
 random with empty windows, or a ragged batch of requests on prefixes) and the range of the
 head weights (non-negative, or of both signs).  The selected sets must equal the oracle's,
@@ -7,6 +7,7 @@ runs block launches only or block and slab launches, one row chunk or several.  
 the oracle to a few seconds per case."""
 import numpy as np
 import pytest
+import torch
 
 import mqa_logits_top_amd as idx
 import oracle
@@ -61,3 +62,51 @@ def test_random_fused_config_against_oracle(seed):
     o = oracle.rows_logits(dq, range(c["T"]))
     gi, gv = idx.idx_logits_topk_fused(d, c["K"], block_k=c["Bk"], row_chunk=c["rc"])
     topk_ok(gi.cpu().numpy(), None if c["w_lo"] < 0 else gv.cpu().numpy(), o, dq.ks, c["K"])
+
+
+N_CAND_CASES = 48
+
+
+def _draw_cand(seed):
+    c = _draw(500 + seed)
+    rng = np.random.default_rng(9000 + seed)
+    c["n_blocks"] = int(rng.choice([1, 5, 64, 512, 2048]))
+    c["K"] = int(rng.choice([1, 64, 512, 2048]))
+    return c
+
+
+def _id_cand(seed):
+    c = _draw_cand(seed)
+    return (f"s{seed}-T{c['T']}-L{c['L']}-H{c['H']}-f{c['fmt']}-nb{c['n_blocks']}-K{c['K']}-B{c['Bk']}-"
+            f"rc{c['rc']}-{c['layout']}-w{c['w_lo']}")
+
+
+@pytest.mark.parametrize("seed", range(N_CAND_CASES), ids=_id_cand)
+def test_random_candidate_source_and_consumers_against_oracle(seed):
+    """The fused candidate source (8-key blocks from each row's ks, top-n_blocks, mask and block
+    ids) against the oracle's block selection; then a consumer layer over the same keys
+    restricted to the mask (selected sets equal the oracle's on the allowed keys) and the same
+    consumer given the block ids (bitwise the mask consumer's result)."""
+    from test_gpu_parity import _check_candidates
+
+    c = _draw_cand(seed)
+    p = synth.make_problem(c["T"], c["L"], c["H"], k_fmt=c["fmt"], seed=300 + seed, w_lo=c["w_lo"], **c["kw"])
+    d = idx.Inputs.from_host(p)
+    dq = oracle.Dequantised(p)
+    o = oracle.rows_logits(dq, range(c["T"]))
+    W = max(d.W, 1)
+    nb = c["n_blocks"]
+    blocks = torch.empty((c["T"], nb), dtype=torch.int32, device="cuda")
+    mask, _ = idx.idx_block_candidates(d, W, n_blocks=nb, block_k=c["Bk"], row_chunk=c["rc"], out_blocks=blocks)
+    m = mask.cpu().numpy()
+    _check_candidates(dq, o, m, blocks.cpu().numpy(), nb)
+    # a later layer over the same keys and windows, restricted to the published candidates
+    p2 = synth.consumer_layer(p, seed=300 + seed)
+    d2 = idx.Inputs.from_host(p2)
+    o2 = oracle.rows_logits(oracle.Dequantised(p2), range(c["T"]))
+    K = c["K"]
+    mi, mv = idx.idx_logits_topk_fused(d2, K, block_k=c["Bk"], row_chunk=c["rc"], mask=mask)
+    allowed = [m[t, :len(o2[t])].astype(bool) for t in range(c["T"])]
+    topk_ok(mi.cpu().numpy(), None if c["w_lo"] < 0 else mv.cpu().numpy(), o2, dq.ks, K, allowed=allowed)
+    bi, bv = idx.idx_logits_topk_fused_blocks(d2, K, blocks, pool=8, block_k=c["Bk"], row_chunk=c["rc"])
+    assert torch.equal(bi, mi) and torch.equal(bv.view(torch.int32), mv.view(torch.int32))
