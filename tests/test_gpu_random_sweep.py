@@ -110,3 +110,43 @@ def test_random_candidate_source_and_consumers_against_oracle(seed):
     topk_ok(mi.cpu().numpy(), None if c["w_lo"] < 0 else mv.cpu().numpy(), o2, dq.ks, K, allowed=allowed)
     bi, bv = idx.idx_logits_topk_fused_blocks(d2, K, blocks, pool=8, block_k=c["Bk"], row_chunk=c["rc"])
     assert torch.equal(bi, mi) and torch.equal(bv.view(torch.int32), mv.view(torch.int32))
+
+
+N_DENSE_CASES = 32
+
+
+def _id_dense(seed):
+    return "d" + _id(800 + seed)
+
+
+@pytest.mark.parametrize("seed", range(N_DENSE_CASES), ids=_id_dense)
+def test_random_dense_path_against_oracle(seed):
+    """Dense row-relative logits against the oracle to the plain bar (non-negative weights;
+    weights of both signs are held to it by a strict xfail elsewhere), the exact top-K of those
+    logits against the oracle's selection on the same values, and dense top-(K + 512) plus
+    refinement against the fused call: the same index sets bitwise, and the same values where
+    every weight is non-negative."""
+    from checks import dense_ref, logits_ok
+    from test_gpu_parity import _oracle_on
+
+    c = _draw(800 + seed)
+    p = synth.make_problem(c["T"], c["L"], c["H"], k_fmt=c["fmt"], seed=600 + seed, w_lo=c["w_lo"], **c["kw"])
+    d = idx.Inputs.from_host(p)
+    dq = oracle.Dequantised(p)
+    o = oracle.rows_logits(dq, range(c["T"]))
+    W = max(d.W, 1)
+    lg = idx.idx_mqa_logits(d, W)
+    if c["w_lo"] >= 0:
+        logits_ok(lg.cpu().numpy(), dense_ref(o, W))
+    K = c["K"]
+    gi, gv = idx.idx_topk(lg, d.ks, d.ke, K, block_k=c["Bk"])
+    gi, gv = gi.cpu().numpy(), gv.cpu().numpy()
+    for t, win in enumerate(_oracle_on(lg.cpu().numpy(), dq)):
+        oi, ov = oracle.topk_row(win, int(dq.ks[t]), K)
+        assert np.array_equal(gi[t], oi) and np.array_equal(gv[t], ov), f"row {t}"
+    ci, cv = idx.idx_topk(lg, d.ks, d.ke, idx.candidate_capacity(K))
+    di, dv = idx.idx_refine_topk(d, ci, cv, K)
+    fi, fv = idx.idx_logits_topk_fused(d, K, block_k=c["Bk"], row_chunk=c["rc"])
+    assert torch.equal(di, fi)
+    if c["w_lo"] >= 0:
+        assert torch.equal(dv.view(torch.int32), fv.view(torch.int32))
