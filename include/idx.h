@@ -33,8 +33,10 @@
  *
  * Conventions for every entry point:
  *   - Data pointers are DEVICE pointers owned by the caller.  libidx never
- *     allocates or frees memory and never synchronises the stream.  Scratch
- *     space is the caller's `ws` buffer, sized by idx_workspace_size().
+ *     allocates or frees memory and never synchronises the stream (the
+ *     IDX_DEBUG checks and idx_launch_timing_read, which waits for its
+ *     events, excepted).  Scratch space is the caller's `ws` buffer, sized by
+ *     idx_workspace_size().
  *   - All work is enqueued on `stream` (a hipStream_t; NULL = default stream).
  *   - A status other than IDX_OK from argument checking means nothing was
  *     enqueued.  IDX_E_LAUNCH reports a failed launch (hipGetLastError); the
