@@ -106,10 +106,10 @@ hipError_t score(const idx::LogitsArgs &a, const idx_problem *p, int mode, bool 
   static_assert(IDX_LAUNCH_DENSE == idx::STORE_DENSE && IDX_LAUNCH_BLOCK == idx::STORE_BLOCK &&
                     IDX_LAUNCH_POOL8 == idx::STORE_POOL8 && IDX_LAUNCH_SLAB == idx::STORE_SLAB,
                 "launch-timing modes name the scoring modes");
-  const int slot = idx::timing_begin(s);
+  const int token = idx::timing_begin(s);
   const hipError_t e =
       exact ? idx::launch_logits_exact(a, p->k_fmt, p->H, mode, s) : idx::launch_logits(a, p->k_fmt, p->H, mode, s);
-  idx::timing_end(slot, s, e == hipSuccess, mode, flagged ? 1 : 0, a.row0, a.nrows, a.key_lo, a.key_hi - a.key_lo);
+  idx::timing_end(token, s, e == hipSuccess, mode, flagged ? 1 : 0, a.row0, a.nrows, a.key_lo, a.key_hi - a.key_lo);
   return e;
 }
 

@@ -32,9 +32,9 @@ idx_status debug_check(const int32_t *ks, const int32_t *ke, int32_t T, int32_t 
                        void *stream);
 
 // Launch timing (idx_launch_timing): timing_begin records a launch's first event on s when a
-// record is on, and returns its slot (-1: not recorded); timing_end records the second event
-// (ok: the launch was enqueued) and the launch's description.
+// record is on, and returns a token for its slot (-1: not recorded); timing_end records the
+// second event (ok: the launch was enqueued) and the launch's description.
 int timing_begin(hipStream_t s);
-void timing_end(int slot, hipStream_t s, bool ok, int mode, int flagged, int row0, int nrows, int key0, int nkeys);
+void timing_end(int token, hipStream_t s, bool ok, int mode, int flagged, int row0, int nrows, int key0, int nkeys);
 
 }  // namespace idx

@@ -17,6 +17,7 @@ struct Record {
   idx_launch_time entry[IDX_TIMING_MAX];
   bool closed[IDX_TIMING_MAX];           // both events recorded
   int n = 0;
+  int gen = 0;                           // bumped whenever the record is cleared
 };
 
 Record &record() {
@@ -26,6 +27,8 @@ Record &record() {
 
 }  // namespace
 
+// A slot token: the entry index and (modulo 2^16) the record generation it belongs to, so that
+// a launch whose record was cleared meanwhile on another thread writes nothing.
 int timing_begin(hipStream_t s) {
   Record &r = record();
   if (!r.on.load(std::memory_order_acquire)) return -1;
@@ -41,14 +44,15 @@ int timing_begin(hipStream_t s) {
   r.closed[i] = false;
   r.entry[i] = idx_launch_time{-1.f, 0, 0, 0, 0, 0, 0};
   ++r.n;
-  return i;
+  return i + IDX_TIMING_MAX * (r.gen & 0xFFFF);
 }
 
-void timing_end(int slot, hipStream_t s, bool ok, int mode, int flagged, int row0, int nrows, int key0, int nkeys) {
-  if (slot < 0) return;
+void timing_end(int token, hipStream_t s, bool ok, int mode, int flagged, int row0, int nrows, int key0, int nkeys) {
+  if (token < 0) return;
   Record &r = record();
   std::lock_guard<std::mutex> g(r.mu);
-  if (slot >= r.n) return;   // the record was cleared meanwhile
+  const int slot = token % IDX_TIMING_MAX;
+  if (token / IDX_TIMING_MAX != (r.gen & 0xFFFF) || slot >= r.n) return;   // the record was cleared meanwhile
   r.entry[slot] = idx_launch_time{-1.f, mode, flagged, row0, nrows, key0, nkeys};
   r.closed[slot] = ok && hipEventRecord(r.ev[2 * slot + 1], s) == hipSuccess;
 }
@@ -85,6 +89,7 @@ idx_status idx_launch_timing(int32_t enable) {
     r.dev = dev;
   }
   r.n = 0;
+  ++r.gen;
   r.on.store(true, std::memory_order_release);
   return IDX_OK;
 }
@@ -105,6 +110,7 @@ idx_status idx_launch_timing_read(idx_launch_time *out, int32_t cap, int32_t *n)
     out[i] = e;
   }
   r.n = 0;
+  ++r.gen;
   return IDX_OK;
 }
 
