@@ -41,7 +41,10 @@ METRIC = "indexer (row,key) pairs/s fused logits+top-K; % fp8 MFMA peak; peak by
 FP8_PEAK = 5.0e15      # MI355X dense fp8 MFMA, FLOP/s
 HBM_PEAK = 8.0e12
 HEADLINE = "long_ctx"
-ROW_CHUNK = {"tiny": 0, "glm_chunk": 0, "dsv4_mxfp4": 0, "long_ctx": 4096, "ragged_cand": 4096}
+# Row chunks: long_ctx is fastest at 4096 (8192 and 16384: +1%); the ragged batch at 8192 (-11%
+# against 4096: half as many row chunks, each planning its launches over all of L, most of them
+# empty for the short requests), still under the 2 GiB logits budget (1092 MiB workspace).
+ROW_CHUNK = {"tiny": 0, "glm_chunk": 0, "dsv4_mxfp4": 0, "long_ctx": 4096, "ragged_cand": 8192}
 DESCRIBE = {
     "tiny": "tiny: T=64 L=4096 H=32 D=128 fp8 q/k per-row scales, causal windows, top-K=512",
     "glm_chunk": "glm_chunk: T=2048 L=65536 H=32 D=128 fp8 q/k per-row scales, causal windows, top-K=2048, "
@@ -51,7 +54,7 @@ DESCRIBE = {
     "long_ctx": "long_ctx: T=16384 L=487936 H=64 D=128 fp8 q/k per-row scales, causal windows, top-K=512, "
                 "fused key blocks B_k=32768, row chunks of 4096",
     "ragged_cand": "ragged_cand: 4 x 7168 new tokens + 2048 new on a 150000-token prefix (30720 rows, 180720 keys), "
-                   "H=64 fp8, top-K=512",
+                   "H=64 fp8, top-K=512, row chunks of 8192",
 }
 
 
@@ -412,7 +415,7 @@ def traffic_probe(dev):
     d5 = idx.Inputs.from_host(p5, device=dev)
     blocks5 = torch.empty((p5.T, c5["n_blocks"]), dtype=torch.int32, device=dev)
     idx.idx_block_candidates(d5, d5.W, pool=c5["pool"], n_blocks=c5["n_blocks"], block_k=c5["block_k"],
-                             row_chunk=4096, out_blocks=blocks5)
+                             row_chunk=ROW_CHUNK["ragged_cand"], out_blocks=blocks5)
     torch.cuda.synchronize()
     del d5, blocks5
     torch.cuda.empty_cache()
@@ -696,27 +699,28 @@ def ragged_extras(dev, stream, rag):
     p5, d5, _, _ = rag
     c5 = p5.meta
     W5, nb5, pool5, K5, bk5 = d5.W, c5["n_blocks"], c5["pool"], c5["K"], c5["block_k"]
+    RC5 = ROW_CHUNK["ragged_cand"]
     blocks5 = torch.empty((d5.T, nb5), dtype=torch.int32, device=dev)
-    ws5 = torch.empty(idx.idx_workspace_size(idx.IDX_OP_BLOCK_CANDIDATES, d5, block_k=bk5, row_chunk=4096,
+    ws5 = torch.empty(idx.idx_workspace_size(idx.IDX_OP_BLOCK_CANDIDATES, d5, block_k=bk5, row_chunk=RC5,
                                              pool=pool5, n_blocks=nb5), dtype=torch.uint8, device=dev)
     mask5 = torch.empty((d5.T, W5), dtype=torch.uint8, device=dev)
     cand_all = time_events(lambda: idx.idx_block_candidates(d5, W5, pool=pool5, n_blocks=nb5, block_k=bk5,
-                                                            row_chunk=4096, mask=mask5, out_blocks=blocks5,
+                                                            row_chunk=RC5, mask=mask5, out_blocks=blocks5,
                                                             ws=ws5, stream=stream), 3, stream)
     tail = idx.idx_tail_rows(torch.from_numpy(p5.cu_q).to(dev), 512)
     d5t = idx.idx_gather_rows(d5, tail)
     mask5t = torch.empty((d5t.T, W5), dtype=torch.uint8, device=dev)
     cand_tail = time_events(lambda: idx.idx_block_candidates(d5t, W5, pool=pool5, n_blocks=nb5, block_k=bk5,
-                                                             row_chunk=4096, mask=mask5t, ws=ws5, stream=stream),
+                                                             row_chunk=RC5, mask=mask5t, ws=ws5, stream=stream),
                             3, stream)
     p5c = synth.consumer_layer(p5)
     d5c = idx.Inputs.from_host(p5c, device=dev)
-    wsc = torch.empty(idx.idx_workspace_size(idx.IDX_OP_LOGITS_TOPK_FUSED, d5c, K=K5, block_k=bk5, row_chunk=4096),
+    wsc = torch.empty(idx.idx_workspace_size(idx.IDX_OP_LOGITS_TOPK_FUSED, d5c, K=K5, block_k=bk5, row_chunk=RC5),
                       dtype=torch.uint8, device=dev)
-    cons_mask = time_events(lambda: idx.idx_logits_topk_fused(d5c, K5, block_k=bk5, row_chunk=4096, mask=mask5,
+    cons_mask = time_events(lambda: idx.idx_logits_topk_fused(d5c, K5, block_k=bk5, row_chunk=RC5, mask=mask5,
                                                               ws=wsc, stream=stream), 3, stream)
     cons_blocks = time_events(lambda: idx.idx_logits_topk_fused_blocks(d5c, K5, blocks5, pool=pool5, block_k=bk5,
-                                                                       row_chunk=4096, ws=wsc, stream=stream),
+                                                                       row_chunk=RC5, ws=wsc, stream=stream),
                               3, stream)
     out = {"all_rows": {"rows": d5.T, "ms": float(np.median(cand_all)), "mask_bytes": int(mask5.numel())},
            "tail_rows_512": {"rows": int(d5t.T), "ms": float(np.median(cand_tail)), "mask_bytes": int(mask5t.numel())},
