@@ -575,7 +575,7 @@ def trace_summary(trace_dir, slab="logits_kernel<0, 64, 4, 4, ", scoring="logits
     rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     ev = [(_short_kernel(r["Kernel_Name"]), int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows]
-    ours = ("logits", "topk", "refine", "slab", "key_bound")
+    ours = ("logits", "topk", "merge", "refine", "slab", "key_bound")
     steps, i = [], 0
     while i < len(ev):
         if not ev[i][0].startswith("ragged_kernel"):

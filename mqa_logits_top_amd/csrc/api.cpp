@@ -547,21 +547,25 @@ idx_status fused_impl(const idx_problem *p, int32_t K, int32_t block_k, int32_t 
           f.only_flagged = ovf;
           if ((st = launched(score(f, p, idx::STORE_BLOCK, false, s, true)))) return st;
           idx::TopkArgs bh = b;
-          if (h0 == 0) {   // slab merges, and the first block's columns for the other rows
-            bh.cand = slab;
-            bh.cand_ld = sld / 2;
-            bh.ccnt = ccnt;
-            bh.nslab = a.nsplit;
-            bh.caps = CAPS;
-            bh.slab_flags = ovf;
-            bh.slab_rpw = rpw;
-            bh.vcols = hn;
-            bh.col_rows = nk > Bk ? col_rows : nullptr;
-          } else {         // the next block's columns, for the rows that read columns
+          if (h0 == 0) {
+            // slab merges of the rows outside flagged row blocks, which mark the rest in col_rows
+            idx::TopkArgs bm = b;
+            bm.cand = slab;
+            bm.cand_ld = sld / 2;
+            bm.ccnt = ccnt;
+            bm.nslab = a.nsplit;
+            bm.caps = CAPS;
+            bm.slab_flags = ovf;
+            bm.slab_rpw = rpw;
+            bm.col_rows = col_rows;
+            if ((st = launched(idx::launch_merge(bm, s)))) return st;
+            bh.vcols = hn;   // then the first block's columns for the marked rows
+          } else {           // the next block's columns, for the same rows
             bh.key0 = kb + h0;
             bh.ncols = hn;
-            bh.only_rows = col_rows;
           }
+          bh.col_rows = col_rows;
+          bh.only_rows = col_rows;
           if ((st = launched(idx::launch_topk(bh, s)))) return st;
         }
         continue;

@@ -114,10 +114,9 @@ struct TopkArgs {
   int32_t *out_idx;       // row r at out_idx + r * K
   float *out_val;         // row r at out_val + r * K
   int32_t first;          // 1: no running state yet (out_* contents are ignored)
-  // TOPK_BLOCK with the scoring launch's candidate slabs (nullable cand; layout as in
-  // LogitsArgs): a row whose list is full and whose nslab slabs all fit merges the slabs
-  // instead of reading vals, unless its row block (slab_rpw rows of the launch) is flagged in
-  // slab_flags (nullable), whose rows were scored again into vals
+  // launch_merge only: the scoring launch's candidate slabs (layout as in LogitsArgs), and the
+  // slab check's flags of its row blocks (slab_rpw rows each), whose rows were scored again into
+  // vals and are left to topk_kernel
   const uint32_t *cand;
   int64_t cand_ld;
   const uint32_t *ccnt;
@@ -125,10 +124,9 @@ struct TopkArgs {
   const uint32_t *slab_flags;
   int32_t slab_rpw;
   float *thr_out;         // nullable: per launch row, the full list's smallest value, else NaN
-  // A launch's columns in two calls: vcols > 0 limits the columns read from vals to [0, vcols)
-  // (rows still merge slabs over all ncols); col_rows (nullable) receives 1 for a row that read
-  // columns instead of merging its slabs, 0 for one that merged; a call with only_rows set
-  // serves only the rows whose word there is nonzero.
+  // A launch's columns in several calls: vcols > 0 limits the columns read from vals to
+  // [0, vcols); col_rows (nullable) receives 1 for a row that reads columns (launch_merge: 0 for a
+  // row it merged); a call with only_rows set serves only the rows whose word there is nonzero.
   int32_t vcols;
   uint32_t *col_rows;
   const uint32_t *only_rows;
@@ -139,6 +137,11 @@ struct TopkArgs {
 };
 constexpr int BMAP_BITS = 9216;   // block bitmap of a top-K launch (65536 keys in 8-key blocks, and slack)
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
+// Slab merge of the rows outside flagged row blocks (TOPK_BLOCK args with cand, ccnt, nslab,
+// caps, slab_flags, slab_rpw, col_rows and thr_out set; no mask or block list): each row's new
+// running list from its list and its slabs.  col_rows receives 0 for a row merged (or with
+// nothing to merge) and 1 for a row left to topk_kernel's column pass.
+hipError_t launch_merge(const TopkArgs &a, hipStream_t s);
 
 // Exact boundary refinement of per-row candidate lists (see refine.hip).
 struct RefineArgs {

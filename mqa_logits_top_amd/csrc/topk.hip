@@ -47,8 +47,8 @@ constexpr int NI = KMAX + CAPK;     // items: the running list, then a segment's
 
 struct Smem {
   // Items in id order: the running list [0, run_n), then the candidates collected
-  // from a segment (or gathered from the scoring kernel's slabs), then one spare
-  // slot per lane for writes that are dropped.  A merge compacts them in place.
+  // from a segment, then one spare slot per lane for writes that are dropped.  A merge
+  // compacts them in place.
   alignas(16) uint32_t ikey[NI + 64];
   alignas(16) int32_t iid[NI + 64];
   // histogram bins (+ one spare slot per lane); the first CAP words double as the
@@ -60,8 +60,9 @@ struct Smem {
   uint32_t bcast[4];
 };
 
-// Block-wide sum, min and max of one value per thread (all threads must call).
-__device__ __forceinline__ void block_sum_minmax(Smem &sm, uint32_t &s, uint32_t &lo, uint32_t &hi, int lane,
+// Block-wide sum, min and max of one value per thread (all threads must call; S has red[3][waves]).
+template <class S>
+__device__ __forceinline__ void block_sum_minmax(S &sm, uint32_t &s, uint32_t &lo, uint32_t &hi, int lane,
                                                  int wave) {
   s = wave_sum(s);
   lo = wave_min(lo);
@@ -73,15 +74,16 @@ __device__ __forceinline__ void block_sum_minmax(Smem &sm, uint32_t &s, uint32_t
   lo = 0xFFFFFFFFu;
   hi = 0;
 #pragma unroll
-  for (int w = 0; w < NWV; ++w) {
+  for (int w = 0; w < (int)(sizeof(sm.red[0]) / 4); ++w) {
     s += sm.red[0][w];
     lo = min(lo, sm.red[1][w]);
     hi = max(hi, sm.red[2][w]);
   }
 }
 
-// Two simultaneous block-wide exclusive scans in thread order, with their totals.
-__device__ __forceinline__ void block_scan2(Smem &sm, uint32_t a, uint32_t b, uint32_t &ea, uint32_t &eb,
+// Two simultaneous block-wide exclusive scans in thread order, with their totals (S has wsum[2][waves]).
+template <class S>
+__device__ __forceinline__ void block_scan2(S &sm, uint32_t a, uint32_t b, uint32_t &ea, uint32_t &eb,
                                             uint32_t &ta, uint32_t &tb, int lane, int wave) {
   const uint32_t ia = wave_incl_scan(a), ib = wave_incl_scan(b);
   __syncthreads();
@@ -91,7 +93,7 @@ __device__ __forceinline__ void block_scan2(Smem &sm, uint32_t a, uint32_t b, ui
   ta = 0;
   tb = 0;
 #pragma unroll
-  for (int w = 0; w < NWV; ++w) {
+  for (int w = 0; w < (int)(sizeof(sm.wsum[0]) / 4); ++w) {
     const uint32_t sa = sm.wsum[0][w], sb = sm.wsum[1][w];
     if (w < wave) { pa += sa; pb += sb; }
     ta += sa;
@@ -234,7 +236,7 @@ __device__ __forceinline__ int merge_items(Smem &sm, int N, int run_n, int id0, 
   return min((int)(atot + min(etot, ne)), K);
 }
 
-template <bool SLABS, bool BLOCKS>
+template <bool BLOCKS>
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) void topk_kernel(TopkArgs a) {
   __shared__ Smem sm;
   // newest rows first: the scoring launch before this one wrote them last, so they are the
@@ -317,96 +319,10 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const int seg = max(min(a.block, SEG) & ~3, 4);
   const int sbase = vec ? (c_lo & ~3) : c_lo;
 
-  // ---- compact path: a full list whose block candidates above its smallest entry all
-  // fit the scoring kernel's slabs merges those instead of reading the block's columns
-  bool merged = false;
   uint32_t list_min = 0;  // smallest key of the list after the last merge (once it is full)
-  // (a row block flagged by the slab check was scored again into vals, over its slabs)
-  if (SLABS && !a.first && run_n == K && !(a.slab_flags && a.slab_flags[r / a.slab_rpw] != 0u)) {
-    // one count word per (slab, part): candidates in the low half, share offset above
-    const int ne = a.nslab * CAND_PARTS;
-    uint32_t cs = 0, over = 0, cw = 0;
-    if (tid < ne) {
-      cw = a.ccnt[(int64_t)r * ne + tid];
-      cs = cw & 0xFFFFu;
-      over = cs == CAND_OVER;
-      if (over) cs = 0;
-    }
-    uint32_t ex, d1, tot_c, osum;   // share offsets, total candidates, overflowed shares
-    block_scan2(sm, cs, over, ex, d1, tot_c, osum, lane, wave);
-    if (osum == 0 && tot_c <= (uint32_t)CAPK && a.caps <= CAPS_MAX && ne <= NTH) {  // uniform
-      // the shares hold their candidates in id order and cover consecutive key ranges,
-      // so appending them after the running list keeps the items in id order
-      if (tid < ne) { sm.hist[tid] = ex; sm.hist[NTH + tid] = (cw & 0xFFFF0000u) | cs; }
-      __syncthreads();
-      auto share_src = [&](int e) __attribute__((always_inline)) -> const uint2 * {
-        return (const uint2 *)a.cand + (int64_t)r * a.cand_ld + (e / CAND_PARTS) * a.caps + (sm.hist[NTH + e] >> 16);
-      };
-      auto put = [&](uint2 ev, uint32_t at) __attribute__((always_inline)) {
-        const int id = (int)ev.y;
-        uint32_t k = fkey(__uint_as_float(ev.x));
-        if (mrow) {
-          const int64_t mj = (int64_t)id - ks;
-          if (!(mj >= 0 && mj < a.mask_w && mrow[mj])) k = 0;
-        }
-        if (BLOCKS && !block_ok((int64_t)id - ks)) k = 0;
-        sm.ikey[at] = k;
-        sm.iid[at] = id;
-      };
-      // Wave w gathers shares w, w + 8, ...: entry `lane` of up to GS of its shares is loaded
-      // at once (one memory round trip when the shares hold at most 64 entries, as they mostly
-      // do), then the rest of the longer shares.
-      constexpr int GS = 8;
-      for (int e0 = wave; e0 < ne; e0 += NWV * GS) {
-        uint2 ev[GS];
-        static_for<GS>([&](auto j) __attribute__((always_inline)) {
-          const int e = e0 + NWV * j;
-          const uint32_t n = e < ne ? sm.hist[NTH + e] & 0xFFFFu : 0u;
-          ev[j] = (uint32_t)lane < n ? share_src(e)[lane] : make_uint2(0u, 0u);
-        });
-        static_for<GS>([&](auto j) __attribute__((always_inline)) {
-          const int e = e0 + NWV * j;
-          const uint32_t n = e < ne ? sm.hist[NTH + e] & 0xFFFFu : 0u;
-          if ((uint32_t)lane < n) put(ev[j], run_n + sm.hist[e] + lane);
-        });
-      }
-      for (int e = wave; e < ne; e += NWV) {
-        const uint32_t n = sm.hist[NTH + e] & 0xFFFFu;
-        if (n <= 64) continue;  // uniform over the wave
-        const uint2 *src = share_src(e);
-        const uint32_t base = run_n + sm.hist[e];
-        uint2 ev[CAPS_MAX / 64 - 1];
-        static_for<CAPS_MAX / 64 - 1>([&](auto m) __attribute__((always_inline)) {
-          const uint32_t i = lane + 64 * (m + 1);
-          ev[m] = i < n ? src[i] : make_uint2(0u, 0u);
-        });
-        static_for<CAPS_MAX / 64 - 1>([&](auto m) __attribute__((always_inline)) {
-          const uint32_t i = lane + 64 * (m + 1);
-          if (i < n) put(ev[m], base + i);
-        });
-      }
-      __syncthreads();
-      const int N = run_n + (int)tot_c;
-      // size and key range of the union
-      uint32_t total = 0, umin = 0xFFFFFFFFu, umax = 0;
-      for (int i = tid; i < N; i += NTH) {
-        const uint32_t k = sm.ikey[i];
-        total += k != 0u;
-        umin = min(umin, k != 0u ? k : 0xFFFFFFFFu);
-        umax = max(umax, k);
-      }
-      block_sum_minmax(sm, total, umin, umax, lane, wave);
-      uint32_t thk = 0;
-      int need_eq = 0;
-      if ((int)total > K) lds_select(sm, N, umin, umax, K, total, thk, need_eq, tid, lane, wave);
-      run_n = merge_items(sm, N, N, 0, thk, need_eq, K, tid, lane, wave);
-      list_min = (int)total > K ? thk : umin;
-      merged = true;
-    }
-  }
 
-  if (a.col_rows && tid == 0) a.col_rows[r] = merged ? 0u : 1u;
-  for (int S = sbase; S < c_rd && !merged; S += seg) {
+  if (a.col_rows && tid == 0) a.col_rows[r] = 1u;   // this row reads the launch's columns
+  for (int S = sbase; S < c_rd; S += seg) {
     const int s0 = max(S, c_lo), s1 = min(S + seg, c_rd);  // valid columns of this segment
 
     auto run_key = [&](int p) __attribute__((always_inline)) -> uint32_t { return sm.ikey[p]; };
@@ -678,8 +594,239 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   if (a.thr_out && tid == 0) a.thr_out[r] = run_n == K ? kval(list_min) : __builtin_nanf("");
 }
 
+// ---- Slab merge (P1 section 2.3: the top-K of a union is the top-K of the union of its parts'
+// top-Ks).  After a candidate-slab scoring launch, a row's new running list is the top Kc of
+// its running list and the candidates its slabs hold (every one above the list's smallest
+// entry), under (value desc, id asc), in id order.  One workgroup per row keeps the items in
+// registers: thread t holds items MIPT t .. MIPT t + MIPT - 1 of the running list followed by
+// the slab shares, which is id order (the list holds keys of earlier launches, and the shares
+// hold consecutive key ranges, each in key order).  A histogram select over the register keys
+// finds the Kc-th key; a block scan then writes the taken items to the list in item order.  The
+// LDS holds only the histogram and the share table, so several rows share a CU.
+// Rows of a row block flagged by the slab check (scored again into the scratch) and rows that
+// do not meet the merge's conditions get col_rows = 1 and are left to topk_kernel.
+constexpr int MNT = 512;               // threads
+constexpr int MNW = MNT / 64;
+constexpr int MIPT = 16;               // items per thread
+constexpr int CPT = NTH / MNT;         // count words per thread (a launch has at most NTH shares)
+static_assert(MNT * MIPT >= KMAX + CAPK && NB % MNT == 0 && NTH % MNT == 0, "merge layout");
+
+struct MergeSmem {
+  uint32_t hist[NB + 64];              // histogram bins; the first CAP words double as the ranking list
+  uint32_t soff[NTH];                  // share e: first item (after the running list)
+  uint32_t sbeg[NTH];                  // share e: slab entry of its first candidate
+  uint32_t red[3][MNW];
+  uint32_t wsum[2][MNW];
+  uint32_t bcast[4];
+};
+
+// (6 waves per SIMD: three rows per CU; 256 threads with 32 items each measured slower)
+__global__ __launch_bounds__(MNT) __attribute__((amdgpu_waves_per_eu(6))) void merge_kernel(TopkArgs a) {
+  __shared__ MergeSmem sm;
+  const int r = a.nrows - 1 - (int)blockIdx.x;        // newest rows first (as topk_kernel)
+  if (a.launch_flag && (*a.launch_flag & 2u) != 0u) return;   // an empty launch: no slab was written
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int K = a.K;
+  int32_t *oidx = a.out_idx + (int64_t)r * K;
+  float *oval = a.out_val + (int64_t)r * K;
+  auto leave = [&](uint32_t cols) __attribute__((always_inline)) {
+    if (tid == 0) a.col_rows[r] = cols;
+  };
+  if (a.slab_flags[r / a.slab_rpw] != 0u) { leave(1u); return; }   // uniform
+
+  // ---- share table: count words CPT t .. CPT t + CPT - 1 -> item offsets
+  const int ne = a.nslab * CAND_PARTS;
+  uint32_t cw[CPT], cs[CPT], my_c = 0, my_o = 0;
+#pragma unroll
+  for (int q = 0; q < CPT; ++q) {
+    const int e = CPT * tid + q;
+    cw[q] = e < ne ? a.ccnt[(int64_t)r * ne + e] : 0u;
+    cs[q] = cw[q] & 0xFFFFu;
+    if (cs[q] == CAND_OVER) { cs[q] = 0; ++my_o; }
+    my_c += cs[q];
+  }
+  uint32_t ex, d1, tot_c, osum;
+  block_scan2(sm, my_c, my_o, ex, d1, tot_c, osum, lane, wave);
+  if (osum != 0 || tot_c > (uint32_t)CAPK || a.caps > CAPS_MAX || ne > NTH || K > KMAX) { leave(1u); return; }
+  if (tot_c == 0) { leave(0u); return; }   // nothing above the list: list and threshold stay
+#pragma unroll
+  for (int q = 0; q < CPT; ++q) {
+    const int e = CPT * tid + q;
+    if (e < ne) { sm.soff[e] = ex; sm.sbeg[e] = cw[q] >> 16; }
+    ex += cs[q];
+  }
+  __syncthreads();
+
+  // ---- items into registers: one round of loads (running list entries, slab candidates)
+  const int N = K + (int)tot_c;
+  const int i0 = tid * MIPT;
+  uint32_t key[MIPT];
+  int32_t id[MIPT];
+  {
+    // the share of this thread's first candidate: the last e with soff[e] <= j
+    int e = 0;
+    const int j0 = max(i0 - K, 0);
+    if (i0 + MIPT > K && i0 < N) {
+      int lo = 0, hi = ne - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int)sm.soff[mid] <= j0) lo = mid;
+        else hi = mid - 1;
+      }
+      e = lo;
+    }
+    // value bits into key[], ids into id[]; then the values become order-preserving keys
+    const uint2 *slabs = (const uint2 *)a.cand + (int64_t)r * a.cand_ld;
+    static_for<MIPT>([&](auto u) __attribute__((always_inline)) {
+      const int i = i0 + u;
+      id[u] = -1;
+      key[u] = 0u;
+      if (i < K) {
+        id[u] = oidx[i];
+        key[u] = __float_as_uint(oval[i]);
+      } else if (i < N) {
+        const int j = i - K;
+        while (e + 1 < ne && (int)sm.soff[e + 1] <= j) ++e;
+        const uint2 c = slabs[(e / CAND_PARTS) * a.caps + sm.sbeg[e] + (j - (int)sm.soff[e])];
+        key[u] = c.x;
+        id[u] = (int32_t)c.y;
+      }
+    });
+    static_for<MIPT>([&](auto u) __attribute__((always_inline)) {
+      key[u] = i0 + (int)u < N && id[u] >= 0 ? fkey(__uint_as_float(key[u])) : 0u;
+    });
+  }
+  // size (nonzero keys, low half) and full running list entries (high half), key range
+  uint32_t cnt = 0, umin = 0xFFFFFFFFu, umax = 0;
+  static_for<MIPT>([&](auto u) __attribute__((always_inline)) {
+    const uint32_t k = key[u];
+    cnt += (k != 0u) + ((uint32_t)(i0 + (int)u < K && id[u] >= 0) << 16);
+    umin = min(umin, k != 0u ? k : 0xFFFFFFFFu);
+    umax = max(umax, k);
+  });
+  block_sum_minmax(sm, cnt, umin, umax, lane, wave);
+  const uint32_t total = cnt & 0xFFFFu;
+  if ((int)(cnt >> 16) != K) { leave(1u); return; }   // (not reached: a row with a partial list has
+                                                      // a NaN threshold, which the slab check flags)
+
+  // ---- the K-th largest key thk and the number need_eq of keys equal to it that are taken
+  uint32_t thk = 0;
+  int need_eq = 0;
+  if ((int)total > K) {
+    uint32_t clo = umin, chi = umax, icnt = total;
+    int need = K;
+    for (;;) {
+      if (clo == chi) { thk = clo; need_eq = need; break; }
+      if (icnt <= (uint32_t)CAP) {
+        // rank the interval's keys directly
+        __syncthreads();
+        if (tid == 0) sm.bcast[0] = 0;
+        __syncthreads();
+        static_for<MIPT>([&](auto u) __attribute__((always_inline)) {
+          const uint32_t k = key[u];
+          if (k >= clo && k <= chi) {
+            const uint32_t slot = atomicAdd(&sm.bcast[0], 1u);
+            if (slot < (uint32_t)CAP) sm.hist[slot] = k;
+          }
+        });
+        __syncthreads();
+        const int n = (int)min(sm.bcast[0], (uint32_t)CAP);
+        const int n4 = (n + 3) >> 2;
+        if (tid < 4 * n4 - n) sm.hist[n + tid] = 0u;   // pad with key 0, below the interval
+        __syncthreads();
+        const uint4 *h4 = reinterpret_cast<const uint4 *>(sm.hist);
+        for (int q = tid; q < n; q += MNT) {
+          const uint32_t mine = sm.hist[q];
+          int gt = 0, ge = 0;
+#pragma unroll 4
+          for (int j = 0; j < n4; ++j) {
+            const uint4 o = h4[j];
+            gt += (o.x > mine) + (o.y > mine) + (o.z > mine) + (o.w > mine);
+            ge += (o.x >= mine) + (o.y >= mine) + (o.z >= mine) + (o.w >= mine);
+          }
+          if (gt < need && need <= ge) { sm.bcast[1] = mine; sm.bcast[2] = (uint32_t)(need - gt); }
+        }
+        __syncthreads();
+        thk = sm.bcast[1];
+        need_eq = (int)sm.bcast[2];
+        break;
+      }
+      const uint32_t span = chi - clo;
+      int sh = 0;
+      while ((span >> sh) >= (uint32_t)NB) ++sh;
+      __syncthreads();
+      for (int i = tid; i < NB; i += MNT) sm.hist[i] = 0;
+      __syncthreads();
+      static_for<MIPT>([&](auto u) __attribute__((always_inline)) {
+        const uint32_t k = key[u];
+        if (k >= clo && k <= chi) atomicAdd(&sm.hist[bin_of(k, chi, sh)], 1u);
+      });
+      __syncthreads();
+      {
+        constexpr int BPT = NB / MNT;
+        uint32_t h[BPT], tot = 0;
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) { h[i] = sm.hist[tid * BPT + i]; tot += h[i]; }
+        uint32_t before, d0, t0, t1;
+        block_scan2(sm, tot, 0u, before, d0, t0, t1, lane, wave);
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+          if (before < (uint32_t)need && (uint32_t)need <= before + h[i]) {
+            sm.bcast[0] = tid * BPT + i;
+            sm.bcast[1] = before;
+            sm.bcast[2] = h[i];
+          }
+          before += h[i];
+        }
+      }
+      __syncthreads();
+      const uint32_t bstar = sm.bcast[0];
+      need -= (int)sm.bcast[1];
+      icnt = sm.bcast[2];
+      const uint32_t nhi = chi - (bstar << sh);
+      clo = max(clo, nhi - min(nhi - clo, (1u << sh) - 1u));
+      chi = nhi;
+    }
+  }
+
+  // ---- the new list: keys above thk, then need_eq keys equal to it in item order
+  uint32_t n1 = 0, n2 = 0;
+  static_for<MIPT>([&](auto u) __attribute__((always_inline)) {
+    const uint32_t k = key[u];
+    n1 += k != 0u && k > thk;
+    n2 += k != 0u && k == thk && need_eq > 0;
+  });
+  uint32_t eo, ao, etot, atot;
+  block_scan2(sm, n2, n1, eo, ao, etot, atot, lane, wave);
+  const uint32_t neq = (uint32_t)need_eq;
+  uint32_t e = eo, pos = ao + min(eo, neq);
+  static_for<MIPT>([&](auto u) __attribute__((always_inline)) {
+    const uint32_t k = key[u];
+    const bool eq = k != 0u && k == thk && need_eq > 0;
+    const bool tk = (k != 0u && k > thk) || (eq && e < neq);
+    e += eq;
+    if (tk && pos < (uint32_t)K) {
+      oidx[pos] = id[u];
+      oval[pos] = kval(k);
+    }
+    pos += tk;
+  });
+  const uint32_t taken = atot + min(etot, neq);
+  // (taken == K when total > K; otherwise every item is taken and the list is the union)
+  if ((int)taken < K)
+    for (int p = (int)taken + tid; p < K; p += MNT) {
+      oidx[p] = -1;
+      oval[p] = -__builtin_inff();
+    }
+  if (tid == 0) {
+    a.col_rows[r] = 0u;
+    if (a.thr_out) a.thr_out[r] = (int)taken == K ? kval((int)total > K ? thk : umin) : __builtin_nanf("");
+  }
+}
+
 // One wave per row block: does any of its rows need the block's scores?  The conditions
-// are those under which topk_kernel<true, *> leaves the slab merge for the column pass.
+// are those under which merge_kernel leaves a row to topk_kernel's column pass.
 // Lanes take the row's count words (nshares <= NTH); the wave sums them.
 __global__ __launch_bounds__(64) void slab_check_kernel(const uint32_t *ccnt, int32_t nshares, const float *thr,
                                                         int32_t nrows, int32_t rpw, uint32_t *flags,
@@ -715,18 +862,20 @@ hipError_t launch_slab_check(const uint32_t *ccnt, int32_t nshares, const float 
   return hipGetLastError();
 }
 
+hipError_t launch_merge(const TopkArgs &a, hipStream_t s) {
+  if (a.nrows <= 0) return hipSuccess;
+  if (!a.cand || !a.ccnt || !a.slab_flags || !a.col_rows || !a.out_val || a.mask || a.blocks) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)a.nrows), dim3(MNT), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
   if (a.nrows <= 0) return hipSuccess;
-  if (a.blocks) {
-    if (a.cand)
-      hipLaunchKernelGGL((topk_kernel<true, true>), dim3((unsigned)a.nrows), dim3(NTH), 0, s, a);
-    else
-      hipLaunchKernelGGL((topk_kernel<false, true>), dim3((unsigned)a.nrows), dim3(NTH), 0, s, a);
-  } else if (a.cand) {
-    hipLaunchKernelGGL((topk_kernel<true, false>), dim3((unsigned)a.nrows), dim3(NTH), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((topk_kernel<false, false>), dim3((unsigned)a.nrows), dim3(NTH), 0, s, a);
-  }
+  if (a.cand) return hipErrorInvalidValue;   // slab merges go to launch_merge
+  if (a.blocks)
+    hipLaunchKernelGGL(topk_kernel<true>, dim3((unsigned)a.nrows), dim3(NTH), 0, s, a);
+  else
+    hipLaunchKernelGGL(topk_kernel<false>, dim3((unsigned)a.nrows), dim3(NTH), 0, s, a);
   return hipGetLastError();
 }
 
