@@ -31,6 +31,8 @@ def _draw(seed):
     layout = str(rng.choice(["causal", "random", "ragged"]))
     w_lo = float(rng.choice([0.0, 0.0, -0.5]))
     kw = {}
+    if layout == "causal":
+        T = min(T, L)   # a causal chunk's rows are the last T of its L keys
     if layout == "random":
         ks = rng.integers(0, L, T).astype(np.int32)
         ke = np.minimum(ks + rng.integers(0, L + 1, T), L).astype(np.int32)
