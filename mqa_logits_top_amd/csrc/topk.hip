@@ -658,7 +658,9 @@ __global__ __launch_bounds__(MNT) __attribute__((amdgpu_waves_per_eu(6))) void m
   }
   __syncthreads();
 
-  // ---- items into registers: one round of loads (running list entries, slab candidates)
+  // ---- items into registers: one round of loads (running list entries, slab candidates).
+  // The new list overwrites the old one in place: every load is consumed before the block
+  // reduction below, and the writes come after two more block barriers.
   const int N = K + (int)tot_c;
   const int i0 = tid * MIPT;
   uint32_t key[MIPT];
