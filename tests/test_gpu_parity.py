@@ -224,6 +224,38 @@ def test_fused_slab_launch_mixed_fallback(Bk):
 
 
 @pytest.mark.parametrize("H,k_fmt", [(64, synth.K_FP8), (32, synth.K_MXFP4)])
+def test_fused_slab_merge_heavy_ties(H, k_fmt):
+    """Slab merges that split a tier of exactly equal scores.  Every key is a byte copy of one of
+    64 key rows, so a row's scores take at most 64 values, each held by ~L / 64 keys.  With
+    K + 512 = 576 and B_k = 4096, keys 0..12288 go in three block launches, after which a row's
+    list holds its top tiers; the three slab launches' candidates (scores above the list's
+    smallest) fall in tiers the list already holds, so every merge keeps part of a tier, by
+    index.  The selection must be the oracle's (value desc, index asc) and, bitwise, the dense
+    path's."""
+    T, L, K, Bk = 32, 60000, 64, 4096
+    p = synth.make_problem(T, L, H, k_fmt=k_fmt, seed=31)
+    src = np.random.default_rng(5).integers(0, 64, L)
+    p.k[:] = p.k[src]
+    p.k_scale[:] = p.k_scale[src]
+    dq = oracle.Dequantised(p)
+    o = oracle.rows_logits(dq, range(T))
+    d = dev(p)
+    fi, fv = idx.idx_logits_topk_fused(d, K, block_k=Bk)
+    topk_ok(fi.cpu().numpy(), fv.cpu().numpy(), o, dq.ks, K)
+    lg = idx.idx_mqa_logits(d, d.W)
+    ci, cv = idx.idx_topk(lg, d.ks, d.ke, idx.candidate_capacity(K))
+    di, dv = idx.idx_refine_topk(d, ci, cv, K)
+    assert torch.equal(di, fi)
+    assert torch.equal(dv.view(torch.int32), fv.view(torch.int32))
+    # the last row's K-th value is shared by selected and unselected keys (a split tier)
+    t = T - 1
+    vals = np.asarray(o[t], np.float32)
+    sel = fi[t].cpu().numpy()
+    vk = vals[sel - int(dq.ks[t])].min()
+    assert (vals == vk).sum() > (vals[sel - int(dq.ks[t])] == vk).sum()
+
+
+@pytest.mark.parametrize("H,k_fmt", [(64, synth.K_FP8), (32, synth.K_MXFP4)])
 def test_fused_slab_launch_negative_weights(H, k_fmt):
     """Slab launches served by the fp32 scoring form: rows 0..31 have head weights of both signs
     (U(-0.5, 1)), rows 32..47 non-negative ones (the f16 form).  With K + 512 = 576 and B_k =
